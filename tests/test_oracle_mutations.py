@@ -1,0 +1,84 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that some pin catches each one.
+
+A pin set that lets any of these through would not be strong enough to trust the oracle."""
+import numpy as np
+import pytest
+
+from oracle import pk_oracle as O
+from tests import oracle_pins as P
+
+
+def _run_all_pins():
+    failures = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, FloatingPointError, IndexError) as e:
+            failures.append(pin.__name__)
+    return failures
+
+
+def _interleaved_rope(x, pos, base, inverse=False):
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    th = O.rope_angles(pos, d, base)
+    c, s = np.cos(th)[:, None, :], np.sin(th)[:, None, :]
+    if inverse:
+        s = -s
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 1::2] * c + x[..., 0::2] * s
+    return out
+
+
+_orig_rope = O.rope_apply
+_orig_build = O.build_meta
+_orig_softmax = O._softmax_rows
+
+
+def _global_positions(lengths, total_tokens, tile_rows=O.TILE_ROWS):
+    m = _orig_build(lengths, total_tokens, tile_rows)
+    if "pos" in m:
+        m["pos"] = np.arange(total_tokens)
+    return m
+
+
+def _cost_off_by_one(cu, seq_id, t, r=O.TILE_ROWS):
+    f, b = _orig_work_lists(cu, seq_id, t, r)
+    f[:, 3] -= 1  # forward keys stop one short of the tile's end
+    return f, b
+
+
+_orig_work_lists = O.work_lists
+
+MUTATIONS = {
+    "gqa_interleaved_groups": ("kv_head_of", lambda h, g: h % g),
+    "mask_excludes_diagonal": ("causal_keep", lambda n: np.tril(np.ones((n, n), bool), -1)),
+    "mask_not_causal": ("causal_keep", lambda n: np.ones((n, n), bool)),
+    "rope_reversed_angle": ("rope_angles", lambda pos, d, base: -(np.asarray(pos, float)[:, None]
+                             * np.power(float(base), -2.0 * np.arange(d // 2) / d)[None, :])),
+    "rope_wrong_frequency": ("rope_angles", lambda pos, d, base: np.asarray(pos, float)[:, None]
+                             * np.power(float(base), -1.0 * np.arange(d // 2) / d)[None, :]),
+    "rope_interleaved_pairs": ("rope_apply", _interleaved_rope),
+    "rope_backward_not_transposed": ("rope_apply", lambda x, pos, base, inverse=False: _orig_rope(x, pos, base)),
+    "positions_not_reset": ("build_meta", _global_positions),
+    "lse_without_max": ("_softmax_rows", lambda s: (_orig_softmax(s)[0], np.log(np.exp(s - s.max(1)[:, None]).sum(1)))),
+    "dS_dropped_D": ("score_grad", lambda p, do, v: p * (do @ v.T)),
+    "dS_sign": ("score_grad", lambda p, do, v: p * (np.sum(do * (p @ v), 1)[:, None] - do @ v.T)),
+    "dQ_missing_scale": ("query_grad", lambda ds, kr, scale: ds @ kr),
+    "dK_transposed_operand": ("key_grad", lambda ds, qr, scale: scale * (ds @ qr)),
+    "worklist_short_range": ("work_lists", _cost_off_by_one),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failures = _run_all_pins()
+    assert failures, "mutation %s passed every pin" % name
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert _run_all_pins() == []

@@ -1,0 +1,9 @@
+"""The oracle against what the pages and the mathematics fix (CPU only)."""
+import pytest
+
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
