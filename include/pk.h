@@ -1,0 +1,165 @@
+/*
+ * pk.h -- packed-sequence causal attention for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * Sources, cited by page title and section:
+ *   [UN-2026] "如何用 Unsloth 和 NVIDIA 让 LLM 训练更快" (Unsloth x NVIDIA, dbyun.net/tutorial/10079),
+ *             §1 "缓存 Packed-Sequence 元数据": short samples are concatenated with no padding; the
+ *             boundaries travel as metadata B = {lengths, cu_seqlens, max_seqlen, mask structure};
+ *             every layer consumes the same B, so it is built once and used L times, and no
+ *             per-layer device-to-host synchronisation is allowed on the path.
+ *             §3 (MoE routing): group once with a stable sort + counts instead of one dynamic
+ *             query per group -- the pattern the work-list build follows.
+ *   [UN-2023] "Introducing Unsloth：LLM 训练提速 30 倍" (dbyun.net/tutorial/10038),
+ *             "手动 Autograd": A(X) = softmax(Q K^T / sqrt(d) + M) V;
+ *             "OpenAI Triton kernels": rotate-half RoPE on the two halves of the head dim.
+ *   [N1N-2026] "利用 Unsloth 和 NVIDIA 硬件加速 LLM 训练：技术深度解析" (explore.n1n.ai),
+ *             §2 "FlashAttention-2 的深度集成": tiles kept on chip, softmax fused with the
+ *             products, no N x N matrix stored.
+ *   [MV] "UnSloth极速微调：底层CUDA优化带来的变革" (maplevalley.com.cn), RoPE paragraph:
+ *             positions' rotation factors served from a precomputed table.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers point to memory the caller allocated on the current HIP device and owns.
+ *     The library allocates no device memory.  Host pointers are marked "host".
+ *   - Every call that takes `hip_stream` (a hipStream_t, NULL = the default stream) only enqueues
+ *     work on that stream and returns; none of them synchronises or reads device memory, except
+ *     pk_meta_check, a debugging aid.
+ *   - Argument errors are detected on the host before anything is launched: the call returns a
+ *     negative pk_status and enqueues nothing.  Errors reported by the HIP runtime at launch
+ *     return PK_ERR_HIP.  No exceptions cross the ABI.
+ *   - Tensor layouts are contiguous "token-major" packs:
+ *       q, out, dout, dq : [T, hq, d]      k, v, dk, dv : [T, hkv, d]      lse : [hq, T]
+ *     q/k/v/out/dout are bfloat16, lse/dq/dk/dv are float32.
+ *   - Supported shapes: d in {64, 128}; hq % hkv == 0; 1 <= hkv <= hq <= 256;
+ *     0 <= T <= PK_MAX_TOKENS; 0 <= n_seqs <= T (n_seqs may be 0 only when T == 0).
+ */
+#ifndef PK_H
+#define PK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PK_TILE_ROWS 128          /* tokens per work item (rule W granularity) */
+#define PK_ITEM_FIELDS 8          /* int32 fields per work item */
+#define PK_MAX_TOKENS (1 << 20)   /* largest pack the library accepts */
+
+typedef enum pk_status {
+    PK_OK = 0,
+    PK_ERR_INVALID = -1,      /* null pointer, negative size, size mismatch, wrong device */
+    PK_ERR_UNSUPPORTED = -2,  /* head_dim, head counts or token count outside the supported set */
+    PK_ERR_CAPACITY = -3,     /* a caller buffer (meta buffer, workspace) is too small */
+    PK_ERR_HIP = -4,          /* the HIP runtime reported an error */
+    PK_ERR_DEVICE = -5        /* pk_meta_check only: the device-side status word is non-zero */
+} pk_status;
+
+/* Device-side status word bits, set by pk_build_meta for data only the device can see. */
+#define PK_META_BAD_LENGTH 1      /* some length < 1 */
+#define PK_META_BAD_TOTAL 2       /* the lengths do not sum to total_tokens */
+
+/* Opaque handle: a small host object that points into the caller's meta buffer.  It is
+ * immutable after pk_build_meta returns, so several streams may read it concurrently. */
+typedef struct pk_meta_s *pk_meta_t;
+
+/* Device pointers into the meta buffer (all int32), for callers and tests that read B. */
+typedef struct pk_meta_view {
+    const int32_t *cu_seqlens;    /* [n_seqs + 1]: cu[0] = 0, cu[s+1] = cu[s] + lengths[s] */
+    const int32_t *max_seqlen;    /* [1] */
+    const int32_t *status;        /* [1]: PK_META_* bits, 0 when the pack is valid */
+    const int32_t *seq_id;        /* [T]: sequence of each token */
+    const int32_t *pos;           /* [T]: position of each token inside its sequence */
+    const int32_t *fwd_items;     /* [n_items][8]: {q_start, q_end, kv_start, kv_end, seq_first,
+                                     seq_last, cost, tile}, longest first */
+    const int32_t *bwd_items;     /* [n_items][8]: {kv_start, kv_end, q_start, q_end, seq_first,
+                                     seq_last, cost, tile}, longest first */
+    int32_t n_seqs;
+    int32_t n_items;              /* ceil(T / PK_TILE_ROWS) */
+    int64_t total_tokens;
+    int32_t device;               /* HIP device the meta was built on */
+} pk_meta_view_t;
+
+/* Work-list granularity (PK_TILE_ROWS), exported for bindings. */
+int32_t pk_tile_rows(void);
+
+/* Bytes of device memory pk_build_meta needs for a pack of n_seqs sequences and T tokens.
+ * Returns 0 for unsupported sizes. */
+size_t pk_meta_bytes(int32_t n_seqs, int64_t total_tokens);
+
+/* Build B for one pack ([UN-2026] §1): cu_seqlens by an on-device prefix sum of `lengths`,
+ * max_seqlen, per-token seq_id and pos, the forward (query-tile) and backward (key-tile) work
+ * lists sorted longest-first, and a status word.  `lengths_dev` is int32 [n_seqs] on the device
+ * and must stay valid until the enqueued work has run.  `meta_buf_dev` (>= pk_meta_bytes bytes,
+ * 256-byte aligned) holds B and must outlive the handle.  On success *out receives a new handle;
+ * release it with pk_meta_destroy.  T and n_seqs come from the host, so nothing is read back:
+ * invalid lengths are only visible in the device status word, and attention calls given such a
+ * meta write zeros. */
+pk_status pk_build_meta(const int32_t *lengths_dev, int32_t n_seqs, int64_t total_tokens,
+                        void *meta_buf_dev, size_t meta_buf_bytes, void *hip_stream,
+                        pk_meta_t *out /* host */);
+
+/* Fill *view (host) with the device pointers and sizes of a meta. */
+pk_status pk_meta_view(pk_meta_t meta, pk_meta_view_t *view /* host */);
+
+/* DEBUGGING AID, SYNCHRONISES `hip_stream`: copy the status word and max_seqlen to the host.
+ * Returns PK_ERR_DEVICE when the status word is non-zero.  Either output pointer may be NULL. */
+pk_status pk_meta_check(pk_meta_t meta, void *hip_stream, int32_t *status_host,
+                        int32_t *max_seqlen_host);
+
+/* Free the handle (host memory only; the caller's meta buffer is untouched). */
+pk_status pk_meta_destroy(pk_meta_t meta);
+
+/* Workspace bytes pk_attn_fwd needs: the rotated K and the RoPE cos/sin table. */
+size_t pk_attn_fwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d);
+
+/* Forward ([UN-2023] "手动 Autograd", [N1N-2026] §2):
+ *   out = softmax(scale * R(q) R(k)^T + M) v,   lse = log-sum-exp of the scaled masked scores,
+ * with M the block-diagonal causal mask of the pack (key j visible to query i iff both are in
+ * the same sequence and j <= i), R the rotate-half RoPE ([UN-2023] "OpenAI Triton kernels") at
+ * the token's position inside its sequence with angle pos * rope_base^(-2i/d), and q head h
+ * reading KV head h / (hq / hkv).  No T x T mask is formed: the work list bounds each tile.
+ * `ws` is device memory of at least pk_attn_fwd_workspace_bytes bytes (256-byte aligned). */
+pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *v,
+                      int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float rope_base,
+                      void *out, float *lse, void *ws, size_t ws_bytes, void *hip_stream);
+
+/* Workspace bytes pk_attn_bwd needs: rotated Q and K, the RoPE table and rowsum(dout * out). */
+size_t pk_attn_bwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d);
+
+/* Backward of pk_attn_fwd for the loss sum(out * dout): float32 dq [T,hq,d], dk and dv
+ * [T,hkv,d] (dk, dv summed over the query heads of each KV group).  `out` and `lse` are the
+ * forward's outputs for the same inputs.  dq, dk and dv are fully overwritten. */
+pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *v,
+                      const void *out, const float *lse, const void *dout,
+                      int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float rope_base,
+                      float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
+                      void *hip_stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *pk_status_str(pk_status status);
+
+/* ---- Kernel timing (for benchmarks; off by default) -------------------------------------
+ * While enabled, every launch of the library records a pair of HIP events around it on its
+ * stream (no synchronisation).  pk_prof_query synchronises on the recorded events and returns
+ * the total milliseconds and launch count of one kernel kind since the last reset. */
+typedef enum pk_kernel_kind {
+    PK_K_META = 0,        /* all metadata-build kernels of one pk_build_meta */
+    PK_K_FWD_PREP = 1,    /* forward prologue: RoPE table + rotated K */
+    PK_K_FWD = 2,         /* forward attention */
+    PK_K_BWD_PREP = 3,    /* backward prologue: RoPE table, rotated Q/K, rowsum(dout*out), dq := 0 */
+    PK_K_BWD = 4,         /* backward attention (dK, dV, dQ accumulation) */
+    PK_K_BWD_POST = 5,    /* backward epilogue: inverse RoPE on dq */
+    PK_K_COUNT = 6
+} pk_kernel_kind;
+
+pk_status pk_prof_enable(int32_t on);
+pk_status pk_prof_reset(void);
+pk_status pk_prof_query(int32_t kind, double *total_ms /* host */, int64_t *launches /* host */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PK_H */

@@ -1,0 +1,235 @@
+"""Packed-sequence causal attention for MI355X: Python binding of libpk.so.
+
+Argument marshalling only: every step of the attention path runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.
+
+    meta = build_meta(lengths_int32_cuda, total_tokens)           # once per pack
+    out, lse = attn_fwd(meta, q, k, v)                              # every layer
+    dq, dk, dv = attn_bwd(meta, q, k, v, out, lse, dout)            # every layer
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import PkError, lib
+
+__all__ = ["PackedMeta", "build_meta", "attn_fwd", "attn_bwd", "fwd_workspace", "bwd_workspace",
+           "PackedCausalAttention", "PkError", "tile_rows", "prof_enable", "prof_reset",
+           "prof_query"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream) -> ctypes.c_void_p:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def tile_rows() -> int:
+    return int(lib().pk_tile_rows())
+
+
+class PackedMeta:
+    """B for one pack: a libpk handle plus the device buffer it lives in (kept alive here)."""
+
+    def __init__(self, handle: ctypes.c_void_p, buf, lengths, total_tokens: int, n_seqs: int):
+        self._handle = handle
+        self.buf = buf
+        self.lengths = lengths
+        self.total_tokens = total_tokens
+        self.n_seqs = n_seqs
+        self.device = buf.device
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._handle is None:
+            raise RuntimeError("meta already destroyed")
+        return self._handle
+
+    def view(self) -> dict:
+        """Device tensors aliasing B: cu_seqlens, max_seqlen, status, seq_id, pos, fwd/bwd items."""
+        torch = _torch()
+        v = _lib.MetaView()
+        _lib.check("pk_meta_view", lib().pk_meta_view(self.handle, ctypes.byref(v)))
+        base = self.buf.data_ptr()
+        as32 = self.buf.view(torch.int32)
+
+        def sl(ptr, n):
+            off = (ptr - base) // 4
+            return as32[off:off + n]
+
+        return {
+            "cu_seqlens": sl(v.cu_seqlens, v.n_seqs + 1),
+            "max_seqlen": sl(v.max_seqlen, 1),
+            "status": sl(v.status, 1),
+            "seq_id": sl(v.seq_id, v.total_tokens),
+            "pos": sl(v.pos, v.total_tokens),
+            "fwd_items": sl(v.fwd_items, v.n_items * 8).view(v.n_items, 8),
+            "bwd_items": sl(v.bwd_items, v.n_items * 8).view(v.n_items, 8),
+            "n_items": v.n_items,
+        }
+
+    def check(self, stream=None) -> Tuple[int, int]:
+        """(status word, max_seqlen).  SYNCHRONISES the stream: debugging and tests only."""
+        st, mx = ctypes.c_int32(0), ctypes.c_int32(0)
+        rc = lib().pk_meta_check(self.handle, _stream_ptr(stream), ctypes.byref(st), ctypes.byref(mx))
+        if rc not in (_lib.PK_OK, _lib.PK_ERR_DEVICE):
+            _lib.check("pk_meta_check", rc)
+        return int(st.value), int(mx.value)
+
+    def close(self) -> None:
+        if self._handle is not None:
+            lib().pk_meta_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def build_meta(lengths, total_tokens: Optional[int] = None, stream=None) -> PackedMeta:
+    """Build B on the device from int32 `lengths` (a CUDA tensor).  `total_tokens` is T, the
+    token count of the pack as the caller's q/k/v hold it (never read back from the device)."""
+    torch = _torch()
+    if lengths.dtype != torch.int32 or not lengths.is_cuda or lengths.dim() != 1:
+        raise ValueError("lengths must be a 1-D int32 CUDA tensor")
+    lengths = lengths.contiguous()
+    n = int(lengths.numel())
+    if total_tokens is None:
+        raise ValueError("total_tokens must be given (it is host-known: q.shape[0])")
+    nbytes = int(lib().pk_meta_bytes(n, int(total_tokens)))
+    if nbytes == 0:
+        raise PkError("pk_meta_bytes", _lib.PK_ERR_INVALID)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=lengths.device)
+    h = ctypes.c_void_p()
+    rc = lib().pk_build_meta(_ptr(lengths), n, int(total_tokens), _ptr(buf), nbytes,
+                             _stream_ptr(stream), ctypes.byref(h))
+    _lib.check("pk_build_meta", rc)
+    return PackedMeta(h, buf, lengths, int(total_tokens), n)
+
+
+def _dims(q, k):
+    t, hq, d = q.shape
+    return int(t), int(hq), int(k.shape[1]), int(d)
+
+
+def fwd_workspace(meta: PackedMeta, hq: int, hkv: int, d: int):
+    torch = _torch()
+    n = int(lib().pk_attn_fwd_workspace_bytes(meta.handle, hq, hkv, d))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=meta.device)
+
+
+def bwd_workspace(meta: PackedMeta, hq: int, hkv: int, d: int):
+    torch = _torch()
+    n = int(lib().pk_attn_bwd_workspace_bytes(meta.handle, hq, hkv, d))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=meta.device)
+
+
+def _check_inputs(meta, *tensors):
+    torch = _torch()
+    for t in tensors:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous CUDA tensors")
+        if t.device != meta.device:
+            raise ValueError("tensor on %s, meta on %s" % (t.device, meta.device))
+
+
+def attn_fwd(meta: PackedMeta, q, k, v, softmax_scale: Optional[float] = None,
+             rope_base: float = 10000.0, out=None, lse=None, workspace=None, stream=None):
+    """(out bf16 [T,hq,d], lse float32 [hq,T]) for bf16 q [T,hq,d], k, v [T,hkv,d]."""
+    torch = _torch()
+    t, hq, hkv, d = _dims(q, k)
+    _check_inputs(meta, q, k, v)
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("q, k, v must be bfloat16")
+    if t != meta.total_tokens or k.shape != v.shape or k.shape[0] != t or k.shape[2] != d:
+        raise ValueError("shape mismatch with the pack")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((hq, t), dtype=torch.float32, device=q.device) if lse is None else lse
+    ws = fwd_workspace(meta, hq, hkv, d) if workspace is None else workspace
+    rc = lib().pk_attn_fwd(meta.handle, _ptr(q), _ptr(k), _ptr(v), hq, hkv, d, scale,
+                           float(rope_base), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                           _stream_ptr(stream))
+    _lib.check("pk_attn_fwd", rc)
+    return out, lse
+
+
+def attn_bwd(meta: PackedMeta, q, k, v, out, lse, dout, softmax_scale: Optional[float] = None,
+             rope_base: float = 10000.0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dq, dk, dv) float32 for the loss sum(out * dout)."""
+    torch = _torch()
+    t, hq, hkv, d = _dims(q, k)
+    _check_inputs(meta, q, k, v, out, lse, dout)
+    if t != meta.total_tokens or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch with the pack")
+    if dout.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or lse.dtype != torch.float32:
+        raise ValueError("out/dout must be bfloat16 and lse float32")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    ws = bwd_workspace(meta, hq, hkv, d) if workspace is None else workspace
+    rc = lib().pk_attn_bwd(meta.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                           hq, hkv, d, scale, float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv),
+                           _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _lib.check("pk_attn_bwd", rc)
+    return dq, dk, dv
+
+
+def prof_enable(on: bool = True) -> None:
+    _lib.check("pk_prof_enable", lib().pk_prof_enable(1 if on else 0))
+
+
+def prof_reset() -> None:
+    _lib.check("pk_prof_reset", lib().pk_prof_reset())
+
+
+def prof_query(kind: str) -> Tuple[float, int]:
+    """(total ms, launches) of one kernel kind since the last reset (synchronises on events)."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _lib.check("pk_prof_query", lib().pk_prof_query(_lib.KERNEL_KINDS[kind], ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)
+
+
+class PackedCausalAttention:
+    """torch.autograd.Function over pk_attn_fwd / pk_attn_bwd (gradients cast to the inputs'
+    bfloat16 by torch).  Use `PackedCausalAttention.apply(q, k, v, meta, scale, rope_base)`."""
+
+    _fn = None
+
+    @classmethod
+    def apply(cls, q, k, v, meta: PackedMeta, softmax_scale=None, rope_base: float = 10000.0):
+        if cls._fn is None:
+            torch = _torch()
+
+            class _F(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, q, k, v, meta, softmax_scale, rope_base):
+                    out, lse = attn_fwd(meta, q, k, v, softmax_scale, rope_base)
+                    ctx.save_for_backward(q, k, v, out, lse)
+                    ctx.meta, ctx.scale, ctx.base = meta, softmax_scale, rope_base
+                    return out
+
+                @staticmethod
+                def backward(ctx, dout):
+                    q, k, v, out, lse = ctx.saved_tensors
+                    dq, dk, dv = attn_bwd(ctx.meta, q, k, v, out, lse,
+                                          dout.to(torch.bfloat16).contiguous(), ctx.scale, ctx.base)
+                    return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None
+
+            cls._fn = _F
+        return cls._fn.apply(q, k, v, meta, softmax_scale, rope_base)

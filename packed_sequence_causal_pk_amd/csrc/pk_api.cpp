@@ -1,0 +1,304 @@
+// C-ABI layer of libpk: argument validation, buffer carving, launches, optional kernel timing.
+// Every check here runs on the host before anything is enqueued; nothing here waits on the
+// device except pk_meta_check and pk_prof_query, which say so in pk.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <new>
+#include <vector>
+
+#include "pk_internal.h"
+
+namespace {
+
+bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool shape_supported(int hq, int hkv, int d) {
+    if (d != 64 && d != 128) return false;
+    if (hkv < 1 || hq < hkv || hq > 256) return false;
+    return hq % hkv == 0;
+}
+
+// ------------------------------------------------------------------ kernel timing (optional)
+struct ProfRecord {
+    int kind;
+    hipEvent_t start, stop;
+};
+struct Prof {
+    bool on = false;
+    std::vector<hipEvent_t> pool;   // created once, reused after a reset
+    std::vector<ProfRecord> recs;
+    size_t used = 0;
+};
+Prof g_prof;
+constexpr size_t kProfCapacity = 16384;  // event pairs
+
+struct ProfScope {
+    ProfRecord *rec = nullptr;
+    hipStream_t stream;
+    ProfScope(int kind, hipStream_t s) : stream(s) {
+        if (!g_prof.on || g_prof.used >= kProfCapacity) return;
+        ProfRecord r;
+        r.kind = kind;
+        r.start = g_prof.pool[2 * g_prof.used];
+        r.stop = g_prof.pool[2 * g_prof.used + 1];
+        if (hipEventRecord(r.start, s) != hipSuccess) return;
+        g_prof.recs.push_back(r);
+        rec = &g_prof.recs.back();
+        ++g_prof.used;
+    }
+    ~ProfScope() {
+        if (rec) (void)hipEventRecord(rec->stop, stream);
+    }
+};
+
+pk_status hip_status(hipError_t e) { return e == hipSuccess ? PK_OK : PK_ERR_HIP; }
+
+bool on_meta_device(const pk_meta_s *m) {
+    int dev = -1;
+    return hipGetDevice(&dev) == hipSuccess && dev == m->device;
+}
+
+}  // namespace
+
+namespace pk {
+
+FwdWorkspace fwd_workspace(int64_t T, int hq, int hkv, int d) {
+    (void)hq;
+    FwdWorkspace w;
+    size_t off = 0;
+    w.krot = off; off += align256((size_t)T * hkv * d * 2);
+    w.rope = off; off += align256((size_t)T * (d / 2) * 8);
+    w.total = off;
+    return w;
+}
+
+BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d) {
+    BwdWorkspace w;
+    size_t off = 0;
+    w.qrot = off; off += align256((size_t)T * hq * d * 2);
+    w.krot = off; off += align256((size_t)T * hkv * d * 2);
+    w.rope = off; off += align256((size_t)T * (d / 2) * 8);
+    w.dsum = off; off += align256((size_t)T * hq * 4);
+    w.total = off;
+    return w;
+}
+
+}  // namespace pk
+
+extern "C" {
+
+int32_t pk_tile_rows(void) { return PK_TILE_ROWS; }
+
+size_t pk_meta_bytes(int32_t n_seqs, int64_t total_tokens) {
+    if (n_seqs < 0 || total_tokens < 0 || total_tokens > PK_MAX_TOKENS || n_seqs > total_tokens) return 0;
+    return pk::meta_layout(n_seqs, total_tokens).total;
+}
+
+pk_status pk_build_meta(const int32_t *lengths_dev, int32_t n_seqs, int64_t total_tokens,
+                        void *meta_buf_dev, size_t meta_buf_bytes, void *hip_stream,
+                        pk_meta_t *out) {
+    if (!out) return PK_ERR_INVALID;
+    *out = nullptr;
+    if (n_seqs < 0 || total_tokens < 0 || n_seqs > total_tokens) return PK_ERR_INVALID;
+    if (total_tokens > PK_MAX_TOKENS) return PK_ERR_UNSUPPORTED;
+    if (n_seqs > 0 && !lengths_dev) return PK_ERR_INVALID;
+    if (!meta_buf_dev || !aligned256(meta_buf_dev)) return PK_ERR_INVALID;
+    const pk::MetaLayout L = pk::meta_layout(n_seqs, total_tokens);
+    if (meta_buf_bytes < L.total) return PK_ERR_CAPACITY;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return PK_ERR_HIP;
+
+    pk_meta_s *m = new (std::nothrow) pk_meta_s;
+    if (!m) return PK_ERR_INVALID;
+    char *base = static_cast<char *>(meta_buf_dev);
+    m->hdr = reinterpret_cast<int32_t *>(base + L.hdr);
+    m->cu = reinterpret_cast<int32_t *>(base + L.cu);
+    m->seq_id = reinterpret_cast<int32_t *>(base + L.seq_id);
+    m->pos = reinterpret_cast<int32_t *>(base + L.pos);
+    m->fwd_items = reinterpret_cast<int32_t *>(base + L.fwd_items);
+    m->bwd_items = reinterpret_cast<int32_t *>(base + L.bwd_items);
+    m->fwd_raw = reinterpret_cast<int32_t *>(base + L.fwd_raw);
+    m->bwd_raw = reinterpret_cast<int32_t *>(base + L.bwd_raw);
+    m->n_seqs = n_seqs;
+    m->total_tokens = total_tokens;
+    m->n_items = (int32_t)pk::n_tiles(total_tokens);
+    m->device = dev;
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e;
+    {
+        ProfScope ps(PK_K_META, s);
+        e = pk::launch_meta(lengths_dev, *m, s);
+    }
+    if (e != hipSuccess) {
+        delete m;
+        return PK_ERR_HIP;
+    }
+    *out = m;
+    return PK_OK;
+}
+
+pk_status pk_meta_view(pk_meta_t meta, pk_meta_view_t *view) {
+    if (!meta || !view) return PK_ERR_INVALID;
+    view->cu_seqlens = meta->cu;
+    view->max_seqlen = meta->hdr + 1;
+    view->status = meta->hdr;
+    view->seq_id = meta->seq_id;
+    view->pos = meta->pos;
+    view->fwd_items = meta->fwd_items;
+    view->bwd_items = meta->bwd_items;
+    view->n_seqs = meta->n_seqs;
+    view->n_items = meta->n_items;
+    view->total_tokens = meta->total_tokens;
+    view->device = meta->device;
+    return PK_OK;
+}
+
+pk_status pk_meta_check(pk_meta_t meta, void *hip_stream, int32_t *status_host,
+                        int32_t *max_seqlen_host) {
+    if (!meta) return PK_ERR_INVALID;
+    if (!on_meta_device(meta)) return PK_ERR_INVALID;
+    int32_t hdr[2] = {0, 0};
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (hipMemcpyAsync(hdr, meta->hdr, sizeof(hdr), hipMemcpyDeviceToHost, s) != hipSuccess) return PK_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return PK_ERR_HIP;
+    if (status_host) *status_host = hdr[0];
+    if (max_seqlen_host) *max_seqlen_host = hdr[1];
+    return hdr[0] ? PK_ERR_DEVICE : PK_OK;
+}
+
+pk_status pk_meta_destroy(pk_meta_t meta) {
+    if (!meta) return PK_ERR_INVALID;
+    delete meta;
+    return PK_OK;
+}
+
+size_t pk_attn_fwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d) {
+    if (!meta || !shape_supported(hq, hkv, d)) return 0;
+    return pk::fwd_workspace(meta->total_tokens, hq, hkv, d).total;
+}
+
+size_t pk_attn_bwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d) {
+    if (!meta || !shape_supported(hq, hkv, d)) return 0;
+    return pk::bwd_workspace(meta->total_tokens, hq, hkv, d).total;
+}
+
+pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *v, int32_t hq,
+                      int32_t hkv, int32_t d, float softmax_scale, float rope_base, void *out,
+                      float *lse, void *ws, size_t ws_bytes, void *hip_stream) {
+    if (!meta) return PK_ERR_INVALID;
+    if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.f) || !(rope_base > 0.f)) return PK_ERR_INVALID;
+    const int64_t T = meta->total_tokens;
+    if (T == 0) return PK_OK;
+    if (!q || !k || !v || !out || !lse || !ws || !aligned256(ws)) return PK_ERR_INVALID;
+    const pk::FwdWorkspace W = pk::fwd_workspace(T, hq, hkv, d);
+    if (ws_bytes < W.total) return PK_ERR_CAPACITY;
+    if (!on_meta_device(meta)) return PK_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    char *w = static_cast<char *>(ws);
+    pk::RopeArgs ra{meta->pos, T, hq, hkv, d, rope_base};
+    hipError_t e;
+    {
+        ProfScope ps(PK_K_FWD_PREP, s);
+        e = pk::launch_fwd_prep(ra, k, w + W.krot, w + W.rope, s);
+    }
+    if (e != hipSuccess) return PK_ERR_HIP;
+    pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
+    {
+        ProfScope ps(PK_K_FWD, s);
+        e = pk::launch_fwd(sh, *meta, q, w + W.krot, v, w + W.rope, out, lse, s);
+    }
+    return hip_status(e);
+}
+
+pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *v,
+                      const void *out, const float *lse, const void *dout, int32_t hq,
+                      int32_t hkv, int32_t d, float softmax_scale, float rope_base, float *dq,
+                      float *dk, float *dv, void *ws, size_t ws_bytes, void *hip_stream) {
+    if (!meta) return PK_ERR_INVALID;
+    if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.f) || !(rope_base > 0.f)) return PK_ERR_INVALID;
+    const int64_t T = meta->total_tokens;
+    if (T == 0) return PK_OK;
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !ws || !aligned256(ws))
+        return PK_ERR_INVALID;
+    const pk::BwdWorkspace W = pk::bwd_workspace(T, hq, hkv, d);
+    if (ws_bytes < W.total) return PK_ERR_CAPACITY;
+    if (!on_meta_device(meta)) return PK_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    char *w = static_cast<char *>(ws);
+    float *dsum = reinterpret_cast<float *>(w + W.dsum);
+    pk::RopeArgs ra{meta->pos, T, hq, hkv, d, rope_base};
+    hipError_t e;
+    {
+        ProfScope ps(PK_K_BWD_PREP, s);
+        e = pk::launch_bwd_prep(ra, q, k, out, dout, w + W.qrot, w + W.krot, w + W.rope, dsum, dq, s);
+    }
+    if (e != hipSuccess) return PK_ERR_HIP;
+    pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
+    {
+        ProfScope ps(PK_K_BWD, s);
+        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, v, dout, lse, dsum, w + W.rope, dq, dk, dv, s);
+    }
+    if (e != hipSuccess) return PK_ERR_HIP;
+    {
+        ProfScope ps(PK_K_BWD_POST, s);
+        e = pk::launch_bwd_post(ra, w + W.rope, dq, s);
+    }
+    return hip_status(e);
+}
+
+const char *pk_status_str(pk_status status) {
+    switch (status) {
+        case PK_OK: return "ok";
+        case PK_ERR_INVALID: return "invalid argument";
+        case PK_ERR_UNSUPPORTED: return "unsupported shape";
+        case PK_ERR_CAPACITY: return "buffer too small";
+        case PK_ERR_HIP: return "HIP runtime error";
+        case PK_ERR_DEVICE: return "device status word set (invalid pack lengths)";
+    }
+    return "unknown status";
+}
+
+pk_status pk_prof_enable(int32_t on) {
+    if (on && g_prof.pool.empty()) {
+        g_prof.pool.resize(2 * kProfCapacity);
+        for (auto &ev : g_prof.pool)
+            if (hipEventCreate(&ev) != hipSuccess) {
+                g_prof.pool.clear();
+                return PK_ERR_HIP;
+            }
+        g_prof.recs.reserve(kProfCapacity);
+    }
+    g_prof.on = on != 0;
+    return PK_OK;
+}
+
+pk_status pk_prof_reset(void) {
+    g_prof.recs.clear();
+    g_prof.used = 0;
+    return PK_OK;
+}
+
+pk_status pk_prof_query(int32_t kind, double *total_ms, int64_t *launches) {
+    if (!total_ms || !launches || kind < 0 || kind >= PK_K_COUNT) return PK_ERR_INVALID;
+    double sum = 0.0;
+    int64_t n = 0;
+    for (const ProfRecord &r : g_prof.recs) {
+        if (r.kind != kind) continue;
+        if (hipEventSynchronize(r.stop) != hipSuccess) return PK_ERR_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return PK_ERR_HIP;
+        sum += ms;
+        ++n;
+    }
+    *total_ms = sum;
+    *launches = n;
+    return PK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,253 @@
+// Forward attention over a packed batch on gfx950 matrix cores.
+//
+// Computes, for every query row i and query head h ([UN-2023] "Introducing Unsloth：LLM 训练提速
+// 30 倍", "手动 Autograd", read with the scale 1/sqrt(d)):
+//     out[i, h] = sum_j softmax_j(scale * <R q_i, R k_j> + M_ij) v_j,   lse[h, i] = log sum_j exp(.)
+// with M_ij = 0 when j lies in i's packed sequence and j <= i, else -inf.  M is never formed:
+// the forward work list gives each 128-query tile the key range [start of its first sequence,
+// end of the tile], and inside that range only tiles that straddle a sequence boundary or the
+// diagonal are masked, element by element, from each query's sequence start lo_i = i - pos_i.
+//
+// Design ([N1N-2026] "利用 Unsloth 和 NVIDIA 硬件加速 LLM 训练", §2 "FlashAttention-2 的深度集成":
+// tiles stay on chip, softmax is fused with the two products, no N x N matrix is stored),
+// laid out for CDNA4:
+//   * one workgroup = one work item (128 queries) x one query head; 4 waves of 32 queries;
+//     items are taken in the work list's longest-first order, heads fastest;
+//   * the scores are computed transposed, S^T = K_rot Q_rot^T, with v_mfma_f32_32x32x16_bf16,
+//     so each lane of a wave owns one query: the row max needs one cross-half exchange and the
+//     O^T accumulator is rescaled with a per-lane factor;
+//   * P^T stays in registers and is the k operand of O^T += V^T P^T; key rows of the first
+//     product are fed in row_perm order so the V^T operand is one 16-byte LDS read per lane;
+//   * K_rot and V tiles of 64 keys are staged in LDS (V transposed) and read by all 4 waves;
+//   * online softmax in the exp2 domain with scale * log2(e) folded into the scores;
+//   * Q is rotated in the prologue from the per-call (cos, sin) table; K comes pre-rotated.
+#include "pk_internal.h"
+#include "pk_device.h"
+
+namespace {
+
+using namespace pkd;
+
+struct FwdArgs {
+    const bf16 *q;        // [T, hq, D]
+    const bf16 *krot;     // [T, hkv, D]
+    const bf16 *v;        // [T, hkv, D]
+    const float2 *rope;   // [T, D/2] (cos, sin)
+    const int32_t *items; // [n_items, 8] longest first
+    const int32_t *pos;   // [T]
+    const int32_t *hdr;   // status, max_seqlen
+    bf16 *out;            // [T, hq, D]
+    float *lse;           // [hq, T]
+    int64_t T;
+    int hq, hkv, group;
+    float scale_log2;     // softmax scale * log2(e)
+};
+
+template <int D>
+__device__ void fwd_zero_tile(const FwdArgs &a, int tile, int h) {
+    const int64_t r0 = (int64_t)tile * PK_TILE_ROWS;
+    for (int e = threadIdx.x; e < PK_TILE_ROWS * (D / 8); e += blockDim.x) {
+        const int64_t i = r0 + e / (D / 8);
+        if (i < a.T) store_bf16x8(a.out + (i * a.hq + h) * D + (e % (D / 8)) * 8, zero_bf16x8());
+    }
+    for (int e = threadIdx.x; e < PK_TILE_ROWS; e += blockDim.x)
+        if (r0 + e < a.T) a.lse[(int64_t)h * a.T + r0 + e] = 0.f;
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
+    constexpr int BK = 64;        // keys per LDS tile
+    constexpr int KP = D + 8;     // lds_k row pitch (bf16): rows start 4 banks apart
+    constexpr int VP = BK + 8;    // lds_vt row pitch
+    constexpr int NKK = D / 16;   // k-steps of the score product
+    constexpr int NDB = D / 32;   // 32-row blocks of O^T
+    constexpr int NMB = BK / 32;  // 32-key blocks per tile
+    __shared__ __attribute__((aligned(16))) bf16 lds_k[BK * KP];
+    __shared__ __attribute__((aligned(16))) bf16 lds_vt[D * VP];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n32 = lane & 31, hb = lane >> 5;
+    const int r = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
+    const int kvh = h / a.group;
+    const int32_t *it = a.items + (int64_t)r * PK_ITEM_FIELDS;
+    if (a.hdr[0] != 0) {
+        fwd_zero_tile<D>(a, it[7], h);
+        return;
+    }
+    const int q_start = it[0], q_end = it[1], kv_start = it[2];
+    const int64_t T = a.T;
+
+    // this lane's query and its wave's query range
+    const int i = q_start + 32 * w + n32;
+    const bool qvalid = i < q_end;
+    const int lo_i = qvalid ? i - a.pos[i] : 0;
+    const int wq0 = q_start + 32 * w;
+    const bool wave_active = wq0 < q_end;
+    const int wq_last = min(wq0 + 31, q_end - 1);
+    const int wlo_min = wave_active ? wq0 - a.pos[wq0] : 0;
+    const int wlo_max = wave_active ? wq_last - a.pos[wq_last] : 0;
+
+    // Q fragments (k operand of S^T = K Q^T), rotated in registers.  Chunk kk holds
+    // d in [16kk + 8hb, +8); chunk kk + NKK/2 holds the RoPE partners d + D/2.
+    bf16x8 qf[NKK];
+    {
+        const bf16 *qrow = a.q + ((int64_t)(qvalid ? i : q_start) * a.hq + h) * D;
+        const float2 *cs = a.rope + (int64_t)(qvalid ? i : q_start) * (D / 2);
+#pragma unroll
+        for (int kk = 0; kk < NKK / 2; ++kk) {
+            const int d0 = 16 * kk + 8 * hb;
+            const bf16x8 x1 = load_bf16x8(qrow + d0);
+            const bf16x8 x2 = load_bf16x8(qrow + d0 + D / 2);
+            bf16x8 y1, y2;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const float2 f = cs[d0 + s];
+                const float a1 = (float)x1[s], a2 = (float)x2[s];
+                y1[s] = (bf16)(qvalid ? a1 * f.x - a2 * f.y : 0.f);
+                y2[s] = (bf16)(qvalid ? a2 * f.x + a1 * f.y : 0.f);
+            }
+            qf[kk] = y1;
+            qf[kk + NKK / 2] = y2;
+        }
+    }
+
+    float m = -INFINITY;  // running max of this query's scores (log2 domain)
+    float l = 0.f;        // running sum of exp2(s - m) over this lane's half of the keys
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = zero_f32x16();
+
+    const int kb_hi = ((q_end - 1) / BK) * BK;
+    const int kb_lo = (kv_start / BK) * BK;
+    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= BK) {
+        __syncthreads();
+        // K_rot tile -> lds_k [BK][D] (rows past T are zero)
+        for (int e = tid; e < BK * (D / 8); e += 256) {
+            const int row = e / (D / 8), ch = e % (D / 8);
+            const int64_t j = k0 + row;
+            const bf16x8 val = j < T ? load_bf16x8(a.krot + (j * a.hkv + kvh) * D + ch * 8) : zero_bf16x8();
+            store_bf16x8(lds_k + row * KP + ch * 8, val);
+        }
+        // V tile -> lds_vt [D][BK] (transposed), two keys per 32-bit LDS store
+        for (int e = tid; e < (BK / 2) * (D / 8); e += 256) {
+            const int kp = e % (BK / 2), ch = e / (BK / 2);
+            const int64_t j0 = k0 + 2 * kp;
+            const bf16x8 v0 = j0 < T ? load_bf16x8(a.v + (j0 * a.hkv + kvh) * D + ch * 8) : zero_bf16x8();
+            const bf16x8 v1 = j0 + 1 < T ? load_bf16x8(a.v + ((j0 + 1) * a.hkv + kvh) * D + ch * 8) : zero_bf16x8();
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                *reinterpret_cast<uint32_t *>(lds_vt + (ch * 8 + s) * VP + 2 * kp) = pack_bf16x2(v0[s], v1[s]);
+        }
+        __syncthreads();
+        if (!wave_active) continue;
+        if (k0 > wq_last) continue;            // every key is after every query of the wave
+        if (k0 + BK - 1 < wlo_min) continue;   // every key is before the wave's first sequence
+        const bool need_mask = !(k0 + BK - 1 <= wq0 && k0 >= wlo_max);
+
+        // S^T (keys x queries), key rows in row_perm order
+        f32x16 s[NMB];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+            s[mb] = zero_f32x16();
+            const bf16 *krow = lds_k + (32 * mb + row_perm(n32)) * KP + 8 * hb;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) s[mb] = mfma32(load_bf16x8(krow + 16 * kk), qf[kk], s[mb]);
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                float x = s[mb][rr] * a.scale_log2;
+                if (need_mask) {
+                    const int j = k0 + 32 * mb + row_perm(acc_row(rr, hb));
+                    x = (qvalid && j >= lo_i && j <= i) ? x : -INFINITY;
+                }
+                s[mb][rr] = x;
+                tmax = fmaxf(tmax, x);
+            }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m, tmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m - m_use);
+        m = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const float p = exp2f(s[mb][rr] - m_use);
+                s[mb][rr] = p;
+                psum += p;
+            }
+        }
+        l = l * alpha + psum;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+
+        // O^T (d x queries) += V^T (d x keys) * P^T (keys x queries)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                bf16x8 pb;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) pb[x] = (bf16)s[mb][8 * e + x];
+                const bf16 *vrow = lds_vt + n32 * VP + 32 * mb + 16 * e + 8 * hb;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) o[db] = mfma32(load_bf16x8(vrow + 32 * db * VP), pb, o[db]);
+            }
+        }
+    }
+
+    // epilogue: O = O^T / l, lse = ln(sum) of the scaled scores
+    const float l_tot = l + __shfl_xor(l, 32, 64);
+    if (qvalid) {
+        const float inv = 1.f / l_tot;
+        bf16 *orow = a.out + ((int64_t)i * a.hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = 32 * db + 8 * g4 + 4 * hb;
+                uint2 raw;
+                raw.x = pack_bf16x2((bf16)(o[db][4 * g4 + 0] * inv), (bf16)(o[db][4 * g4 + 1] * inv));
+                raw.y = pack_bf16x2((bf16)(o[db][4 * g4 + 2] * inv), (bf16)(o[db][4 * g4 + 3] * inv));
+                *reinterpret_cast<uint2 *>(orow + d) = raw;
+            }
+        }
+        if (hb == 0) a.lse[(int64_t)h * T + i] = (m + log2f(l_tot)) * kLn2;
+    }
+}
+
+}  // namespace
+
+namespace pk {
+
+hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, const void *krot,
+                      const void *v, const void *rope, void *out, float *lse, hipStream_t s) {
+    FwdArgs a;
+    a.q = (const bf16 *)q;
+    a.krot = (const bf16 *)krot;
+    a.v = (const bf16 *)v;
+    a.rope = (const float2 *)rope;
+    a.items = m.fwd_items;
+    a.pos = m.pos;
+    a.hdr = m.hdr;
+    a.out = (bf16 *)out;
+    a.lse = lse;
+    a.T = sh.T;
+    a.hq = sh.hq;
+    a.hkv = sh.hkv;
+    a.group = sh.hq / sh.hkv;
+    a.scale_log2 = sh.scale * pkd::kLog2e;
+    const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hq;
+    if (sh.d == 128)
+        k_attn_fwd<128><<<grid, 256, 0, s>>>(a);
+    else
+        k_attn_fwd<64><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace pk

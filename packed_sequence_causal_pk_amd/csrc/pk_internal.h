@@ -1,0 +1,73 @@
+// Internal interface between the C-ABI layer (pk_api.cpp) and the HIP kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pk.h"
+
+// The host object behind pk_meta_t: pointers into the caller's meta buffer plus the sizes the
+// host already knows (so no launch ever needs a device read to size its grid).
+struct pk_meta_s {
+    int32_t *hdr;        // [0] = status bits, [1] = max_seqlen
+    int32_t *cu;         // [n_seqs + 1]
+    int32_t *seq_id;     // [T]
+    int32_t *pos;        // [T]
+    int32_t *fwd_items;  // [n_items * 8], longest first
+    int32_t *bwd_items;  // [n_items * 8], longest first
+    int32_t *fwd_raw;    // [n_items * 8], tile order (build scratch)
+    int32_t *bwd_raw;    // [n_items * 8], tile order (build scratch)
+    int32_t n_seqs;
+    int32_t n_items;
+    int64_t total_tokens;
+    int32_t device;
+};
+
+namespace pk {
+
+// Byte layout of the meta buffer; every region starts on a 256-byte boundary.
+struct MetaLayout {
+    size_t hdr, cu, seq_id, pos, fwd_items, bwd_items, fwd_raw, bwd_raw, total;
+};
+MetaLayout meta_layout(int32_t n_seqs, int64_t total_tokens);
+
+// Byte layout of the attention workspaces.
+struct FwdWorkspace {
+    size_t krot, rope, total;
+};
+struct BwdWorkspace {
+    size_t qrot, krot, rope, dsum, total;
+};
+FwdWorkspace fwd_workspace(int64_t T, int hq, int hkv, int d);
+BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d);
+
+inline int64_t n_tiles(int64_t T) { return (T + PK_TILE_ROWS - 1) / PK_TILE_ROWS; }
+
+// Launchers.  Each enqueues its kernels on `stream` and returns the launch status.
+hipError_t launch_meta(const int32_t *lengths, const pk_meta_s &m, hipStream_t stream);
+
+struct RopeArgs {
+    const int32_t *pos;
+    int64_t T;
+    int hq, hkv, d;
+    float rope_base;
+};
+hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, void *krot, void *rope, hipStream_t s);
+hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *out,
+                           const void *dout, void *qrot, void *krot, void *rope, float *dsum,
+                           float *dq, hipStream_t s);
+hipError_t launch_bwd_post(const RopeArgs &r, const void *rope, float *dq, hipStream_t s);
+
+struct AttnShape {
+    int64_t T;
+    int hq, hkv, d, n_items;
+    float scale;
+};
+hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, const void *krot,
+                      const void *v, const void *rope, void *out, float *lse, hipStream_t s);
+hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
+                      const void *krot, const void *v, const void *dout, const float *lse,
+                      const float *dsum, const void *rope, float *dq, float *dk, float *dv,
+                      hipStream_t s);
+
+}  // namespace pk

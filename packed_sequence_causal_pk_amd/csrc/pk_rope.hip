@@ -1,0 +1,212 @@
+// Prologue and epilogue passes of the attention calls: the RoPE rotation table, rotated K (and Q
+// for the backward), rowsum(dout * out), and the inverse rotation of dq.
+//
+// Rotate-half RoPE ([UN-2023] "Introducing Unsloth：LLM 训练提速 30 倍", "OpenAI Triton kernels"):
+// with x1 the first half of a head vector and x2 the second half,
+//     R(x) = [x1 cos - x2 sin, x2 cos + x1 sin],
+// and its backward is the transpose, sin -> -sin.  The angle of pair i at position p is
+// p * base^(-2i/d); p restarts at 0 in every packed sequence ([UN-2026] §1: positions come from
+// the pack's metadata).  The factors are computed once per call into a [T, d/2] table of
+// (cos, sin), the "rotation factors served from a precomputed table" idea of
+// [MV] "UnSloth极速微调：底层CUDA优化带来的变革", and read by the attention kernels instead of
+// evaluating sin/cos in their loops.
+//
+// Thread layout of all three kernels: one thread per (token t, group c of 4 rotation pairs);
+// the thread owns elements d in [4c, 4c+4) and their partners d + D/2 for every head, so each
+// rotation stays inside one thread and a token's D/8 threads read each half-row contiguously.
+#include "pk_internal.h"
+#include "pk_device.h"
+
+namespace {
+
+using pkd::zero_bf16x8;
+
+template <int D>
+__device__ __forceinline__ void rope_factors(const int32_t *__restrict__ pos, int64_t t, int c,
+                                             float base, float2 *__restrict__ table, float cs[4],
+                                             float sn[4]) {
+    const double p = (double)pos[t];
+    const double lb = log2((double)base);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = 4 * c + k;
+        const double inv_freq = exp2(-(2.0 * i / D) * lb);
+        double s, co;
+        sincos(p * inv_freq, &s, &co);
+        cs[k] = (float)co;
+        sn[k] = (float)s;
+    }
+    float4 *dst = reinterpret_cast<float4 *>(table + t * (D / 2) + 4 * c);
+    dst[0] = make_float4(cs[0], sn[0], cs[1], sn[1]);
+    dst[1] = make_float4(cs[2], sn[2], cs[3], sn[3]);
+}
+
+__device__ __forceinline__ void load4(const bf16 *p, float x[4]) {
+    const uint2 raw = *reinterpret_cast<const uint2 *>(p);
+    const bf16 *b = reinterpret_cast<const bf16 *>(&raw);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = (float)b[k];
+}
+
+__device__ __forceinline__ void store4(bf16 *p, const float x[4]) {
+    uint2 raw;
+    raw.x = pkd::pack_bf16x2((bf16)x[0], (bf16)x[1]);
+    raw.y = pkd::pack_bf16x2((bf16)x[2], (bf16)x[3]);
+    *reinterpret_cast<uint2 *>(p) = raw;
+}
+
+// Rotate 4 pairs of one head row: row points at the head's element 0.
+template <int D>
+__device__ __forceinline__ void rotate_row(const bf16 *__restrict__ src, bf16 *__restrict__ dst,
+                                           int c, const float cs[4], const float sn[4]) {
+    float x1[4], x2[4], y1[4], y2[4];
+    load4(src + 4 * c, x1);
+    load4(src + D / 2 + 4 * c, x2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        y1[k] = x1[k] * cs[k] - x2[k] * sn[k];
+        y2[k] = x2[k] * cs[k] + x1[k] * sn[k];
+    }
+    store4(dst + 4 * c, y1);
+    store4(dst + D / 2 + 4 * c, y2);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_fwd_prep(const int32_t *__restrict__ pos, int64_t T,
+                                                  int hkv, float base,
+                                                  const bf16 *__restrict__ k,
+                                                  bf16 *__restrict__ krot,
+                                                  float2 *__restrict__ table) {
+    constexpr int G = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = gid / G;
+    const int c = (int)(gid % G);
+    if (t >= T) return;
+    float cs[4], sn[4];
+    rope_factors<D>(pos, t, c, base, table, cs, sn);
+    for (int h = 0; h < hkv; ++h) {
+        const int64_t off = (t * hkv + h) * D;
+        rotate_row<D>(k + off, krot + off, c, cs, sn);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ pos, int64_t T,
+                                                  int hq, int hkv, float base,
+                                                  const bf16 *__restrict__ q,
+                                                  const bf16 *__restrict__ k,
+                                                  const bf16 *__restrict__ out,
+                                                  const bf16 *__restrict__ dout,
+                                                  bf16 *__restrict__ qrot,
+                                                  bf16 *__restrict__ krot,
+                                                  float2 *__restrict__ table,
+                                                  float *__restrict__ dsum,
+                                                  float *__restrict__ dq) {
+    constexpr int G = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = gid / G;
+    const int c = (int)(gid % G);
+    // T * G threads are launched in whole waves; the G threads of a token share a wave, so the
+    // shuffle reduction below only mixes lanes of the same token.  Threads past T exit together.
+    if (t >= T) return;
+    float cs[4], sn[4];
+    rope_factors<D>(pos, t, c, base, table, cs, sn);
+    for (int h = 0; h < hkv; ++h) {
+        const int64_t off = (t * hkv + h) * D;
+        rotate_row<D>(k + off, krot + off, c, cs, sn);
+    }
+    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int h = 0; h < hq; ++h) {
+        const int64_t off = (t * hq + h) * D;
+        rotate_row<D>(q + off, qrot + off, c, cs, sn);
+        float o1[4], o2[4], g1[4], g2[4];
+        load4(out + off + 4 * c, o1);
+        load4(out + off + D / 2 + 4 * c, o2);
+        load4(dout + off + 4 * c, g1);
+        load4(dout + off + D / 2 + 4 * c, g2);
+        float part = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) part += o1[kk] * g1[kk] + o2[kk] * g2[kk];
+#pragma unroll
+        for (int s = G / 2; s > 0; s >>= 1) part += __shfl_xor(part, s, 64);
+        if (c == 0) dsum[(int64_t)h * T + t] = part;
+        *reinterpret_cast<float4 *>(dq + off + 4 * c) = zero4;
+        *reinterpret_cast<float4 *>(dq + off + D / 2 + 4 * c) = zero4;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_post(int64_t T, int hq,
+                                                  const float2 *__restrict__ table,
+                                                  float *__restrict__ dq) {
+    constexpr int G = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = gid / G;
+    const int c = (int)(gid % G);
+    if (t >= T) return;
+    const float4 *tp = reinterpret_cast<const float4 *>(table + t * (D / 2) + 4 * c);
+    const float4 f01 = tp[0], f23 = tp[1];
+    const float cs[4] = {f01.x, f01.z, f23.x, f23.z};
+    const float sn[4] = {f01.y, f01.w, f23.y, f23.w};
+    for (int h = 0; h < hq; ++h) {
+        float *row = dq + (t * hq + h) * D;
+        const float4 a = *reinterpret_cast<const float4 *>(row + 4 * c);
+        const float4 b = *reinterpret_cast<const float4 *>(row + D / 2 + 4 * c);
+        const float x1[4] = {a.x, a.y, a.z, a.w};
+        const float x2[4] = {b.x, b.y, b.z, b.w};
+        float y1[4], y2[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            y1[k] = x1[k] * cs[k] + x2[k] * sn[k];
+            y2[k] = x2[k] * cs[k] - x1[k] * sn[k];
+        }
+        *reinterpret_cast<float4 *>(row + 4 * c) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+        *reinterpret_cast<float4 *>(row + D / 2 + 4 * c) = make_float4(y2[0], y2[1], y2[2], y2[3]);
+    }
+}
+
+unsigned grid_for(int64_t T, int d) { return (unsigned)((T * (d / 8) + 255) / 256); }
+
+}  // namespace
+
+namespace pk {
+
+hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, void *krot, void *rope,
+                           hipStream_t s) {
+    const unsigned g = grid_for(r.T, r.d);
+    if (r.d == 128)
+        k_fwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hkv, r.rope_base, (const bf16 *)k,
+                                           (bf16 *)krot, (float2 *)rope);
+    else
+        k_fwd_prep<64><<<g, 256, 0, s>>>(r.pos, r.T, r.hkv, r.rope_base, (const bf16 *)k,
+                                          (bf16 *)krot, (float2 *)rope);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *out,
+                           const void *dout, void *qrot, void *krot, void *rope, float *dsum,
+                           float *dq, hipStream_t s) {
+    const unsigned g = grid_for(r.T, r.d);
+    if (r.d == 128)
+        k_bwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
+                                           (const bf16 *)k, (const bf16 *)out,
+                                           (const bf16 *)dout, (bf16 *)qrot, (bf16 *)krot,
+                                           (float2 *)rope, dsum, dq);
+    else
+        k_bwd_prep<64><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
+                                          (const bf16 *)k, (const bf16 *)out,
+                                          (const bf16 *)dout, (bf16 *)qrot, (bf16 *)krot,
+                                          (float2 *)rope, dsum, dq);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_post(const RopeArgs &r, const void *rope, float *dq, hipStream_t s) {
+    const unsigned g = grid_for(r.T, r.d);
+    if (r.d == 128)
+        k_bwd_post<128><<<g, 256, 0, s>>>(r.T, r.hq, (const float2 *)rope, dq);
+    else
+        k_bwd_post<64><<<g, 256, 0, s>>>(r.T, r.hq, (const float2 *)rope, dq);
+    return hipGetLastError();
+}
+
+}  // namespace pk

@@ -1,0 +1,226 @@
+"""HIP path vs the float64 oracle on the GPU, through the C ABI (needs an MI355X).
+
+Metadata and work lists must match bit for bit; O, lse, dQ, dK, dV must match within the gate
+(max-abs 2e-2 and relative L2 1e-2 per tensor; lse max-abs 1e-2).  Full-size workloads are
+compared on whole sampled sequences and KV-head groups, which the oracle computes exactly
+because packed sequences are independent (a property the oracle's own pins establish)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import packed_sequence_causal_pk_amd as pk
+from oracle import pk_oracle as O
+from packed_sequence_causal_pk_amd import synth
+from tests.gpu_helpers import LSE_MAX_ABS, compare, dev, meta_to_np, run_pk, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _meta_matches_oracle(lengths, t):
+    ref = O.build_meta(lengths, t)
+    meta = pk.build_meta(torch.tensor(np.asarray(lengths, np.int32), device="cuda"), t)
+    got = meta_to_np(meta)
+    assert int(got["status"][0]) == ref["status"]
+    assert np.array_equal(got["cu_seqlens"], ref["cu_seqlens"])
+    assert int(got["max_seqlen"][0]) == ref["max_seqlen"]
+    assert np.array_equal(got["seq_id"], ref["seq_id"])
+    assert np.array_equal(got["pos"], ref["pos"])
+    assert np.array_equal(got["fwd_items"], ref["fwd_items"])
+    assert np.array_equal(got["bwd_items"], ref["bwd_items"])
+    return meta
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_meta_bit_exact_workloads(name):
+    say("meta", name)
+    w = synth.WORKLOADS[name]
+    _meta_matches_oracle(synth.pack_lengths(name), w.total_tokens)
+
+
+def test_meta_bit_exact_fuzz():
+    rng = np.random.default_rng(2024)
+    for trial in range(24):
+        hi = int(rng.choice([1, 2, 16, 200, 3000, 9000]))
+        n = int(rng.integers(1, 5000 if hi <= 200 else 60))
+        lengths = rng.integers(1, hi, size=n, endpoint=True).astype(np.int32)
+        t = int(lengths.sum())
+        say("meta fuzz", trial, "n", n, "T", t)
+        _meta_matches_oracle(lengths, t)
+
+
+def test_meta_invalid_lengths_flag_and_zero_outputs():
+    for lengths, t in (([3, 0, 5], 8), ([4, -2, 6], 8), ([3, 3], 7), ([200, 100], 250)):
+        say("invalid pack", lengths, t)
+        ref = O.build_meta(lengths, t)
+        lens_d = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+        meta = pk.build_meta(lens_d, t)
+        status, _ = meta.check()
+        assert status == ref["status"] and status != 0
+        q = torch.randn(t, 2, 64, device="cuda").bfloat16()
+        k = torch.randn(t, 1, 64, device="cuda").bfloat16()
+        v = torch.randn(t, 1, 64, device="cuda").bfloat16()
+        out = torch.full_like(q, 7.0)
+        lse = torch.full((2, t), 7.0, device="cuda")
+        pk.attn_fwd(meta, q, k, v, out=out, lse=lse)
+        dq, dk, dv = pk.attn_bwd(meta, q, k, v, out, lse, q)
+        torch.cuda.synchronize()
+        for x in (out, lse, dq, dk, dv):
+            assert torch.count_nonzero(x).item() == 0
+
+
+def test_empty_pack():
+    say("empty pack")
+    meta = pk.build_meta(torch.zeros(0, dtype=torch.int32, device="cuda"), 0)
+    status, mx = meta.check()
+    assert status == 0 and mx == 0
+    q = torch.zeros(0, 2, 64, device="cuda", dtype=torch.bfloat16)
+    k = torch.zeros(0, 1, 64, device="cuda", dtype=torch.bfloat16)
+    out, lse = pk.attn_fwd(meta, q, k, k)
+    dq, dk, dv = pk.attn_bwd(meta, q, k, k, out, lse, q)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 2, 64) and dq.shape == (0, 2, 64)
+
+
+SMALL_CASES = [
+    # (lengths, hq, hkv, d)
+    ([37, 100, 5, 114], 2, 1, 64),          # the tiny workload's pack
+    ([1], 2, 1, 64),                         # a single token
+    ([1, 1, 1, 1, 1], 4, 2, 128),            # only length-1 sequences
+    ([300], 2, 2, 128),                      # one sequence, ragged last tile
+    ([700, 1, 29], 5, 1, 128),               # long sequence across tiles, GQA 5
+    ([128, 128], 3, 3, 64),                  # tile-aligned boundaries, MHA
+    ([64, 1, 63, 130, 2, 250], 8, 2, 64),    # boundaries inside tiles at many offsets
+    ("short", 4, 1, 128),                    # many short sequences (1..16), skew-like
+    ([2000, 47], 2, 1, 64),                  # long sequence, d = 64
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_fwd_bwd_small(case):
+    lengths, hq, hkv, d = SMALL_CASES[case]
+    if lengths == "short":
+        lengths = synth.random_lengths(np.random.default_rng(5), 120, 1, 16)
+    say("small case", case, "T", int(np.sum(lengths)), "hq/hkv/d", hq, hkv, d)
+    lens, q, k, v, do = synth.small_problem(100 + case, lengths, hq, hkv, d)
+    scale = 1.0 / math.sqrt(d)
+    res = run_pk(lens, q, k, v, do, scale)
+    o_ref, lse_ref = O.attn_fwd(q, k, v, lens, scale, 1e4)
+    dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, scale, 1e4)
+    compare("out", to_np(res["out"]), o_ref)
+    compare("lse", to_np(res["lse"]), lse_ref, max_abs=LSE_MAX_ABS)
+    compare("dq", to_np(res["dq"]), dq_ref)
+    compare("dk", to_np(res["dk"]), dk_ref)
+    compare("dv", to_np(res["dv"]), dv_ref)
+
+
+def _sub_pack(lengths, seqs):
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
+    return [int(lengths[s]) for s in seqs], idx
+
+
+def _check_workload(name, layer, seqs=None, kv_heads=None):
+    w = synth.WORKLOADS[name]
+    lengths = synth.pack_lengths(name)
+    q, k, v, do = synth.layer_tensors(w, layer)
+    say("workload", name, "layer", layer, "seqs", "all" if seqs is None else len(seqs),
+        "kv heads", "all" if kv_heads is None else list(kv_heads))
+    res = run_pk(lengths, q, k, v, do, w.softmax_scale, w.rope_base)
+    if seqs is None:
+        seqs = list(range(len(lengths)))
+    sub_len, idx = _sub_pack(lengths, seqs)
+    kvs = list(range(w.hkv)) if kv_heads is None else list(kv_heads)
+    heads = [h for h in range(w.hq) if h // w.group in kvs]
+    o_ref, lse_ref = O.attn_fwd(q[idx], k[idx], v[idx], sub_len, w.softmax_scale, w.rope_base, heads=heads)
+    dq_ref, dk_ref, dv_ref = O.attn_bwd(q[idx], k[idx], v[idx], do[idx], sub_len, w.softmax_scale,
+                                        w.rope_base, kv_heads=kvs)
+    out = to_np(res["out"])[idx][:, heads]
+    compare("out", out, o_ref[:, heads])
+    compare("lse", to_np(res["lse"])[heads][:, idx], lse_ref[heads], max_abs=LSE_MAX_ABS)
+    compare("dq", to_np(res["dq"])[idx][:, heads], dq_ref[:, heads])
+    compare("dk", to_np(res["dk"])[idx][:, kvs], dk_ref[:, kvs])
+    compare("dv", to_np(res["dv"])[idx][:, kvs], dv_ref[:, kvs])
+    return res, lengths, (q, k, v, do)
+
+
+def test_workload_tiny():
+    _check_workload("tiny", 0)
+
+
+@pytest.mark.parametrize("layer", [0, 15])
+def test_workload_llama1b(layer):
+    _check_workload("llama1b", layer)
+
+
+@pytest.mark.parametrize("layer", [0, 27])
+def test_workload_qwen06b(layer):
+    _check_workload("qwen06b", layer)
+
+
+def test_workload_qwen14b_sampled():
+    # the longest, the shortest and the last sequence; the first and last KV-head groups
+    _check_workload("qwen14b", 0, seqs=[0, 7, 9], kv_heads=[0, 7])
+
+
+def test_workload_skewed_sampled():
+    lengths = synth.pack_lengths("skewed")
+    rng = np.random.default_rng(1)
+    short = sorted(rng.choice(np.arange(4, len(lengths)), size=300, replace=False).tolist())
+    res, lengths, (q, k, v, do) = _check_workload("skewed", 0, seqs=[2] + short, kv_heads=[5])
+    # closed forms on every length-1 sequence of the pack: O = V, lse = scale <q, k>,
+    # dQ = dK = 0, dV = sum of the group's dout
+    w = synth.WORKLOADS["skewed"]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    ones = cu[:-1][lengths == 1]
+    assert len(ones) == 249
+    g = np.arange(w.hq) // w.group
+    out, lse = to_np(res["out"])[ones], to_np(res["lse"])[:, ones]
+    compare("out1", out, v[ones][:, g].astype(np.float64))
+    lse_ref = w.softmax_scale * np.einsum("thd,thd->ht", q[ones].astype(np.float64), k[ones][:, g].astype(np.float64))
+    compare("lse1", lse, lse_ref, max_abs=LSE_MAX_ABS)
+    assert np.abs(to_np(res["dq"])[ones]).max() < 1e-6
+    assert np.abs(to_np(res["dk"])[ones]).max() < 1e-6
+    dv_ref = do[ones].astype(np.float64).reshape(len(ones), w.hkv, w.group, w.head_dim).sum(axis=2)
+    compare("dv1", to_np(res["dv"])[ones], dv_ref)
+
+
+def test_meta_reuse_determinism_and_dk_invariant():
+    """One meta reused by several layers gives the same results as a fresh meta per layer; fwd,
+    dK and dV are bitwise repeatable; sum_j R(theta_j) dK_j = 0 per sequence and KV head."""
+    w = synth.WORKLOADS["llama1b"]
+    lengths = synth.pack_lengths("llama1b")
+    say("meta reuse, llama1b")
+    shared = pk.build_meta(torch.tensor(lengths, device="cuda"), w.total_tokens)
+    for layer in (0, 1, 15):
+        q, k, v, do = synth.layer_tensors(w, layer)
+        a = run_pk(lengths, q, k, v, do, w.softmax_scale, meta=shared)
+        b = run_pk(lengths, q, k, v, do, w.softmax_scale)
+        c = run_pk(lengths, q, k, v, do, w.softmax_scale, meta=shared)
+        for key in ("out", "lse", "dk", "dv"):
+            assert torch.equal(a[key], b[key]) and torch.equal(a[key], c[key]), key
+        assert torch.allclose(a["dq"], b["dq"], atol=1e-5, rtol=0)
+    pos = np.concatenate([np.arange(n) for n in lengths])
+    dk = to_np(a["dk"])
+    th = O.rope_angles(pos, w.head_dim, w.rope_base)
+    c_, s_ = np.cos(th)[:, None, :], np.sin(th)[:, None, :]
+    half = w.head_dim // 2
+    dk_rot = np.concatenate([dk[..., :half] * c_ - dk[..., half:] * s_, dk[..., half:] * c_ + dk[..., :half] * s_], -1)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    scale_ref = np.abs(dk).max()
+    for s in range(len(lengths)):
+        assert np.abs(dk_rot[cu[s]:cu[s + 1]].sum(axis=0)).max() < 2e-2 * max(1.0, scale_ref)
+
+
+def test_autograd_function():
+    say("autograd wrapper")
+    lens, q, k, v, do = synth.small_problem(77, [50, 20, 1], 4, 2, 64)
+    meta = pk.build_meta(torch.tensor(lens, device="cuda"), int(lens.sum()))
+    tq, tk, tv = (dev(x).requires_grad_(True) for x in (q, k, v))
+    out = pk.PackedCausalAttention.apply(tq, tk, tv, meta, 0.125, 1e4)
+    out.backward(dev(do))
+    dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, 0.125, 1e4)
+    compare("dq", to_np(tq.grad), dq_ref)
+    compare("dk", to_np(tk.grad), dk_ref)
+    compare("dv", to_np(tv.grad), dv_ref)
