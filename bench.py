@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Packed causal attention fwd+bwd benchmark on one MI355X.
+
+One step = one pass of the whole path over one synthetic pack: build the packed metadata once,
+then the forward of every layer, then the backward of every layer (the layer loop of a training
+step), all on one stream with no host synchronisation inside the step.  Default workload: the
+Qwen3-14B-shaped pack (16384 tokens, 40/8 heads, d=128, 40 layers).
+
+Prints ONE JSON line.  `value` is algorithmic fwd+bwd TFLOP/s over the timed steps
+(4*hq*d*P + 10*hq*d*P per layer, P = kept query/key pairs), `roofline` reports the dominant
+kernel (the backward) against the chip's dense 16-bit matrix peak, timed per launch with HIP
+events recorded by the library on its stream, and `cpu_baseline` times the float64 CPU oracle on
+a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen14b] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed causal attn fwd+bwd TFLOP/s + tokens/s per layer; % bf16 MFMA peak"
+PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 matrix peak (256 CUs x 4096 flop/clk x 2.4 GHz)
+HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="qwen14b")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-target-s", type=float, default=15.0,
+                   help="approximate CPU seconds for the oracle sample")
+    return p.parse_args()
+
+
+def cpu_baseline(w, lengths, target_s):
+    """Time the float64 oracle (as it is) on whole sequences of layer 0, one KV-head group,
+    adding sequences (shortest first) until about target_s seconds of work."""
+    import numpy as np
+    from oracle import pk_oracle as O
+    from packed_sequence_causal_pk_amd import synth
+
+    q, k, v, do = synth.layer_tensors(w, 0)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    order = np.argsort(lengths, kind="stable")
+    done_flops, done_s, chosen = 0, 0.0, []
+    for s in order:
+        idx = np.arange(cu[s], cu[s + 1])
+        n = len(idx)
+        heads = list(range(w.group))  # KV head 0 and its query heads
+        t0 = time.perf_counter()
+        O.attn_fwd(q[idx], k[idx], v[idx], [n], w.softmax_scale, w.rope_base, heads=heads)
+        O.attn_bwd(q[idx], k[idx], v[idx], do[idx], [n], w.softmax_scale, w.rope_base, kv_heads=[0])
+        done_s += time.perf_counter() - t0
+        f, b = O.attn_flops([n], w.group, w.head_dim)
+        done_flops += f + b
+        chosen.append(int(n))
+        if done_s >= target_s:
+            break
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": done_flops / done_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": "layer 0, KV head 0 with its %d query heads, %d whole sequences (lengths %s) of "
+                  "the pack; fwd+bwd float64 numpy, %.1f s" % (w.group, len(chosen), chosen, done_s),
+        "seconds": done_s,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path is a single-GPU kernel (see the design notes "
+              "for how it would shard); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import packed_sequence_causal_pk_amd as pk
+    from oracle import pk_oracle as O
+    from packed_sequence_causal_pk_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    lengths = synth.pack_lengths(args.workload)
+    T, L = w.total_tokens, w.layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # inputs: independent seeded N(0,1) tensors per layer, rounded to bf16, resident in HBM
+    gen = torch.Generator(device=dev)
+    layers = []
+    for l in range(L):
+        gen.manual_seed(1000 + l)
+        mk = lambda *shape: (torch.randn(*shape, generator=gen, device=dev) * w.input_scale).bfloat16()
+        layers.append({"q": mk(T, w.hq, w.head_dim), "k": mk(T, w.hkv, w.head_dim),
+                       "v": mk(T, w.hkv, w.head_dim), "do": mk(T, w.hq, w.head_dim),
+                       "out": torch.empty(T, w.hq, w.head_dim, dtype=torch.bfloat16, device=dev),
+                       "lse": torch.empty(w.hq, T, dtype=torch.float32, device=dev)})
+    dq = torch.empty(T, w.hq, w.head_dim, dtype=torch.float32, device=dev)
+    dk = torch.empty(T, w.hkv, w.head_dim, dtype=torch.float32, device=dev)
+    dv = torch.empty(T, w.hkv, w.head_dim, dtype=torch.float32, device=dev)
+    lengths_d = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    meta0 = pk.build_meta(lengths_d, T)
+    ws_f = pk.fwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
+    ws_b = pk.bwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
+    meta0.close()
+    torch.cuda.synchronize()
+    print("bench: %s, T=%d, %d layers, hq/hkv/d=%d/%d/%d" % (args.workload, T, L, w.hq, w.hkv, w.head_dim),
+          file=sys.stderr, flush=True)
+
+    def step():
+        meta = pk.build_meta(lengths_d, T)  # once per pack; every layer reuses it
+        for x in layers:
+            pk.attn_fwd(meta, x["q"], x["k"], x["v"], w.softmax_scale, w.rope_base,
+                        out=x["out"], lse=x["lse"], workspace=ws_f)
+        for x in reversed(layers):
+            pk.attn_bwd(meta, x["q"], x["k"], x["v"], x["out"], x["lse"], x["do"], w.softmax_scale,
+                        w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        return meta
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("bench: warmup done", file=sys.stderr, flush=True)
+
+    pk.prof_reset()
+    pk.prof_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    metas = [step() for _ in range(args.steps)]
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pk.prof_enable(False)
+    del metas
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    kern = {}
+    for name in ("meta", "fwd_prep", "fwd", "bwd_prep", "bwd", "bwd_post"):
+        ms, n = pk.prof_query(name)
+        kern[name] = {"total_ms": ms, "launches": n, "avg_us": 1000.0 * ms / max(n, 1)}
+    print("bench: timed %d steps, %.2f ms/step (wall %.2f s)" % (args.steps, step_ms, wall),
+          file=sys.stderr, flush=True)
+
+    fwd_flops, bwd_flops = O.attn_flops(lengths, w.hq, w.head_dim)
+    layer_ms = step_ms / L
+    tflops = (fwd_flops + bwd_flops) * L / (step_ms * 1e-3) / 1e12
+    bwd_us = kern["bwd"]["avg_us"]
+    fwd_us = kern["fwd"]["avg_us"]
+    per_layer_fwd_ms = (kern["fwd_prep"]["total_ms"] + kern["fwd"]["total_ms"]) / args.steps / L
+    per_layer_bwd_ms = (kern["bwd_prep"]["total_ms"] + kern["bwd"]["total_ms"]
+                        + kern["bwd_post"]["total_ms"]) / args.steps / L
+    bwd_achieved = bwd_flops / (bwd_us * 1e-6) / 1e12
+    fwd_achieved = fwd_flops / (fwd_us * 1e-6) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "description": w.description, "total_tokens": T,
+            "n_seqs": int(len(lengths)), "hq": w.hq, "hkv": w.hkv, "head_dim": w.head_dim,
+            "layers": L, "step": "build meta once + %d layer forwards + %d layer backwards" % (L, L),
+            "io_dtypes": "q/k/v/out/dout bf16, lse/dq/dk/dv fp32",
+        },
+        "tokens_per_s_per_layer": round(T / (layer_ms * 1e-3), 1),
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
+        "ms_per_layer_fwd_bwd": round(layer_ms, 4),
+        "ms_per_layer_fwd": round(per_layer_fwd_ms, 4),
+        "ms_per_layer_bwd": round(per_layer_bwd_ms, 4),
+        "build_meta_us": round(kern["meta"]["avg_us"], 2),
+        "kernels_avg_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+        "fwd_kernel_tflops": round(fwd_achieved, 2),
+        "roofline": {
+            "kernel": "k_attn_bwd (backward attention)",
+            "bound": "mfma", "achieved": round(bwd_achieved, 2), "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(bwd_achieved / PEAK_TFLOPS, 4), "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, lengths, args.cpu_target_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

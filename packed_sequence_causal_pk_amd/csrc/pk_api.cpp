@@ -82,6 +82,8 @@ BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d) {
     w.krot = off; off += align256((size_t)T * hkv * d * 2);
     w.rope = off; off += align256((size_t)T * (d / 2) * 8);
     w.dsum = off; off += align256((size_t)T * hq * 4);
+    w.blockmax = off; off += align256((size_t)prep_blocks(T, d) * 4);
+    w.scale = off; off += align256(2 * 4);
     w.total = off;
     return w;
 }
@@ -232,17 +234,21 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     char *w = static_cast<char *>(ws);
     float *dsum = reinterpret_cast<float *>(w + W.dsum);
+    float *blockmax = reinterpret_cast<float *>(w + W.blockmax);
+    float *scale = reinterpret_cast<float *>(w + W.scale);
     pk::RopeArgs ra{meta->pos, T, hq, hkv, d, rope_base};
     hipError_t e;
     {
         ProfScope ps(PK_K_BWD_PREP, s);
-        e = pk::launch_bwd_prep(ra, q, k, out, dout, w + W.qrot, w + W.krot, w + W.rope, dsum, dq, s);
+        e = pk::launch_bwd_prep(ra, q, k, out, dout, w + W.qrot, w + W.krot, w + W.rope, dsum, dq,
+                                blockmax, scale, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
     {
         ProfScope ps(PK_K_BWD, s);
-        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, v, dout, lse, dsum, w + W.rope, dq, dk, dv, s);
+        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, v, dout, lse, dsum, scale, w + W.rope,
+                           dq, dk, dv, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     {

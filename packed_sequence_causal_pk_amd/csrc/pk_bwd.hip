@@ -11,7 +11,7 @@
 //
 // Layout for CDNA4 (one workgroup = one backward work item, i.e. 128 keys, x one KV head):
 //   * the 4 waves own 32 keys each; K_rot and V of those keys sit in registers as the k operand
-//     of S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16), so each lane owns one key column;
+//     of S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_f16), so each lane owns one key column;
 //   * dK^T and dV^T accumulate in registers over every query block AND every query head of the
 //     GQA group, so the group sum costs nothing and dK, dV are written once;
 //   * query blocks of 64 rows are staged in LDS row-major (for S, dP) and transposed (for the
@@ -21,7 +21,10 @@
 //     LDS and accumulated into the float32 dq buffer with hardware float atomics (the inverse
 //     RoPE of dq runs in the epilogue pass once all atomics are done);
 //   * the mask is applied element-wise only on blocks that straddle a sequence boundary or the
-//     diagonal; blocks fully outside the wave's visible range skip their products.
+//     diagonal; blocks fully outside the wave's visible range skip their products;
+//   * operands are fp16 with fp32 accumulation.  dout enters scaled by the power of two sigma
+//     the prologue chose (max|dout| * sigma in [1, 2)), so dP and dS are sigma-scaled too; the
+//     results are unscaled exactly by 1/sigma when dQ, dK and dV are written.
 #include "pk_internal.h"
 #include "pk_device.h"
 
@@ -30,12 +33,13 @@ namespace {
 using namespace pkd;
 
 struct BwdArgs {
-    const bf16 *qrot;     // [T, hq, D]
-    const bf16 *krot;     // [T, hkv, D]
+    const f16 *qrot;      // [T, hq, D] fp16
+    const f16 *krot;      // [T, hkv, D] fp16
     const bf16 *v;        // [T, hkv, D]
     const bf16 *dout;     // [T, hq, D]
     const float *lse;     // [hq, T]
     const float *dsum;    // [hq, T]
+    const float *dscale;  // {sigma, 1/sigma}
     const float2 *rope;   // [T, D/2]
     const int32_t *items; // [n_items, 8] longest first
     const int32_t *pos;   // [T]
@@ -56,14 +60,14 @@ struct BwdSmem {
     static constexpr int TP = BQ + 8;    // transposed Q / dO pitch
     static constexpr int SP = BKV + 8;   // dS pitch
     static constexpr int KTP = BKV + 8;  // transposed K pitch
-    bf16 q[BQ * QP];
-    bf16 dO[BQ * QP];
-    bf16 qt[D * TP];
-    bf16 dOt[D * TP];
-    bf16 ds[BQ * SP];
-    bf16 kt[D * KTP];
+    f16 q[BQ * QP];
+    f16 dO[BQ * QP];
+    f16 qt[D * TP];
+    f16 dOt[D * TP];
+    f16 ds[BQ * SP];
+    f16 kt[D * KTP];
     float lse[BQ];   // lse * log2(e); +inf for rows past the item
-    float dd[BQ];    // D_i
+    float dd[BQ];    // D_i * sigma
     int lo[BQ];      // first key of the row's sequence; INT_MAX past the item
 };
 
@@ -81,22 +85,28 @@ __device__ void bwd_zero_tile(const BwdArgs &a, int tile, int kvh) {
     }
 }
 
-// Stage rows [qb, qb+BQ) of one head of a [T, H, D] bf16 tensor into LDS, row-major and
-// transposed.  Each thread moves a pair of rows x 8 columns; rows at or past `q_end` are zero.
-template <int D>
-__device__ __forceinline__ void stage_rows(const bf16 *__restrict__ src, int H, int h, int qb,
-                                           int q_end, bf16 *rowmaj, bf16 *trans) {
+__device__ __forceinline__ f16x8 load_as_f16x8(const f16 *p, float) { return load_f16x8(p); }
+__device__ __forceinline__ f16x8 load_as_f16x8(const bf16 *p, float scale) {
+    return bf16x8_to_f16x8(load_bf16x8(p), scale);
+}
+
+// Stage rows [qb, qb+BQ) of one head of a [T, H, D] tensor (fp16, or bf16 times `scale`) into
+// LDS as fp16, row-major and transposed.  Each thread moves a pair of rows x 8 columns; rows at
+// or past `q_end` are zero.
+template <int D, typename Src>
+__device__ __forceinline__ void stage_rows(const Src *__restrict__ src, float scale, int H, int h,
+                                           int qb, int q_end, f16 *rowmaj, f16 *trans) {
     using S = BwdSmem<D>;
     for (int e = threadIdx.x; e < (S::BQ / 2) * (D / 8); e += 256) {
         const int rp = e % (S::BQ / 2), ch = e / (S::BQ / 2);
         const int i0 = qb + 2 * rp;
-        const bf16x8 x0 = i0 < q_end ? load_bf16x8(src + ((int64_t)i0 * H + h) * D + ch * 8) : zero_bf16x8();
-        const bf16x8 x1 = i0 + 1 < q_end ? load_bf16x8(src + ((int64_t)(i0 + 1) * H + h) * D + ch * 8) : zero_bf16x8();
-        store_bf16x8(rowmaj + (2 * rp) * S::QP + ch * 8, x0);
-        store_bf16x8(rowmaj + (2 * rp + 1) * S::QP + ch * 8, x1);
+        const f16x8 x0 = i0 < q_end ? load_as_f16x8(src + ((int64_t)i0 * H + h) * D + ch * 8, scale) : zero_f16x8();
+        const f16x8 x1 = i0 + 1 < q_end ? load_as_f16x8(src + ((int64_t)(i0 + 1) * H + h) * D + ch * 8, scale) : zero_f16x8();
+        store_f16x8(rowmaj + (2 * rp) * S::QP + ch * 8, x0);
+        store_f16x8(rowmaj + (2 * rp + 1) * S::QP + ch * 8, x1);
 #pragma unroll
         for (int s = 0; s < 8; ++s)
-            *reinterpret_cast<uint32_t *>(trans + (ch * 8 + s) * S::TP + 2 * rp) = pack_bf16x2(x0[s], x1[s]);
+            *reinterpret_cast<uint32_t *>(trans + (ch * 8 + s) * S::TP + 2 * rp) = pack_f16x2(x0[s], x1[s]);
     }
 }
 
@@ -119,6 +129,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
     }
     const int kv_start = it[0], kv_end = it[1], q_start = it[2], q_end = it[3];
     const int64_t T = a.T;
+    const float sigma = a.dscale[0], inv_sigma = a.dscale[1];
 
     const int j = kv_start + 32 * w + n32;  // this lane's key
     const bool kvalid = j < kv_end;
@@ -128,24 +139,24 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
     const int blk_last = kv_end - 1;
 
     // K_rot and V of this lane's key, as k operands (d in [16kk + 8hb, +8))
-    bf16x8 kf[NKK], vf[NKK];
+    f16x8 kf[NKK], vf[NKK];
     {
         const int64_t row = ((int64_t)(kvalid ? j : kv_start) * a.hkv + kvh) * D + 8 * hb;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            kf[kk] = kvalid ? load_bf16x8(a.krot + row + 16 * kk) : zero_bf16x8();
-            vf[kk] = kvalid ? load_bf16x8(a.v + row + 16 * kk) : zero_bf16x8();
+            kf[kk] = kvalid ? load_f16x8(a.krot + row + 16 * kk) : zero_f16x8();
+            vf[kk] = kvalid ? bf16x8_to_f16x8(load_bf16x8(a.v + row + 16 * kk)) : zero_f16x8();
         }
     }
     // K_rot^T of the workgroup's 128 keys -> LDS, for dQ
     for (int e = tid; e < (BKV / 2) * (D / 8); e += 256) {
         const int kp = e % (BKV / 2), ch = e / (BKV / 2);
         const int j0 = kv_start + 2 * kp;
-        const bf16x8 x0 = j0 < kv_end ? load_bf16x8(a.krot + ((int64_t)j0 * a.hkv + kvh) * D + ch * 8) : zero_bf16x8();
-        const bf16x8 x1 = j0 + 1 < kv_end ? load_bf16x8(a.krot + ((int64_t)(j0 + 1) * a.hkv + kvh) * D + ch * 8) : zero_bf16x8();
+        const f16x8 x0 = j0 < kv_end ? load_f16x8(a.krot + ((int64_t)j0 * a.hkv + kvh) * D + ch * 8) : zero_f16x8();
+        const f16x8 x1 = j0 + 1 < kv_end ? load_f16x8(a.krot + ((int64_t)(j0 + 1) * a.hkv + kvh) * D + ch * 8) : zero_f16x8();
 #pragma unroll
         for (int s = 0; s < 8; ++s)
-            *reinterpret_cast<uint32_t *>(sm.kt + (ch * 8 + s) * S::KTP + 2 * kp) = pack_bf16x2(x0[s], x1[s]);
+            *reinterpret_cast<uint32_t *>(sm.kt + (ch * 8 + s) * S::KTP + 2 * kp) = pack_f16x2(x0[s], x1[s]);
     }
 
     f32x16 dka[NDB], dva[NDB];
@@ -159,13 +170,13 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
         const int h = kvh * a.group + hh;
         for (int qb = q_start; qb < q_end; qb += BQ) {
             __syncthreads();
-            stage_rows<D>(a.qrot, a.hq, h, qb, q_end, sm.q, sm.qt);
-            stage_rows<D>(a.dout, a.hq, h, qb, q_end, sm.dO, sm.dOt);
+            stage_rows<D>(a.qrot, 1.f, a.hq, h, qb, q_end, sm.q, sm.qt);
+            stage_rows<D>(a.dout, sigma, a.hq, h, qb, q_end, sm.dO, sm.dOt);
             if (tid < BQ) {
                 const int i = qb + tid;
                 const bool ok = i < q_end;
                 sm.lse[tid] = ok ? a.lse[(int64_t)h * T + i] * kLog2e : INFINITY;
-                sm.dd[tid] = ok ? a.dsum[(int64_t)h * T + i] : 0.f;
+                sm.dd[tid] = ok ? a.dsum[(int64_t)h * T + i] * sigma : 0.f;
                 sm.lo[tid] = ok ? i - a.pos[i] : INT_MAX;
             }
             __syncthreads();
@@ -183,12 +194,12 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
                     sp[qm] = zero_f32x16();
                     dp[qm] = zero_f32x16();
                     const int row = 32 * qm + row_perm(n32);
-                    const bf16 *qrow = sm.q + row * S::QP + 8 * hb;
-                    const bf16 *grow = sm.dO + row * S::QP + 8 * hb;
+                    const f16 *qrow = sm.q + row * S::QP + 8 * hb;
+                    const f16 *grow = sm.dO + row * S::QP + 8 * hb;
 #pragma unroll
                     for (int kk = 0; kk < NKK; ++kk) {
-                        sp[qm] = mfma32(load_bf16x8(qrow + 16 * kk), kf[kk], sp[qm]);
-                        dp[qm] = mfma32(load_bf16x8(grow + 16 * kk), vf[kk], dp[qm]);
+                        sp[qm] = mfma32(load_f16x8(qrow + 16 * kk), kf[kk], sp[qm]);
+                        dp[qm] = mfma32(load_f16x8(grow + 16 * kk), vf[kk], dp[qm]);
                     }
                 }
                 const float sl2 = a.scale * kLog2e;
@@ -211,18 +222,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
                 for (int qm = 0; qm < 2; ++qm) {
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
-                        bf16x8 pb, sb;
+                        f16x8 pb, sb;
 #pragma unroll
                         for (int x = 0; x < 8; ++x) {
-                            pb[x] = (bf16)sp[qm][8 * e + x];
-                            sb[x] = (bf16)dp[qm][8 * e + x];
+                            pb[x] = (f16)sp[qm][8 * e + x];
+                            sb[x] = (f16)dp[qm][8 * e + x];
                         }
                         const int col = 32 * qm + 16 * e + 8 * hb;
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
                             const int drow = 32 * db + n32;
-                            dva[db] = mfma32(load_bf16x8(sm.dOt + drow * S::TP + col), pb, dva[db]);
-                            dka[db] = mfma32(load_bf16x8(sm.qt + drow * S::TP + col), sb, dka[db]);
+                            dva[db] = mfma32(load_f16x8(sm.dOt + drow * S::TP + col), pb, dva[db]);
+                            dka[db] = mfma32(load_f16x8(sm.qt + drow * S::TP + col), sb, dka[db]);
                         }
                     }
                 }
@@ -231,9 +242,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
                 for (int qm = 0; qm < 2; ++qm)
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr)
-                        sm.ds[(32 * qm + row_perm(acc_row(rr, hb))) * S::SP + 32 * w + n32] = (bf16)dp[qm][rr];
+                        sm.ds[(32 * qm + row_perm(acc_row(rr, hb))) * S::SP + 32 * w + n32] = (f16)dp[qm][rr];
             } else {
-                for (int row = hb; row < BQ; row += 2) sm.ds[row * S::SP + 32 * w + n32] = (bf16)0.f;
+                for (int row = hb; row < BQ; row += 2) sm.ds[row * S::SP + 32 * w + n32] = (f16)0.f;
             }
             __syncthreads();
             // dQ_rot[qb .. qb+64) += scale * dS K_rot, split in 32x32 blocks over the 4 waves
@@ -242,16 +253,17 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
                 const int pidx = w * QB_PER_WAVE + u;
                 const int qm = pidx / NDB, db = pidx % NDB;
                 f32x16 c = zero_f32x16();
-                const bf16 *arow = sm.ds + (32 * qm + n32) * S::SP + 8 * hb;
-                const bf16 *brow = sm.kt + (32 * db + n32) * S::KTP + 8 * hb;
+                const f16 *arow = sm.ds + (32 * qm + n32) * S::SP + 8 * hb;
+                const f16 *brow = sm.kt + (32 * db + n32) * S::KTP + 8 * hb;
 #pragma unroll
                 for (int ks = 0; ks < BKV / 16; ++ks)
-                    c = mfma32(load_bf16x8(arow + 16 * ks), load_bf16x8(brow + 16 * ks), c);
+                    c = mfma32(load_f16x8(arow + 16 * ks), load_f16x8(brow + 16 * ks), c);
+                const float cscale = a.scale * inv_sigma;
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
                     const int i = qb + 32 * qm + acc_row(rr, hb);
                     if (i < q_end)
-                        unsafeAtomicAdd(a.dq + ((int64_t)i * a.hq + h) * D + 32 * db + n32, c[rr] * a.scale);
+                        unsafeAtomicAdd(a.dq + ((int64_t)i * a.hq + h) * D + 32 * db + n32, c[rr] * cscale);
                 }
             }
         }
@@ -262,13 +274,15 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
         float *dvrow = a.dv + ((int64_t)j * a.hkv + kvh) * D;
         float *dkrow = a.dk + ((int64_t)j * a.hkv + kvh) * D;
         const float2 *cs = a.rope + (int64_t)j * (D / 2);
+        const float kscale = a.scale * inv_sigma;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int d = 32 * db + 8 * g4 + 4 * hb;
                 *reinterpret_cast<float4 *>(dvrow + d) =
-                    make_float4(dva[db][4 * g4], dva[db][4 * g4 + 1], dva[db][4 * g4 + 2], dva[db][4 * g4 + 3]);
+                    make_float4(dva[db][4 * g4] * inv_sigma, dva[db][4 * g4 + 1] * inv_sigma,
+                                dva[db][4 * g4 + 2] * inv_sigma, dva[db][4 * g4 + 3] * inv_sigma);
             }
 #pragma unroll
         for (int db = 0; db < NDB / 2; ++db)
@@ -279,8 +293,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     const float2 f = cs[d + x];
-                    const float x1 = dka[db][4 * g4 + x] * a.scale;
-                    const float x2 = dka[db + NDB / 2][4 * g4 + x] * a.scale;
+                    const float x1 = dka[db][4 * g4 + x] * kscale;
+                    const float x2 = dka[db + NDB / 2][4 * g4 + x] * kscale;
                     y1[x] = x1 * f.x + x2 * f.y;
                     y2[x] = x2 * f.x - x1 * f.y;
                 }
@@ -296,11 +310,12 @@ namespace pk {
 
 hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                       const void *krot, const void *v, const void *dout, const float *lse,
-                      const float *dsum, const void *rope, float *dq, float *dk, float *dv,
-                      hipStream_t s) {
+                      const float *dsum, const float *scale, const void *rope, float *dq,
+                      float *dk, float *dv, hipStream_t s) {
     BwdArgs a;
-    a.qrot = (const bf16 *)qrot;
-    a.krot = (const bf16 *)krot;
+    a.qrot = (const f16 *)qrot;
+    a.krot = (const f16 *)krot;
+    a.dscale = scale;
     a.v = (const bf16 *)v;
     a.dout = (const bf16 *)dout;
     a.lse = lse;

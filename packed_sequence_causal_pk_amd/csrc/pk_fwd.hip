@@ -13,14 +13,16 @@
 // laid out for CDNA4:
 //   * one workgroup = one work item (128 queries) x one query head; 4 waves of 32 queries;
 //     items are taken in the work list's longest-first order, heads fastest;
-//   * the scores are computed transposed, S^T = K_rot Q_rot^T, with v_mfma_f32_32x32x16_bf16,
+//   * the scores are computed transposed, S^T = K_rot Q_rot^T, with v_mfma_f32_32x32x16_f16,
 //     so each lane of a wave owns one query: the row max needs one cross-half exchange and the
 //     O^T accumulator is rescaled with a per-lane factor;
 //   * P^T stays in registers and is the k operand of O^T += V^T P^T; key rows of the first
 //     product are fed in row_perm order so the V^T operand is one 16-byte LDS read per lane;
 //   * K_rot and V tiles of 64 keys are staged in LDS (V transposed) and read by all 4 waves;
 //   * online softmax in the exp2 domain with scale * log2(e) folded into the scores;
-//   * Q is rotated in the prologue from the per-call (cos, sin) table; K comes pre-rotated.
+//   * Q is rotated in the prologue from the per-call (cos, sin) table; K comes pre-rotated;
+//   * operands are fp16 (the bf16 inputs convert exactly; rotated values, P keep 3 more bits
+//     than bf16), accumulators and the softmax state fp32.
 #include "pk_internal.h"
 #include "pk_device.h"
 
@@ -30,7 +32,7 @@ using namespace pkd;
 
 struct FwdArgs {
     const bf16 *q;        // [T, hq, D]
-    const bf16 *krot;     // [T, hkv, D]
+    const f16 *krot;      // [T, hkv, D] fp16
     const bf16 *v;        // [T, hkv, D]
     const float2 *rope;   // [T, D/2] (cos, sin)
     const int32_t *items; // [n_items, 8] longest first
@@ -62,8 +64,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     constexpr int NKK = D / 16;   // k-steps of the score product
     constexpr int NDB = D / 32;   // 32-row blocks of O^T
     constexpr int NMB = BK / 32;  // 32-key blocks per tile
-    __shared__ __attribute__((aligned(16))) bf16 lds_k[BK * KP];
-    __shared__ __attribute__((aligned(16))) bf16 lds_vt[D * VP];
+    __shared__ __attribute__((aligned(16))) f16 lds_k[BK * KP];
+    __shared__ __attribute__((aligned(16))) f16 lds_vt[D * VP];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n32 = lane & 31, hb = lane >> 5;
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
 
     // Q fragments (k operand of S^T = K Q^T), rotated in registers.  Chunk kk holds
     // d in [16kk + 8hb, +8); chunk kk + NKK/2 holds the RoPE partners d + D/2.
-    bf16x8 qf[NKK];
+    f16x8 qf[NKK];
     {
         const bf16 *qrow = a.q + ((int64_t)(qvalid ? i : q_start) * a.hq + h) * D;
         const float2 *cs = a.rope + (int64_t)(qvalid ? i : q_start) * (D / 2);
@@ -98,13 +100,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
             const int d0 = 16 * kk + 8 * hb;
             const bf16x8 x1 = load_bf16x8(qrow + d0);
             const bf16x8 x2 = load_bf16x8(qrow + d0 + D / 2);
-            bf16x8 y1, y2;
+            f16x8 y1, y2;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const float2 f = cs[d0 + s];
                 const float a1 = (float)x1[s], a2 = (float)x2[s];
-                y1[s] = (bf16)(qvalid ? a1 * f.x - a2 * f.y : 0.f);
-                y2[s] = (bf16)(qvalid ? a2 * f.x + a1 * f.y : 0.f);
+                y1[s] = (f16)(qvalid ? a1 * f.x - a2 * f.y : 0.f);
+                y2[s] = (f16)(qvalid ? a2 * f.x + a1 * f.y : 0.f);
             }
             qf[kk] = y1;
             qf[kk + NKK / 2] = y2;
@@ -125,18 +127,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
         for (int e = tid; e < BK * (D / 8); e += 256) {
             const int row = e / (D / 8), ch = e % (D / 8);
             const int64_t j = k0 + row;
-            const bf16x8 val = j < T ? load_bf16x8(a.krot + (j * a.hkv + kvh) * D + ch * 8) : zero_bf16x8();
-            store_bf16x8(lds_k + row * KP + ch * 8, val);
+            const f16x8 val = j < T ? load_f16x8(a.krot + (j * a.hkv + kvh) * D + ch * 8) : zero_f16x8();
+            store_f16x8(lds_k + row * KP + ch * 8, val);
         }
         // V tile -> lds_vt [D][BK] (transposed), two keys per 32-bit LDS store
         for (int e = tid; e < (BK / 2) * (D / 8); e += 256) {
             const int kp = e % (BK / 2), ch = e / (BK / 2);
             const int64_t j0 = k0 + 2 * kp;
-            const bf16x8 v0 = j0 < T ? load_bf16x8(a.v + (j0 * a.hkv + kvh) * D + ch * 8) : zero_bf16x8();
-            const bf16x8 v1 = j0 + 1 < T ? load_bf16x8(a.v + ((j0 + 1) * a.hkv + kvh) * D + ch * 8) : zero_bf16x8();
+            const f16x8 v0 = bf16x8_to_f16x8(j0 < T ? load_bf16x8(a.v + (j0 * a.hkv + kvh) * D + ch * 8) : zero_bf16x8());
+            const f16x8 v1 = bf16x8_to_f16x8(j0 + 1 < T ? load_bf16x8(a.v + ((j0 + 1) * a.hkv + kvh) * D + ch * 8) : zero_bf16x8());
 #pragma unroll
             for (int s = 0; s < 8; ++s)
-                *reinterpret_cast<uint32_t *>(lds_vt + (ch * 8 + s) * VP + 2 * kp) = pack_bf16x2(v0[s], v1[s]);
+                *reinterpret_cast<uint32_t *>(lds_vt + (ch * 8 + s) * VP + 2 * kp) = pack_f16x2(v0[s], v1[s]);
         }
         __syncthreads();
         if (!wave_active) continue;
@@ -149,9 +151,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
             s[mb] = zero_f32x16();
-            const bf16 *krow = lds_k + (32 * mb + row_perm(n32)) * KP + 8 * hb;
+            const f16 *krow = lds_k + (32 * mb + row_perm(n32)) * KP + 8 * hb;
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) s[mb] = mfma32(load_bf16x8(krow + 16 * kk), qf[kk], s[mb]);
+            for (int kk = 0; kk < NKK; ++kk) s[mb] = mfma32(load_f16x8(krow + 16 * kk), qf[kk], s[mb]);
         }
         float tmax = -INFINITY;
 #pragma unroll
@@ -191,12 +193,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
         for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                bf16x8 pb;
+                f16x8 pb;
 #pragma unroll
-                for (int x = 0; x < 8; ++x) pb[x] = (bf16)s[mb][8 * e + x];
-                const bf16 *vrow = lds_vt + n32 * VP + 32 * mb + 16 * e + 8 * hb;
+                for (int x = 0; x < 8; ++x) pb[x] = (f16)s[mb][8 * e + x];
+                const f16 *vrow = lds_vt + n32 * VP + 32 * mb + 16 * e + 8 * hb;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) o[db] = mfma32(load_bf16x8(vrow + 32 * db * VP), pb, o[db]);
+                for (int db = 0; db < NDB; ++db) o[db] = mfma32(load_f16x8(vrow + 32 * db * VP), pb, o[db]);
             }
         }
     }
@@ -229,7 +231,7 @@ hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, co
                       const void *v, const void *rope, void *out, float *lse, hipStream_t s) {
     FwdArgs a;
     a.q = (const bf16 *)q;
-    a.krot = (const bf16 *)krot;
+    a.krot = (const f16 *)krot;
     a.v = (const bf16 *)v;
     a.rope = (const float2 *)rope;
     a.items = m.fwd_items;

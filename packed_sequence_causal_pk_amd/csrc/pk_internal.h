@@ -36,7 +36,7 @@ struct FwdWorkspace {
     size_t krot, rope, total;
 };
 struct BwdWorkspace {
-    size_t qrot, krot, rope, dsum, total;
+    size_t qrot, krot, rope, dsum, blockmax, scale, total;
 };
 FwdWorkspace fwd_workspace(int64_t T, int hq, int hkv, int d);
 BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d);
@@ -53,9 +53,11 @@ struct RopeArgs {
     float rope_base;
 };
 hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, void *krot, void *rope, hipStream_t s);
+// Blocks of the per-token prologue/epilogue kernels (one thread per token and 4 rotation pairs).
+unsigned prep_blocks(int64_t T, int d);
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *out,
                            const void *dout, void *qrot, void *krot, void *rope, float *dsum,
-                           float *dq, hipStream_t s);
+                           float *dq, float *blockmax, float *scale, hipStream_t s);
 hipError_t launch_bwd_post(const RopeArgs &r, const void *rope, float *dq, hipStream_t s);
 
 struct AttnShape {
@@ -67,7 +69,7 @@ hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, co
                       const void *v, const void *rope, void *out, float *lse, hipStream_t s);
 hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                       const void *krot, const void *v, const void *dout, const float *lse,
-                      const float *dsum, const void *rope, float *dq, float *dk, float *dv,
-                      hipStream_t s);
+                      const float *dsum, const float *scale, const void *rope, float *dq,
+                      float *dk, float *dv, hipStream_t s);
 
 }  // namespace pk

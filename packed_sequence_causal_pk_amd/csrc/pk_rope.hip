@@ -11,7 +11,13 @@
 // [MV] "UnSloth极速微调：底层CUDA优化带来的变革", and read by the attention kernels instead of
 // evaluating sin/cos in their loops.
 //
-// Thread layout of all three kernels: one thread per (token t, group c of 4 rotation pairs);
+// Rotated q and k are written as fp16, the matrix-core operand format of the attention kernels.
+// The backward prologue also records max|dout| per block; k_bwd_scale turns it into a power of
+// two sigma with max|dout| * sigma in [1, 2), so the backward's fp16 gradient operands (dout and
+// dS, both scaled by sigma, unscaled exactly at the end) stay inside fp16's range whatever the
+// magnitude of the incoming gradient.
+//
+// Thread layout of the three per-token kernels: one thread per (token t, group c of 4 rotation pairs);
 // the thread owns elements d in [4c, 4c+4) and their partners d + D/2 for every head, so each
 // rotation stays inside one thread and a token's D/8 threads read each half-row contiguously.
 #include "pk_internal.h"
@@ -48,16 +54,16 @@ __device__ __forceinline__ void load4(const bf16 *p, float x[4]) {
     for (int k = 0; k < 4; ++k) x[k] = (float)b[k];
 }
 
-__device__ __forceinline__ void store4(bf16 *p, const float x[4]) {
+__device__ __forceinline__ void store4(f16 *p, const float x[4]) {
     uint2 raw;
-    raw.x = pkd::pack_bf16x2((bf16)x[0], (bf16)x[1]);
-    raw.y = pkd::pack_bf16x2((bf16)x[2], (bf16)x[3]);
+    raw.x = pkd::pack_f16x2((f16)x[0], (f16)x[1]);
+    raw.y = pkd::pack_f16x2((f16)x[2], (f16)x[3]);
     *reinterpret_cast<uint2 *>(p) = raw;
 }
 
 // Rotate 4 pairs of one head row: row points at the head's element 0.
 template <int D>
-__device__ __forceinline__ void rotate_row(const bf16 *__restrict__ src, bf16 *__restrict__ dst,
+__device__ __forceinline__ void rotate_row(const bf16 *__restrict__ src, f16 *__restrict__ dst,
                                            int c, const float cs[4], const float sn[4]) {
     float x1[4], x2[4], y1[4], y2[4];
     load4(src + 4 * c, x1);
@@ -75,7 +81,7 @@ template <int D>
 __global__ __launch_bounds__(256) void k_fwd_prep(const int32_t *__restrict__ pos, int64_t T,
                                                   int hkv, float base,
                                                   const bf16 *__restrict__ k,
-                                                  bf16 *__restrict__ krot,
+                                                  f16 *__restrict__ krot,
                                                   float2 *__restrict__ table) {
     constexpr int G = D / 8;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -97,41 +103,80 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ po
                                                   const bf16 *__restrict__ k,
                                                   const bf16 *__restrict__ out,
                                                   const bf16 *__restrict__ dout,
-                                                  bf16 *__restrict__ qrot,
-                                                  bf16 *__restrict__ krot,
+                                                  f16 *__restrict__ qrot,
+                                                  f16 *__restrict__ krot,
                                                   float2 *__restrict__ table,
                                                   float *__restrict__ dsum,
-                                                  float *__restrict__ dq) {
+                                                  float *__restrict__ dq,
+                                                  float *__restrict__ blockmax) {
     constexpr int G = D / 8;
+    __shared__ float s_max[4];
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t t = gid / G;
     const int c = (int)(gid % G);
-    // T * G threads are launched in whole waves; the G threads of a token share a wave, so the
-    // shuffle reduction below only mixes lanes of the same token.  Threads past T exit together.
-    if (t >= T) return;
-    float cs[4], sn[4];
-    rope_factors<D>(pos, t, c, base, table, cs, sn);
-    for (int h = 0; h < hkv; ++h) {
-        const int64_t off = (t * hkv + h) * D;
-        rotate_row<D>(k + off, krot + off, c, cs, sn);
+    // The G threads of a token share a wave and agree on `active`, so the shuffle reduction
+    // below only mixes lanes of one token.
+    const bool active = t < T;
+    float amax = 0.f;
+    if (active) {
+        float cs[4], sn[4];
+        rope_factors<D>(pos, t, c, base, table, cs, sn);
+        for (int h = 0; h < hkv; ++h) {
+            const int64_t off = (t * hkv + h) * D;
+            rotate_row<D>(k + off, krot + off, c, cs, sn);
+        }
+        const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int h = 0; h < hq; ++h) {
+            const int64_t off = (t * hq + h) * D;
+            rotate_row<D>(q + off, qrot + off, c, cs, sn);
+            float o1[4], o2[4], g1[4], g2[4];
+            load4(out + off + 4 * c, o1);
+            load4(out + off + D / 2 + 4 * c, o2);
+            load4(dout + off + 4 * c, g1);
+            load4(dout + off + D / 2 + 4 * c, g2);
+            float part = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                part += o1[kk] * g1[kk] + o2[kk] * g2[kk];
+                amax = fmaxf(amax, fmaxf(fabsf(g1[kk]), fabsf(g2[kk])));
+            }
+#pragma unroll
+            for (int s = G / 2; s > 0; s >>= 1) part += __shfl_xor(part, s, 64);
+            if (c == 0) dsum[(int64_t)h * T + t] = part;
+            *reinterpret_cast<float4 *>(dq + off + 4 * c) = zero4;
+            *reinterpret_cast<float4 *>(dq + off + D / 2 + 4 * c) = zero4;
+        }
     }
-    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int h = 0; h < hq; ++h) {
-        const int64_t off = (t * hq + h) * D;
-        rotate_row<D>(q + off, qrot + off, c, cs, sn);
-        float o1[4], o2[4], g1[4], g2[4];
-        load4(out + off + 4 * c, o1);
-        load4(out + off + D / 2 + 4 * c, o2);
-        load4(dout + off + 4 * c, g1);
-        load4(dout + off + D / 2 + 4 * c, g2);
-        float part = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) part += o1[kk] * g1[kk] + o2[kk] * g2[kk];
+    for (int s = 32; s > 0; s >>= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        blockmax[blockIdx.x] = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+}
+
+// One workgroup: sigma = 2^e with max|dout| * sigma in [1, 2) (sigma = 1 when the maximum is 0
+// or not finite); writes {sigma, 1/sigma}.
+__global__ __launch_bounds__(256) void k_bwd_scale(const float *__restrict__ blockmax, int nb,
+                                                   float *__restrict__ scale) {
+    __shared__ float s_max[4];
+    float m = 0.f;
+    for (int i = threadIdx.x; i < nb; i += 256) m = fmaxf(m, blockmax[i]);
 #pragma unroll
-        for (int s = G / 2; s > 0; s >>= 1) part += __shfl_xor(part, s, 64);
-        if (c == 0) dsum[(int64_t)h * T + t] = part;
-        *reinterpret_cast<float4 *>(dq + off + 4 * c) = zero4;
-        *reinterpret_cast<float4 *>(dq + off + D / 2 + 4 * c) = zero4;
+    for (int s = 32; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+        int ex = 0;
+        float sigma = 1.f;
+        if (m > 0.f && m <= 3.0e38f) {
+            (void)frexpf(m, &ex);           // m = f * 2^ex, f in [0.5, 1)
+            ex = min(max(1 - ex, -100), 100);
+            sigma = ldexpf(1.f, ex);
+        }
+        scale[0] = sigma;
+        scale[1] = 1.f / sigma;
     }
 }
 
@@ -165,43 +210,46 @@ __global__ __launch_bounds__(256) void k_bwd_post(int64_t T, int hq,
     }
 }
 
-unsigned grid_for(int64_t T, int d) { return (unsigned)((T * (d / 8) + 255) / 256); }
-
 }  // namespace
 
 namespace pk {
 
+unsigned prep_blocks(int64_t T, int d) { return (unsigned)((T * (d / 8) + 255) / 256); }
+
 hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, void *krot, void *rope,
                            hipStream_t s) {
-    const unsigned g = grid_for(r.T, r.d);
+    const unsigned g = prep_blocks(r.T, r.d);
     if (r.d == 128)
         k_fwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hkv, r.rope_base, (const bf16 *)k,
-                                           (bf16 *)krot, (float2 *)rope);
+                                           (f16 *)krot, (float2 *)rope);
     else
         k_fwd_prep<64><<<g, 256, 0, s>>>(r.pos, r.T, r.hkv, r.rope_base, (const bf16 *)k,
-                                          (bf16 *)krot, (float2 *)rope);
+                                          (f16 *)krot, (float2 *)rope);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *out,
                            const void *dout, void *qrot, void *krot, void *rope, float *dsum,
-                           float *dq, hipStream_t s) {
-    const unsigned g = grid_for(r.T, r.d);
+                           float *dq, float *blockmax, float *scale, hipStream_t s) {
+    const unsigned g = prep_blocks(r.T, r.d);
     if (r.d == 128)
         k_bwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
                                            (const bf16 *)k, (const bf16 *)out,
-                                           (const bf16 *)dout, (bf16 *)qrot, (bf16 *)krot,
-                                           (float2 *)rope, dsum, dq);
+                                           (const bf16 *)dout, (f16 *)qrot, (f16 *)krot,
+                                           (float2 *)rope, dsum, dq, blockmax);
     else
         k_bwd_prep<64><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
                                           (const bf16 *)k, (const bf16 *)out,
-                                          (const bf16 *)dout, (bf16 *)qrot, (bf16 *)krot,
-                                          (float2 *)rope, dsum, dq);
+                                          (const bf16 *)dout, (f16 *)qrot, (f16 *)krot,
+                                          (float2 *)rope, dsum, dq, blockmax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_bwd_scale<<<1, 256, 0, s>>>(blockmax, (int)g, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_post(const RopeArgs &r, const void *rope, float *dq, hipStream_t s) {
-    const unsigned g = grid_for(r.T, r.d);
+    const unsigned g = prep_blocks(r.T, r.d);
     if (r.d == 128)
         k_bwd_post<128><<<g, 256, 0, s>>>(r.T, r.hq, (const float2 *)rope, dq);
     else
