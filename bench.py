@@ -146,7 +146,7 @@ def main():
     del metas
     step_ms = ev0.elapsed_time(ev1) / args.steps
     kern = {}
-    for name in ("meta", "fwd_prep", "fwd", "bwd_prep", "bwd", "bwd_post"):
+    for name in ("meta", "fwd_prep", "fwd", "bwd_prep", "bwd", "bwd_dq"):
         ms, n = pk.prof_query(name)
         kern[name] = {"total_ms": ms, "launches": n, "avg_us": 1000.0 * ms / max(n, 1)}
     print("bench: timed %d steps, %.2f ms/step (wall %.2f s)" % (args.steps, step_ms, wall),
@@ -155,13 +155,18 @@ def main():
     fwd_flops, bwd_flops = O.attn_flops(lengths, w.hq, w.head_dim)
     layer_ms = step_ms / L
     tflops = (fwd_flops + bwd_flops) * L / (step_ms * 1e-3) / 1e12
-    bwd_us = kern["bwd"]["avg_us"]
-    fwd_us = kern["fwd"]["avg_us"]
+    # algorithmic FLOPs of each attention kernel over the kept pairs P: the forward's 2 products;
+    # the key-outer backward's S, dP, dV, dK (4 products); the query-outer backward's dQ product
+    # (its recomputed S and dP are counted once already, in the key-outer kernel)
+    unit = fwd_flops // 2
+    algo = {"fwd": 2 * unit, "bwd": 4 * unit, "bwd_dq": unit}
+    achieved = {k: algo[k] / (kern[k]["avg_us"] * 1e-6) / 1e12 for k in algo}
+    dominant = max(algo, key=lambda k: kern[k]["avg_us"])
     per_layer_fwd_ms = (kern["fwd_prep"]["total_ms"] + kern["fwd"]["total_ms"]) / args.steps / L
     per_layer_bwd_ms = (kern["bwd_prep"]["total_ms"] + kern["bwd"]["total_ms"]
-                        + kern["bwd_post"]["total_ms"]) / args.steps / L
-    bwd_achieved = bwd_flops / (bwd_us * 1e-6) / 1e12
-    fwd_achieved = fwd_flops / (fwd_us * 1e-6) / 1e12
+                        + kern["bwd_dq"]["total_ms"]) / args.steps / L
+    kernel_names = {"fwd": "k_attn_fwd (forward)", "bwd": "k_attn_bwd_kv (backward dK, dV)",
+                    "bwd_dq": "k_attn_bwd_q (backward dQ)"}
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -188,11 +193,11 @@ def main():
         "ms_per_layer_bwd": round(per_layer_bwd_ms, 4),
         "build_meta_us": round(kern["meta"]["avg_us"], 2),
         "kernels_avg_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
-        "fwd_kernel_tflops": round(fwd_achieved, 2),
+        "kernels_algorithmic_tflops": {k: round(v, 2) for k, v in achieved.items()},
         "roofline": {
-            "kernel": "k_attn_bwd (backward attention)",
-            "bound": "mfma", "achieved": round(bwd_achieved, 2), "peak": PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(bwd_achieved / PEAK_TFLOPS, 4), "traffic": None,
+            "kernel": kernel_names[dominant],
+            "bound": "mfma", "achieved": round(achieved[dominant], 2), "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved[dominant] / PEAK_TFLOPS, 4), "traffic": None,
         },
     }
     if not args.no_cpu_baseline:

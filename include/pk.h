@@ -125,7 +125,8 @@ pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *
                       int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float rope_base,
                       void *out, float *lse, void *ws, size_t ws_bytes, void *hip_stream);
 
-/* Workspace bytes pk_attn_bwd needs: rotated Q and K, the RoPE table and rowsum(dout * out). */
+/* Workspace bytes pk_attn_bwd needs: rotated Q and K, the RoPE table, rowsum(dout * out) and
+ * the dout scale. */
 size_t pk_attn_bwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d);
 
 /* Backward of pk_attn_fwd for the loss sum(out * dout): float32 dq [T,hq,d], dk and dv
@@ -148,9 +149,9 @@ typedef enum pk_kernel_kind {
     PK_K_META = 0,        /* all metadata-build kernels of one pk_build_meta */
     PK_K_FWD_PREP = 1,    /* forward prologue: RoPE table + rotated K */
     PK_K_FWD = 2,         /* forward attention */
-    PK_K_BWD_PREP = 3,    /* backward prologue: RoPE table, rotated Q/K, rowsum(dout*out), dq := 0 */
-    PK_K_BWD = 4,         /* backward attention (dK, dV, dQ accumulation) */
-    PK_K_BWD_POST = 5,    /* backward epilogue: inverse RoPE on dq */
+    PK_K_BWD_PREP = 3,    /* backward prologue: RoPE table, rotated Q/K, rowsum(dout*out), dout scale */
+    PK_K_BWD = 4,         /* backward attention, key-tile outer: dK, dV */
+    PK_K_BWD_DQ = 5,      /* backward attention, query-tile outer: dQ */
     PK_K_COUNT = 6
 } pk_kernel_kind;
 

@@ -240,7 +240,7 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     hipError_t e;
     {
         ProfScope ps(PK_K_BWD_PREP, s);
-        e = pk::launch_bwd_prep(ra, q, k, out, dout, w + W.qrot, w + W.krot, w + W.rope, dsum, dq,
+        e = pk::launch_bwd_prep(ra, q, k, out, dout, w + W.qrot, w + W.krot, w + W.rope, dsum,
                                 blockmax, scale, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
@@ -248,12 +248,13 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     {
         ProfScope ps(PK_K_BWD, s);
         e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, v, dout, lse, dsum, scale, w + W.rope,
-                           dq, dk, dv, s);
+                           dq, dk, dv, 0, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     {
-        ProfScope ps(PK_K_BWD_POST, s);
-        e = pk::launch_bwd_post(ra, w + W.rope, dq, s);
+        ProfScope ps(PK_K_BWD_DQ, s);
+        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, v, dout, lse, dsum, scale, w + W.rope,
+                           dq, dk, dv, 1, s);
     }
     return hip_status(e);
 }

@@ -9,22 +9,25 @@
 // formula in [UN-2023] "Introducing Unsloth：LLM 训练提速 30 倍", "手动 Autograd" (which derives
 // its gradients by hand), applied to A = softmax(Q K^T / sqrt(d) + M) V.
 //
-// Layout for CDNA4 (one workgroup = one backward work item, i.e. 128 keys, x one KV head):
-//   * the 4 waves own 32 keys each; K_rot and V of those keys sit in registers as the k operand
-//     of S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_f16), so each lane owns one key column;
-//   * dK^T and dV^T accumulate in registers over every query block AND every query head of the
-//     GQA group, so the group sum costs nothing and dK, dV are written once;
-//   * query blocks of 64 rows are staged in LDS row-major (for S, dP) and transposed (for the
-//     dV^T += dO^T P and dK^T += Q^T dS products); query rows of S and dP are fed in row_perm
-//     order so the transposed operands are single 16-byte LDS reads;
-//   * dS goes to LDS once per block, and dQ_rot += dS K_rot is computed by all four waves from
-//     LDS and accumulated into the float32 dq buffer with hardware float atomics (the inverse
-//     RoPE of dq runs in the epilogue pass once all atomics are done);
-//   * the mask is applied element-wise only on blocks that straddle a sequence boundary or the
-//     diagonal; blocks fully outside the wave's visible range skip their products;
-//   * operands are fp16 with fp32 accumulation.  dout enters scaled by the power of two sigma
-//     the prologue chose (max|dout| * sigma in [1, 2)), so dP and dS are sigma-scaled too; the
-//     results are unscaled exactly by 1/sigma when dQ, dK and dV are written.
+// Two kernels, neither with atomics, so every gradient is written exactly once:
+//   k_attn_bwd_kv  one workgroup per backward work item (128 keys) x KV head.  The 4 waves own
+//                  32 keys each; K_rot and V of those keys are the k operands of S = Q K^T and
+//                  dP = dO V^T (v_mfma_f32_32x32x16_f16), dK^T and dV^T accumulate in registers
+//                  over every query block AND every query head of the GQA group (so the group
+//                  sum is free), and dK, dV are written once.
+//   k_attn_bwd_q   one workgroup per forward work item (128 queries) x query head, laid out like
+//                  the forward: S^T = K Q^T and dP^T = V dO^T give each lane one query, so its
+//                  lse and D are per-lane scalars; dQ^T += K^T dS^T accumulates in registers and
+//                  dQ is rotated back by R(-theta) and written once.
+// Recomputing S and dP in the second kernel costs two extra products; it replaces float atomics
+// on dQ (whose throughput, about 2.6 TB/s on this part, made them slower than the recompute),
+// a zero-fill of dq and a separate inverse-rotation pass.
+//
+// Common to both: the mask is applied element-wise only on tiles that straddle a sequence
+// boundary or the diagonal, and tiles outside a wave's visible range skip their products;
+// operands are fp16 with fp32 accumulation; dout enters scaled by the power of two sigma the
+// prologue chose (max|dout| * sigma in [1, 2)), so dP and dS are sigma-scaled and the results
+// are unscaled exactly by 1/sigma when written.
 #include "pk_internal.h"
 #include "pk_device.h"
 
@@ -41,10 +44,10 @@ struct BwdArgs {
     const float *dsum;    // [hq, T]
     const float *dscale;  // {sigma, 1/sigma}
     const float2 *rope;   // [T, D/2]
-    const int32_t *items; // [n_items, 8] longest first
+    const int32_t *items; // [n_items, 8] longest first (backward list for _kv, forward for _q)
     const int32_t *pos;   // [T]
     const int32_t *hdr;
-    float *dq;            // [T, hq, D]  (accumulator, zeroed by the prologue pass)
+    float *dq;            // [T, hq, D]
     float *dk;            // [T, hkv, D]
     float *dv;            // [T, hkv, D]
     int64_t T;
@@ -52,27 +55,25 @@ struct BwdArgs {
     float scale;
 };
 
+// ------------------------------------------------------------------------------------------
+// dK, dV: key-tile outer
+// ------------------------------------------------------------------------------------------
 template <int D>
-struct BwdSmem {
+struct KvSmem {
     static constexpr int BQ = 64;        // query rows per block
-    static constexpr int BKV = 128;      // keys per workgroup
     static constexpr int QP = D + 8;     // row-major Q / dO pitch
     static constexpr int TP = BQ + 8;    // transposed Q / dO pitch
-    static constexpr int SP = BKV + 8;   // dS pitch
-    static constexpr int KTP = BKV + 8;  // transposed K pitch
     f16 q[BQ * QP];
     f16 dO[BQ * QP];
     f16 qt[D * TP];
     f16 dOt[D * TP];
-    f16 ds[BQ * SP];
-    f16 kt[D * KTP];
     float lse[BQ];   // lse * log2(e); +inf for rows past the item
     float dd[BQ];    // D_i * sigma
     int lo[BQ];      // first key of the row's sequence; INT_MAX past the item
 };
 
 template <int D>
-__device__ void bwd_zero_tile(const BwdArgs &a, int tile, int kvh) {
+__device__ void kv_zero_tile(const BwdArgs &a, int tile, int kvh) {
     const int64_t r0 = (int64_t)tile * PK_TILE_ROWS;
     const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int e = threadIdx.x; e < PK_TILE_ROWS * (D / 4); e += blockDim.x) {
@@ -85,38 +86,77 @@ __device__ void bwd_zero_tile(const BwdArgs &a, int tile, int kvh) {
     }
 }
 
-__device__ __forceinline__ f16x8 load_as_f16x8(const f16 *p, float) { return load_f16x8(p); }
-__device__ __forceinline__ f16x8 load_as_f16x8(const bf16 *p, float scale) {
-    return bf16x8_to_f16x8(load_bf16x8(p), scale);
-}
+// Per-thread share of one staged query block, loaded from global memory one iteration ahead so
+// the loads overlap the current block's products.
+template <int D>
+struct KvPrefetch {
+    static constexpr int N = (KvSmem<D>::BQ / 2) * (D / 8) / 256;  // row pairs x 8 columns
+    uint4 q[2 * N];   // Q_rot, fp16 bits
+    uint4 g[2 * N];   // dout, bf16 bits
+    float lse, dd;
+    int lo;
+};
 
-// Stage rows [qb, qb+BQ) of one head of a [T, H, D] tensor (fp16, or bf16 times `scale`) into
-// LDS as fp16, row-major and transposed.  Each thread moves a pair of rows x 8 columns; rows at
-// or past `q_end` are zero.
-template <int D, typename Src>
-__device__ __forceinline__ void stage_rows(const Src *__restrict__ src, float scale, int H, int h,
-                                           int qb, int q_end, f16 *rowmaj, f16 *trans) {
-    using S = BwdSmem<D>;
-    for (int e = threadIdx.x; e < (S::BQ / 2) * (D / 8); e += 256) {
+template <int D>
+__device__ __forceinline__ void kv_prefetch(const BwdArgs &a, int h, int qb, int q_end,
+                                            KvPrefetch<D> &pf) {
+    using S = KvSmem<D>;
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < KvPrefetch<D>::N; ++u) {
+        const int e = threadIdx.x + 256 * u;
         const int rp = e % (S::BQ / 2), ch = e / (S::BQ / 2);
         const int i0 = qb + 2 * rp;
-        const f16x8 x0 = i0 < q_end ? load_as_f16x8(src + ((int64_t)i0 * H + h) * D + ch * 8, scale) : zero_f16x8();
-        const f16x8 x1 = i0 + 1 < q_end ? load_as_f16x8(src + ((int64_t)(i0 + 1) * H + h) * D + ch * 8, scale) : zero_f16x8();
-        store_f16x8(rowmaj + (2 * rp) * S::QP + ch * 8, x0);
-        store_f16x8(rowmaj + (2 * rp + 1) * S::QP + ch * 8, x1);
+        const int64_t o0 = ((int64_t)i0 * a.hq + h) * D + ch * 8;
+        const int64_t o1 = o0 + (int64_t)a.hq * D;
+        pf.q[2 * u] = i0 < q_end ? *reinterpret_cast<const uint4 *>(a.qrot + o0) : z;
+        pf.q[2 * u + 1] = i0 + 1 < q_end ? *reinterpret_cast<const uint4 *>(a.qrot + o1) : z;
+        pf.g[2 * u] = i0 < q_end ? *reinterpret_cast<const uint4 *>(a.dout + o0) : z;
+        pf.g[2 * u + 1] = i0 + 1 < q_end ? *reinterpret_cast<const uint4 *>(a.dout + o1) : z;
+    }
+    if (threadIdx.x < S::BQ) {
+        const int i = qb + threadIdx.x;
+        const bool ok = i < q_end;
+        pf.lse = ok ? a.lse[(int64_t)h * a.T + i] : INFINITY;
+        pf.dd = ok ? a.dsum[(int64_t)h * a.T + i] : 0.f;
+        pf.lo = ok ? i - a.pos[i] : INT_MAX;
+    }
+}
+
+// Write a prefetched block into LDS: Q_rot and sigma * dout as fp16, row-major and transposed.
+template <int D>
+__device__ __forceinline__ void kv_stage(const KvPrefetch<D> &pf, float sigma, KvSmem<D> &sm) {
+    using S = KvSmem<D>;
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            *reinterpret_cast<uint32_t *>(trans + (ch * 8 + s) * S::TP + 2 * rp) = pack_f16x2(x0[s], x1[s]);
+    for (int u = 0; u < KvPrefetch<D>::N; ++u) {
+        const int e = threadIdx.x + 256 * u;
+        const int rp = e % (S::BQ / 2), ch = e / (S::BQ / 2);
+        const f16x8 q0 = __builtin_bit_cast(f16x8, pf.q[2 * u]);
+        const f16x8 q1 = __builtin_bit_cast(f16x8, pf.q[2 * u + 1]);
+        const f16x8 g0 = bf16x8_to_f16x8(__builtin_bit_cast(bf16x8, pf.g[2 * u]), sigma);
+        const f16x8 g1 = bf16x8_to_f16x8(__builtin_bit_cast(bf16x8, pf.g[2 * u + 1]), sigma);
+        store_f16x8(sm.q + (2 * rp) * S::QP + ch * 8, q0);
+        store_f16x8(sm.q + (2 * rp + 1) * S::QP + ch * 8, q1);
+        store_f16x8(sm.dO + (2 * rp) * S::QP + ch * 8, g0);
+        store_f16x8(sm.dO + (2 * rp + 1) * S::QP + ch * 8, g1);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            *reinterpret_cast<uint32_t *>(sm.qt + (ch * 8 + x) * S::TP + 2 * rp) = pack_f16x2(q0[x], q1[x]);
+            *reinterpret_cast<uint32_t *>(sm.dOt + (ch * 8 + x) * S::TP + 2 * rp) = pack_f16x2(g0[x], g1[x]);
+        }
+    }
+    if (threadIdx.x < S::BQ) {
+        sm.lse[threadIdx.x] = pf.lse * kLog2e;
+        sm.dd[threadIdx.x] = pf.dd * sigma;
+        sm.lo[threadIdx.x] = pf.lo;
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
-    using S = BwdSmem<D>;
-    constexpr int BQ = S::BQ, BKV = S::BKV;
+__global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
+    using S = KvSmem<D>;
+    constexpr int BQ = S::BQ;
     constexpr int NKK = D / 16, NDB = D / 32;
-    constexpr int NQB = 2 * NDB;          // 32x32 blocks of one dQ block (2 query x NDB d)
-    constexpr int QB_PER_WAVE = NQB / 4;  // 2 for D = 128, 1 for D = 64
     __shared__ __attribute__((aligned(16))) S sm;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -124,11 +164,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
     const int r = blockIdx.x / a.hkv, kvh = blockIdx.x % a.hkv;
     const int32_t *it = a.items + (int64_t)r * PK_ITEM_FIELDS;
     if (a.hdr[0] != 0) {
-        bwd_zero_tile<D>(a, it[7], kvh);
+        kv_zero_tile<D>(a, it[7], kvh);
         return;
     }
     const int kv_start = it[0], kv_end = it[1], q_start = it[2], q_end = it[3];
-    const int64_t T = a.T;
     const float sigma = a.dscale[0], inv_sigma = a.dscale[1];
 
     const int j = kv_start + 32 * w + n32;  // this lane's key
@@ -136,7 +175,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
     const int wk0 = kv_start + 32 * w;
     const bool wave_active = wk0 < kv_end;
     const int wk_last = min(wk0 + 31, kv_end - 1);
-    const int blk_last = kv_end - 1;
+
+    const int nqb = (q_end - q_start + BQ - 1) / BQ;
+    const int n_iter = a.group * nqb;
+    KvPrefetch<D> pf;
+    kv_prefetch<D>(a, kvh * a.group, q_start, q_end, pf);
 
     // K_rot and V of this lane's key, as k operands (d in [16kk + 8hb, +8))
     f16x8 kf[NKK], vf[NKK];
@@ -148,16 +191,6 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
             vf[kk] = kvalid ? bf16x8_to_f16x8(load_bf16x8(a.v + row + 16 * kk)) : zero_f16x8();
         }
     }
-    // K_rot^T of the workgroup's 128 keys -> LDS, for dQ
-    for (int e = tid; e < (BKV / 2) * (D / 8); e += 256) {
-        const int kp = e % (BKV / 2), ch = e / (BKV / 2);
-        const int j0 = kv_start + 2 * kp;
-        const f16x8 x0 = j0 < kv_end ? load_f16x8(a.krot + ((int64_t)j0 * a.hkv + kvh) * D + ch * 8) : zero_f16x8();
-        const f16x8 x1 = j0 + 1 < kv_end ? load_f16x8(a.krot + ((int64_t)(j0 + 1) * a.hkv + kvh) * D + ch * 8) : zero_f16x8();
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            *reinterpret_cast<uint32_t *>(sm.kt + (ch * 8 + s) * S::KTP + 2 * kp) = pack_f16x2(x0[s], x1[s]);
-    }
 
     f32x16 dka[NDB], dva[NDB];
 #pragma unroll
@@ -165,111 +198,67 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
         dka[db] = zero_f32x16();
         dva[db] = zero_f32x16();
     }
+    const float sl2 = a.scale * kLog2e;
 
-    for (int hh = 0; hh < a.group; ++hh) {
-        const int h = kvh * a.group + hh;
-        for (int qb = q_start; qb < q_end; qb += BQ) {
-            __syncthreads();
-            stage_rows<D>(a.qrot, 1.f, a.hq, h, qb, q_end, sm.q, sm.qt);
-            stage_rows<D>(a.dout, sigma, a.hq, h, qb, q_end, sm.dO, sm.dOt);
-            if (tid < BQ) {
-                const int i = qb + tid;
-                const bool ok = i < q_end;
-                sm.lse[tid] = ok ? a.lse[(int64_t)h * T + i] * kLog2e : INFINITY;
-                sm.dd[tid] = ok ? a.dsum[(int64_t)h * T + i] * sigma : 0.f;
-                sm.lo[tid] = ok ? i - a.pos[i] : INT_MAX;
+    for (int itn = 0; itn < n_iter; ++itn) {
+        const int hh = itn / nqb;
+        const int qb = q_start + (itn - hh * nqb) * BQ;
+        __syncthreads();
+        kv_stage<D>(pf, sigma, sm);
+        __syncthreads();
+        if (itn + 1 < n_iter) {
+            const int hn = (itn + 1) / nqb;
+            kv_prefetch<D>(a, kvh * a.group + hn, q_start + (itn + 1 - hn * nqb) * BQ, q_end, pf);
+        }
+        if (!wave_active) continue;
+        const int nrows = min(BQ, q_end - qb);
+#pragma unroll
+        for (int qm = 0; qm < 2; ++qm) {
+            // rows [qb + 32qm, +32) of the block against this wave's 32 keys
+            const int r0 = 32 * qm;
+            const int hrows = min(32, nrows - r0);
+            if (hrows <= 0 || qb + r0 + hrows - 1 < wk0 || sm.lo[r0] > wk_last) continue;
+            const bool need_mask = !(qb + r0 >= wk0 + 31 && sm.lo[r0 + hrows - 1] <= wk0);
+            f32x16 sp = zero_f32x16(), dp = zero_f32x16();
+            {
+                const int row = r0 + row_perm(n32);
+                const f16 *qrow = sm.q + row * S::QP + 8 * hb;
+                const f16 *grow = sm.dO + row * S::QP + 8 * hb;
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    sp = mfma32(load_f16x8(qrow + 16 * kk), kf[kk], sp);
+                    dp = mfma32(load_f16x8(grow + 16 * kk), vf[kk], dp);
+                }
             }
-            __syncthreads();
-            const int nrows = min(BQ, q_end - qb);
-            const int lo_first = sm.lo[0], lo_last = sm.lo[nrows - 1];
-            // is any (query, key) pair of this block visible?
-            if (qb + nrows - 1 < kv_start || lo_first > blk_last) continue;
-
-            const bool active = wave_active && !(qb + nrows - 1 < wk0) && !(lo_first > wk_last);
-            if (active) {
-                const bool need_mask = !(qb >= wk0 + 31 && lo_last <= wk0);
-                f32x16 sp[2], dp[2];
 #pragma unroll
-                for (int qm = 0; qm < 2; ++qm) {
-                    sp[qm] = zero_f32x16();
-                    dp[qm] = zero_f32x16();
-                    const int row = 32 * qm + row_perm(n32);
-                    const f16 *qrow = sm.q + row * S::QP + 8 * hb;
-                    const f16 *grow = sm.dO + row * S::QP + 8 * hb;
-#pragma unroll
-                    for (int kk = 0; kk < NKK; ++kk) {
-                        sp[qm] = mfma32(load_f16x8(qrow + 16 * kk), kf[kk], sp[qm]);
-                        dp[qm] = mfma32(load_f16x8(grow + 16 * kk), vf[kk], dp[qm]);
-                    }
-                }
-                const float sl2 = a.scale * kLog2e;
-#pragma unroll
-                for (int qm = 0; qm < 2; ++qm) {
-#pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) {
-                        const int row = 32 * qm + row_perm(acc_row(rr, hb));
-                        float p = exp2f(sp[qm][rr] * sl2 - sm.lse[row]);
-                        if (need_mask) {
-                            const int i = qb + row;
-                            p = (j >= sm.lo[row] && j <= i) ? p : 0.f;
-                        }
-                        sp[qm][rr] = p;
-                        dp[qm][rr] = p * (dp[qm][rr] - sm.dd[row]);
-                    }
-                }
-                // dV^T += dO^T P,  dK^T += Q^T dS  (queries are the k dimension)
-#pragma unroll
-                for (int qm = 0; qm < 2; ++qm) {
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        f16x8 pb, sb;
-#pragma unroll
-                        for (int x = 0; x < 8; ++x) {
-                            pb[x] = (f16)sp[qm][8 * e + x];
-                            sb[x] = (f16)dp[qm][8 * e + x];
-                        }
-                        const int col = 32 * qm + 16 * e + 8 * hb;
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-                            const int drow = 32 * db + n32;
-                            dva[db] = mfma32(load_f16x8(sm.dOt + drow * S::TP + col), pb, dva[db]);
-                            dka[db] = mfma32(load_f16x8(sm.qt + drow * S::TP + col), sb, dka[db]);
-                        }
-                    }
-                }
-                // dS -> LDS [query][key]
-#pragma unroll
-                for (int qm = 0; qm < 2; ++qm)
-#pragma unroll
-                    for (int rr = 0; rr < 16; ++rr)
-                        sm.ds[(32 * qm + row_perm(acc_row(rr, hb))) * S::SP + 32 * w + n32] = (f16)dp[qm][rr];
-            } else {
-                for (int row = hb; row < BQ; row += 2) sm.ds[row * S::SP + 32 * w + n32] = (f16)0.f;
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = r0 + row_perm(acc_row(rr, hb));
+                float p = exp2f(sp[rr] * sl2 - sm.lse[row]);
+                if (need_mask) p = (j >= sm.lo[row] && j <= qb + row) ? p : 0.f;
+                sp[rr] = p;
+                dp[rr] = p * (dp[rr] - sm.dd[row]);
             }
-            __syncthreads();
-            // dQ_rot[qb .. qb+64) += scale * dS K_rot, split in 32x32 blocks over the 4 waves
+            // dV^T += dO^T P,  dK^T += Q^T dS  (queries are the k dimension)
 #pragma unroll
-            for (int u = 0; u < QB_PER_WAVE; ++u) {
-                const int pidx = w * QB_PER_WAVE + u;
-                const int qm = pidx / NDB, db = pidx % NDB;
-                f32x16 c = zero_f32x16();
-                const f16 *arow = sm.ds + (32 * qm + n32) * S::SP + 8 * hb;
-                const f16 *brow = sm.kt + (32 * db + n32) * S::KTP + 8 * hb;
+            for (int e = 0; e < 2; ++e) {
+                f16x8 pb, sb;
 #pragma unroll
-                for (int ks = 0; ks < BKV / 16; ++ks)
-                    c = mfma32(load_f16x8(arow + 16 * ks), load_f16x8(brow + 16 * ks), c);
-                const float cscale = a.scale * inv_sigma;
+                for (int x = 0; x < 8; ++x) {
+                    pb[x] = (f16)sp[8 * e + x];
+                    sb[x] = (f16)dp[8 * e + x];
+                }
+                const int col = r0 + 16 * e + 8 * hb;
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int i = qb + 32 * qm + acc_row(rr, hb);
-                    if (i < q_end)
-                        unsafeAtomicAdd(a.dq + ((int64_t)i * a.hq + h) * D + 32 * db + n32, c[rr] * cscale);
+                for (int db = 0; db < NDB; ++db) {
+                    const int drow = 32 * db + n32;
+                    dva[db] = mfma32(load_f16x8(sm.dOt + drow * S::TP + col), pb, dva[db]);
+                    dka[db] = mfma32(load_f16x8(sm.qt + drow * S::TP + col), sb, dka[db]);
                 }
             }
         }
     }
 
-    // epilogue: dV as is; dK = R(-theta) (scale * dK_rot)
+    // epilogue: dV as is; dK = R(-theta) (scale * dK_rot); both unscaled by 1/sigma
     if (kvalid) {
         float *dvrow = a.dv + ((int64_t)j * a.hkv + kvh) * D;
         float *dkrow = a.dk + ((int64_t)j * a.hkv + kvh) * D;
@@ -304,6 +293,162 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd(BwdArgs a) {
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// dQ: query-tile outer
+// ------------------------------------------------------------------------------------------
+template <int D>
+__device__ void q_zero_tile(const BwdArgs &a, int tile, int h) {
+    const int64_t r0 = (int64_t)tile * PK_TILE_ROWS;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = threadIdx.x; e < PK_TILE_ROWS * (D / 4); e += blockDim.x) {
+        const int64_t i = r0 + e / (D / 4);
+        if (i < a.T) *reinterpret_cast<float4 *>(a.dq + (i * a.hq + h) * D + (e % (D / 4)) * 4) = z;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
+    constexpr int BK = 64;        // keys per LDS tile
+    constexpr int KP = D + 8;     // row-major K / V pitch
+    constexpr int VP = BK + 8;    // transposed K pitch
+    constexpr int NKK = D / 16, NDB = D / 32, NMB = BK / 32;
+    __shared__ __attribute__((aligned(16))) f16 lds_k[BK * KP];
+    __shared__ __attribute__((aligned(16))) f16 lds_v[BK * KP];
+    __shared__ __attribute__((aligned(16))) f16 lds_kt[D * VP];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n32 = lane & 31, hb = lane >> 5;
+    const int r = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
+    const int kvh = h / a.group;
+    const int32_t *it = a.items + (int64_t)r * PK_ITEM_FIELDS;
+    if (a.hdr[0] != 0) {
+        q_zero_tile<D>(a, it[7], h);
+        return;
+    }
+    const int q_start = it[0], q_end = it[1], kv_start = it[2];
+    const int64_t T = a.T;
+    const float sigma = a.dscale[0], inv_sigma = a.dscale[1];
+
+    // this lane's query and its wave's query range
+    const int i = q_start + 32 * w + n32;
+    const bool qvalid = i < q_end;
+    const int ii = qvalid ? i : q_start;
+    const int lo_i = qvalid ? i - a.pos[i] : 0;
+    const int wq0 = q_start + 32 * w;
+    const bool wave_active = wq0 < q_end;
+    const int wq_last = min(wq0 + 31, q_end - 1);
+    const int wlo_min = wave_active ? wq0 - a.pos[wq0] : 0;
+    const int wlo_max = wave_active ? wq_last - a.pos[wq_last] : 0;
+    const float lse2 = qvalid ? a.lse[(int64_t)h * T + i] * kLog2e : INFINITY;
+    const float dd = qvalid ? a.dsum[(int64_t)h * T + i] * sigma : 0.f;
+
+    // Q_rot and sigma * dout of this lane's query as k operands (d in [16kk + 8hb, +8))
+    f16x8 qf[NKK], gf[NKK];
+    {
+        const int64_t row = ((int64_t)ii * a.hq + h) * D + 8 * hb;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            qf[kk] = qvalid ? load_f16x8(a.qrot + row + 16 * kk) : zero_f16x8();
+            gf[kk] = qvalid ? bf16x8_to_f16x8(load_bf16x8(a.dout + row + 16 * kk), sigma) : zero_f16x8();
+        }
+    }
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = zero_f32x16();
+    const float sl2 = a.scale * kLog2e;
+
+    const int kb_hi = ((q_end - 1) / BK) * BK;
+    const int kb_lo = (kv_start / BK) * BK;
+    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= BK) {
+        __syncthreads();
+        // K_rot tile -> lds_k (row-major) and lds_kt (transposed); V tile -> lds_v (row-major)
+        for (int e = tid; e < (BK / 2) * (D / 8); e += 256) {
+            const int kp = e % (BK / 2), ch = e / (BK / 2);
+            const int64_t j0 = k0 + 2 * kp;
+            const int64_t o0 = (j0 * a.hkv + kvh) * D + ch * 8, o1 = o0 + (int64_t)a.hkv * D;
+            const f16x8 x0 = j0 < T ? load_f16x8(a.krot + o0) : zero_f16x8();
+            const f16x8 x1 = j0 + 1 < T ? load_f16x8(a.krot + o1) : zero_f16x8();
+            const f16x8 v0 = j0 < T ? bf16x8_to_f16x8(load_bf16x8(a.v + o0)) : zero_f16x8();
+            const f16x8 v1 = j0 + 1 < T ? bf16x8_to_f16x8(load_bf16x8(a.v + o1)) : zero_f16x8();
+            store_f16x8(lds_k + (2 * kp) * KP + ch * 8, x0);
+            store_f16x8(lds_k + (2 * kp + 1) * KP + ch * 8, x1);
+            store_f16x8(lds_v + (2 * kp) * KP + ch * 8, v0);
+            store_f16x8(lds_v + (2 * kp + 1) * KP + ch * 8, v1);
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+                *reinterpret_cast<uint32_t *>(lds_kt + (ch * 8 + x) * VP + 2 * kp) = pack_f16x2(x0[x], x1[x]);
+        }
+        __syncthreads();
+        if (!wave_active) continue;
+        if (k0 > wq_last) continue;            // every key is after every query of the wave
+        if (k0 + BK - 1 < wlo_min) continue;   // every key is before the wave's first sequence
+        const bool need_mask = !(k0 + BK - 1 <= wq0 && k0 >= wlo_max);
+
+        // S^T = K Q^T and dP^T = V dO^T (keys x queries), key rows in row_perm order
+        f32x16 s[NMB], dp[NMB];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+            s[mb] = zero_f32x16();
+            dp[mb] = zero_f32x16();
+            const int row = (32 * mb + row_perm(n32)) * KP + 8 * hb;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                s[mb] = mfma32(load_f16x8(lds_k + row + 16 * kk), qf[kk], s[mb]);
+                dp[mb] = mfma32(load_f16x8(lds_v + row + 16 * kk), gf[kk], dp[mb]);
+            }
+        }
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                float p = exp2f(s[mb][rr] * sl2 - lse2);
+                if (need_mask) {
+                    const int jj = k0 + 32 * mb + row_perm(acc_row(rr, hb));
+                    p = (qvalid && jj >= lo_i && jj <= i) ? p : 0.f;
+                }
+                dp[mb][rr] = p * (dp[mb][rr] - dd);
+            }
+        }
+        // dQ^T (d x queries) += K^T (d x keys) * dS^T (keys x queries)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                f16x8 sb;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) sb[x] = (f16)dp[mb][8 * e + x];
+                const f16 *krow = lds_kt + n32 * VP + 32 * mb + 16 * e + 8 * hb;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) acc[db] = mfma32(load_f16x8(krow + 32 * db * VP), sb, acc[db]);
+            }
+        }
+    }
+
+    // epilogue: dQ = R(-theta) (scale / sigma * dQ_rot), written once
+    if (qvalid) {
+        float *row = a.dq + ((int64_t)i * a.hq + h) * D;
+        const float2 *cs = a.rope + (int64_t)i * (D / 2);
+        const float qscale = a.scale * inv_sigma;
+#pragma unroll
+        for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = 32 * db + 8 * g4 + 4 * hb;  // first half; partner d + D/2
+                float y1[4], y2[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float2 f = cs[d + x];
+                    const float x1 = acc[db][4 * g4 + x] * qscale;
+                    const float x2 = acc[db + NDB / 2][4 * g4 + x] * qscale;
+                    y1[x] = x1 * f.x + x2 * f.y;
+                    y2[x] = x2 * f.x - x1 * f.y;
+                }
+                *reinterpret_cast<float4 *>(row + d) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+                *reinterpret_cast<float4 *>(row + d + D / 2) = make_float4(y2[0], y2[1], y2[2], y2[3]);
+            }
+    }
+}
+
 }  // namespace
 
 namespace pk {
@@ -311,17 +456,16 @@ namespace pk {
 hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                       const void *krot, const void *v, const void *dout, const float *lse,
                       const float *dsum, const float *scale, const void *rope, float *dq,
-                      float *dk, float *dv, hipStream_t s) {
+                      float *dk, float *dv, int which, hipStream_t s) {
     BwdArgs a;
     a.qrot = (const f16 *)qrot;
     a.krot = (const f16 *)krot;
-    a.dscale = scale;
     a.v = (const bf16 *)v;
     a.dout = (const bf16 *)dout;
     a.lse = lse;
     a.dsum = dsum;
+    a.dscale = scale;
     a.rope = (const float2 *)rope;
-    a.items = m.bwd_items;
     a.pos = m.pos;
     a.hdr = m.hdr;
     a.dq = dq;
@@ -332,11 +476,21 @@ hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
     a.hkv = sh.hkv;
     a.group = sh.hq / sh.hkv;
     a.scale = sh.scale;
-    const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hkv;
-    if (sh.d == 128)
-        k_attn_bwd<128><<<grid, 256, 0, s>>>(a);
-    else
-        k_attn_bwd<64><<<grid, 256, 0, s>>>(a);
+    if (which == 0) {
+        a.items = m.bwd_items;
+        const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hkv;
+        if (sh.d == 128)
+            k_attn_bwd_kv<128><<<grid, 256, 0, s>>>(a);
+        else
+            k_attn_bwd_kv<64><<<grid, 256, 0, s>>>(a);
+    } else {
+        a.items = m.fwd_items;
+        const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hq;
+        if (sh.d == 128)
+            k_attn_bwd_q<128><<<grid, 256, 0, s>>>(a);
+        else
+            k_attn_bwd_q<64><<<grid, 256, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -57,8 +57,7 @@ hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, void *krot, void *r
 unsigned prep_blocks(int64_t T, int d);
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *out,
                            const void *dout, void *qrot, void *krot, void *rope, float *dsum,
-                           float *dq, float *blockmax, float *scale, hipStream_t s);
-hipError_t launch_bwd_post(const RopeArgs &r, const void *rope, float *dq, hipStream_t s);
+                           float *blockmax, float *scale, hipStream_t s);
 
 struct AttnShape {
     int64_t T;
@@ -70,6 +69,6 @@ hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, co
 hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                       const void *krot, const void *v, const void *dout, const float *lse,
                       const float *dsum, const float *scale, const void *rope, float *dq,
-                      float *dk, float *dv, hipStream_t s);
+                      float *dk, float *dv, int which /* 0: dK, dV; 1: dQ */, hipStream_t s);
 
 }  // namespace pk

@@ -1,5 +1,5 @@
-// Prologue and epilogue passes of the attention calls: the RoPE rotation table, rotated K (and Q
-// for the backward), rowsum(dout * out), and the inverse rotation of dq.
+// Prologue passes of the attention calls: the RoPE rotation table, rotated K (and Q for the
+// backward), rowsum(dout * out) and the dout scale.
 //
 // Rotate-half RoPE ([UN-2023] "Introducing Unsloth：LLM 训练提速 30 倍", "OpenAI Triton kernels"):
 // with x1 the first half of a head vector and x2 the second half,
@@ -17,7 +17,7 @@
 // dS, both scaled by sigma, unscaled exactly at the end) stay inside fp16's range whatever the
 // magnitude of the incoming gradient.
 //
-// Thread layout of the three per-token kernels: one thread per (token t, group c of 4 rotation pairs);
+// Thread layout of the two per-token kernels: one thread per (token t, group c of 4 rotation pairs);
 // the thread owns elements d in [4c, 4c+4) and their partners d + D/2 for every head, so each
 // rotation stays inside one thread and a token's D/8 threads read each half-row contiguously.
 #include "pk_internal.h"
@@ -107,7 +107,6 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ po
                                                   f16 *__restrict__ krot,
                                                   float2 *__restrict__ table,
                                                   float *__restrict__ dsum,
-                                                  float *__restrict__ dq,
                                                   float *__restrict__ blockmax) {
     constexpr int G = D / 8;
     __shared__ float s_max[4];
@@ -125,7 +124,6 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ po
             const int64_t off = (t * hkv + h) * D;
             rotate_row<D>(k + off, krot + off, c, cs, sn);
         }
-        const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int h = 0; h < hq; ++h) {
             const int64_t off = (t * hq + h) * D;
             rotate_row<D>(q + off, qrot + off, c, cs, sn);
@@ -143,8 +141,6 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ po
 #pragma unroll
             for (int s = G / 2; s > 0; s >>= 1) part += __shfl_xor(part, s, 64);
             if (c == 0) dsum[(int64_t)h * T + t] = part;
-            *reinterpret_cast<float4 *>(dq + off + 4 * c) = zero4;
-            *reinterpret_cast<float4 *>(dq + off + D / 2 + 4 * c) = zero4;
         }
     }
 #pragma unroll
@@ -180,36 +176,6 @@ __global__ __launch_bounds__(256) void k_bwd_scale(const float *__restrict__ blo
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void k_bwd_post(int64_t T, int hq,
-                                                  const float2 *__restrict__ table,
-                                                  float *__restrict__ dq) {
-    constexpr int G = D / 8;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t t = gid / G;
-    const int c = (int)(gid % G);
-    if (t >= T) return;
-    const float4 *tp = reinterpret_cast<const float4 *>(table + t * (D / 2) + 4 * c);
-    const float4 f01 = tp[0], f23 = tp[1];
-    const float cs[4] = {f01.x, f01.z, f23.x, f23.z};
-    const float sn[4] = {f01.y, f01.w, f23.y, f23.w};
-    for (int h = 0; h < hq; ++h) {
-        float *row = dq + (t * hq + h) * D;
-        const float4 a = *reinterpret_cast<const float4 *>(row + 4 * c);
-        const float4 b = *reinterpret_cast<const float4 *>(row + D / 2 + 4 * c);
-        const float x1[4] = {a.x, a.y, a.z, a.w};
-        const float x2[4] = {b.x, b.y, b.z, b.w};
-        float y1[4], y2[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            y1[k] = x1[k] * cs[k] + x2[k] * sn[k];
-            y2[k] = x2[k] * cs[k] - x1[k] * sn[k];
-        }
-        *reinterpret_cast<float4 *>(row + 4 * c) = make_float4(y1[0], y1[1], y1[2], y1[3]);
-        *reinterpret_cast<float4 *>(row + D / 2 + 4 * c) = make_float4(y2[0], y2[1], y2[2], y2[3]);
-    }
-}
-
 }  // namespace
 
 namespace pk {
@@ -230,30 +196,21 @@ hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, void *krot, void *r
 
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *out,
                            const void *dout, void *qrot, void *krot, void *rope, float *dsum,
-                           float *dq, float *blockmax, float *scale, hipStream_t s) {
+                           float *blockmax, float *scale, hipStream_t s) {
     const unsigned g = prep_blocks(r.T, r.d);
     if (r.d == 128)
         k_bwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
                                            (const bf16 *)k, (const bf16 *)out,
                                            (const bf16 *)dout, (f16 *)qrot, (f16 *)krot,
-                                           (float2 *)rope, dsum, dq, blockmax);
+                                           (float2 *)rope, dsum, blockmax);
     else
         k_bwd_prep<64><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
                                           (const bf16 *)k, (const bf16 *)out,
                                           (const bf16 *)dout, (f16 *)qrot, (f16 *)krot,
-                                          (float2 *)rope, dsum, dq, blockmax);
+                                          (float2 *)rope, dsum, blockmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_bwd_scale<<<1, 256, 0, s>>>(blockmax, (int)g, scale);
-    return hipGetLastError();
-}
-
-hipError_t launch_bwd_post(const RopeArgs &r, const void *rope, float *dq, hipStream_t s) {
-    const unsigned g = prep_blocks(r.T, r.d);
-    if (r.d == 128)
-        k_bwd_post<128><<<g, 256, 0, s>>>(r.T, r.hq, (const float2 *)rope, dq);
-    else
-        k_bwd_post<64><<<g, 256, 0, s>>>(r.T, r.hq, (const float2 *)rope, dq);
     return hipGetLastError();
 }
 
