@@ -70,6 +70,7 @@ FwdWorkspace fwd_workspace(int64_t T, int hq, int hkv, int d) {
     FwdWorkspace w;
     size_t off = 0;
     w.krot = off; off += align256((size_t)T * hkv * d * 2);
+    w.vh = off; off += align256((size_t)T * hkv * d * 2);
     w.rope = off; off += align256((size_t)T * (d / 2) * 8);
     w.total = off;
     return w;
@@ -80,6 +81,7 @@ BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d) {
     size_t off = 0;
     w.qrot = off; off += align256((size_t)T * hq * d * 2);
     w.krot = off; off += align256((size_t)T * hkv * d * 2);
+    w.vh = off; off += align256((size_t)T * hkv * d * 2);
     w.rope = off; off += align256((size_t)T * (d / 2) * 8);
     w.dsum = off; off += align256((size_t)T * hq * 4);
     w.blockmax = off; off += align256((size_t)prep_blocks(T, d) * 4);
@@ -206,13 +208,13 @@ pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *
     hipError_t e;
     {
         ProfScope ps(PK_K_FWD_PREP, s);
-        e = pk::launch_fwd_prep(ra, k, w + W.krot, w + W.rope, s);
+        e = pk::launch_fwd_prep(ra, k, v, w + W.krot, w + W.vh, w + W.rope, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
     {
         ProfScope ps(PK_K_FWD, s);
-        e = pk::launch_fwd(sh, *meta, q, w + W.krot, v, w + W.rope, out, lse, s);
+        e = pk::launch_fwd(sh, *meta, q, w + W.krot, w + W.vh, w + W.rope, out, lse, s);
     }
     return hip_status(e);
 }
@@ -240,21 +242,21 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     hipError_t e;
     {
         ProfScope ps(PK_K_BWD_PREP, s);
-        e = pk::launch_bwd_prep(ra, q, k, out, dout, w + W.qrot, w + W.krot, w + W.rope, dsum,
-                                blockmax, scale, s);
+        e = pk::launch_bwd_prep(ra, q, k, v, out, dout, w + W.qrot, w + W.krot, w + W.vh,
+                                w + W.rope, dsum, blockmax, scale, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
     {
         ProfScope ps(PK_K_BWD, s);
-        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, v, dout, lse, dsum, scale, w + W.rope,
-                           dq, dk, dv, 0, s);
+        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, dout, lse, dsum, scale,
+                           w + W.rope, dq, dk, dv, 0, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     {
         ProfScope ps(PK_K_BWD_DQ, s);
-        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, v, dout, lse, dsum, scale, w + W.rope,
-                           dq, dk, dv, 1, s);
+        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, dout, lse, dsum, scale,
+                           w + W.rope, dq, dk, dv, 1, s);
     }
     return hip_status(e);
 }

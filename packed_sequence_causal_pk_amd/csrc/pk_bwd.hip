@@ -38,7 +38,7 @@ using namespace pkd;
 struct BwdArgs {
     const f16 *qrot;      // [T, hq, D] fp16
     const f16 *krot;      // [T, hkv, D] fp16
-    const bf16 *v;        // [T, hkv, D]
+    const f16 *v;         // [T, hkv, D] fp16 copy of v
     const bf16 *dout;     // [T, hq, D]
     const float *lse;     // [hq, T]
     const float *dsum;    // [hq, T]
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             kf[kk] = kvalid ? load_f16x8(a.krot + row + 16 * kk) : zero_f16x8();
-            vf[kk] = kvalid ? bf16x8_to_f16x8(load_bf16x8(a.v + row + 16 * kk)) : zero_f16x8();
+            vf[kk] = kvalid ? load_f16x8(a.v + row + 16 * kk) : zero_f16x8();
         }
     }
 
@@ -309,12 +309,9 @@ __device__ void q_zero_tile(const BwdArgs &a, int tile, int h) {
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     constexpr int BK = 64;        // keys per LDS tile
-    constexpr int KP = D + 8;     // row-major K / V pitch
-    constexpr int VP = BK + 8;    // transposed K pitch
     constexpr int NKK = D / 16, NDB = D / 32, NMB = BK / 32;
-    __shared__ __attribute__((aligned(16))) f16 lds_k[BK * KP];
-    __shared__ __attribute__((aligned(16))) f16 lds_v[BK * KP];
-    __shared__ __attribute__((aligned(16))) f16 lds_kt[D * VP];
+    __shared__ __attribute__((aligned(16))) f16 lds_k[2][BK * D];   // double-buffered tiles
+    __shared__ __attribute__((aligned(16))) f16 lds_v[2][BK * D];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n32 = lane & 31, hb = lane >> 5;
@@ -359,49 +356,49 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
 
     const int kb_hi = ((q_end - 1) / BK) * BK;
     const int kb_lo = (kv_start / BK) * BK;
-    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= BK) {
+
+    // K_rot / V tiles stream into double-buffered swizzled LDS tiles with asynchronous
+    // global->LDS copies (rows past T clamped to T-1; their weight is masked to zero)
+    auto issue_tile = [&](int k0, int buf) {
+        tile_copy_async<D, BK>(lds_k[buf], 4, [&](int row) {
+            return a.krot + ((int64_t)min((int64_t)(k0 + row), T - 1) * a.hkv + kvh) * D;
+        });
+        tile_copy_async<D, BK>(lds_v[buf], 4, [&](int row) {
+            return a.v + ((int64_t)min((int64_t)(k0 + row), T - 1) * a.hkv + kvh) * D;
+        });
+    };
+
+    issue_tile(kb_hi, 0);
+    int buf = 0;
+    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= BK, buf ^= 1) {
+        lds_copy_wait();
         __syncthreads();
-        // K_rot tile -> lds_k (row-major) and lds_kt (transposed); V tile -> lds_v (row-major)
-        for (int e = tid; e < (BK / 2) * (D / 8); e += 256) {
-            const int kp = e % (BK / 2), ch = e / (BK / 2);
-            const int64_t j0 = k0 + 2 * kp;
-            const int64_t o0 = (j0 * a.hkv + kvh) * D + ch * 8, o1 = o0 + (int64_t)a.hkv * D;
-            const f16x8 x0 = j0 < T ? load_f16x8(a.krot + o0) : zero_f16x8();
-            const f16x8 x1 = j0 + 1 < T ? load_f16x8(a.krot + o1) : zero_f16x8();
-            const f16x8 v0 = j0 < T ? bf16x8_to_f16x8(load_bf16x8(a.v + o0)) : zero_f16x8();
-            const f16x8 v1 = j0 + 1 < T ? bf16x8_to_f16x8(load_bf16x8(a.v + o1)) : zero_f16x8();
-            store_f16x8(lds_k + (2 * kp) * KP + ch * 8, x0);
-            store_f16x8(lds_k + (2 * kp + 1) * KP + ch * 8, x1);
-            store_f16x8(lds_v + (2 * kp) * KP + ch * 8, v0);
-            store_f16x8(lds_v + (2 * kp + 1) * KP + ch * 8, v1);
-#pragma unroll
-            for (int x = 0; x < 8; ++x)
-                *reinterpret_cast<uint32_t *>(lds_kt + (ch * 8 + x) * VP + 2 * kp) = pack_f16x2(x0[x], x1[x]);
-        }
-        __syncthreads();
+        if (k0 - BK >= kb_lo) issue_tile(k0 - BK, buf ^ 1);
         if (!wave_active) continue;
         if (k0 > wq_last) continue;            // every key is after every query of the wave
         if (k0 + BK - 1 < wlo_min) continue;   // every key is before the wave's first sequence
         const bool need_mask = !(k0 + BK - 1 <= wq0 && k0 >= wlo_max);
+        const f16 *tk = lds_k[buf];
+        const f16 *tv = lds_v[buf];
 
         // S^T = K Q^T and dP^T = V dO^T (keys x queries), key rows in row_perm order
-        f32x16 s[NMB], dp[NMB];
+        f32x16 sc[NMB], dp[NMB];
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-            s[mb] = zero_f32x16();
+            sc[mb] = zero_f32x16();
             dp[mb] = zero_f32x16();
-            const int row = (32 * mb + row_perm(n32)) * KP + 8 * hb;
+            const int krow = 32 * mb + row_perm(n32);
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
-                s[mb] = mfma32(load_f16x8(lds_k + row + 16 * kk), qf[kk], s[mb]);
-                dp[mb] = mfma32(load_f16x8(lds_v + row + 16 * kk), gf[kk], dp[mb]);
+                sc[mb] = mfma32(tile_row8<D>(tk, krow, 16 * kk + 8 * hb), qf[kk], sc[mb]);
+                dp[mb] = mfma32(tile_row8<D>(tv, krow, 16 * kk + 8 * hb), gf[kk], dp[mb]);
             }
         }
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                float p = exp2f(s[mb][rr] * sl2 - lse2);
+                float p = exp2f(sc[mb][rr] * sl2 - lse2);
                 if (need_mask) {
                     const int jj = k0 + 32 * mb + row_perm(acc_row(rr, hb));
                     p = (qvalid && jj >= lo_i && jj <= i) ? p : 0.f;
@@ -409,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
                 dp[mb][rr] = p * (dp[mb][rr] - dd);
             }
         }
-        // dQ^T (d x queries) += K^T (d x keys) * dS^T (keys x queries)
+        // dQ^T (d x queries) += K^T (d x keys) * dS^T (keys x queries); K^T read transposed
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
@@ -417,9 +414,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
                 f16x8 sb;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) sb[x] = (f16)dp[mb][8 * e + x];
-                const f16 *krow = lds_kt + n32 * VP + 32 * mb + 16 * e + 8 * hb;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[db] = mfma32(load_f16x8(krow + 32 * db * VP), sb, acc[db]);
+                for (int db = 0; db < NDB; ++db)
+                    acc[db] = mfma32(tile_a_tr<D>(tk, 32 * mb + 16 * e, 32 * db), sb, acc[db]);
             }
         }
     }
@@ -460,7 +457,7 @@ hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
     BwdArgs a;
     a.qrot = (const f16 *)qrot;
     a.krot = (const f16 *)krot;
-    a.v = (const bf16 *)v;
+    a.v = (const f16 *)v;
     a.dout = (const bf16 *)dout;
     a.lse = lse;
     a.dsum = dsum;

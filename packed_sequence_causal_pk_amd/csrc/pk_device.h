@@ -43,6 +43,79 @@ __device__ __forceinline__ int row_perm(int m) {
 // Row of 32x32 result register r for a lane in half hb (before any permutation).
 __device__ __forceinline__ int acc_row(int r, int hb) { return 8 * (r >> 2) + 4 * hb + (r & 3); }
 
+// ---- Swizzled row-major fp16 LDS tiles ------------------------------------------------------
+// A tile holds rows of D halves with no padding; the 16-byte chunk c of row r is stored at chunk
+// position c ^ swz(r).  Two read patterns are conflict-free on the 64 LDS banks:
+//   * ds_read_b128 of one chunk by 16 lanes on 16 different rows (operand rows);
+//   * ds_read_b64_tr_b16 by 32 lanes on 4 consecutive rows x 64 bytes (transposed operands).
+// D = 128 (256-byte rows): swz(r) = 4*(r%4) + (r/4)%4.
+// D = 64 (128-byte rows, two per bank sweep): swz(r) = 4*((r/2)%2) + (r/4)%4.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Offset in halves of element (r, col) of a swizzled tile (col any multiple of 4).
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {
+    return r * D + 8 * ((col >> 3) ^ swz<D>(r)) + (col & 7);
+}
+
+// 8 halves (one 16-byte chunk, col multiple of 8) of row r.
+template <int D>
+__device__ __forceinline__ f16x8 tile_row8(const f16 *tile, int r, int col) {
+    return *reinterpret_cast<const f16x8 *>(tile + tile_off<D>(r, col));
+}
+
+template <int D>
+__device__ __forceinline__ void tile_store8(f16 *tile, int r, int col, f16x8 v) {
+    *reinterpret_cast<f16x8 *>(tile + tile_off<D>(r, col)) = v;
+}
+
+// A operand (32 rows m x 16 k) of mfma32 taken transposed from a swizzled tile X:
+// A[m][k] = X[k0 + k][m0 + m] (k0 multiple of 4, m0 multiple of 32).  Two ds_read_b64_tr_b16:
+// within each 16-lane group, source lane j addresses the 4 halves X[kb + j/4][mb + 4(j%4) ..],
+// and lane i receives element i%4 of the halves read by source lanes i/4 + 4t (t = 0..3),
+// i.e. the 4 consecutive k of its own column m.
+template <int D>
+__device__ __forceinline__ f16x8 tile_a_tr(const f16 *tile, int k0, int m0) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+    const int r = k0 + 8 * (g >> 1) + (j >> 2);
+    const int col = m0 + 16 * (g & 1) + 4 * (j & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + tile_off<D>(r, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + tile_off<D>(r + 4, col)));
+    return __builtin_bit_cast(f16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Asynchronous copy of one row-major [rows x D] fp16 tile from global memory into a swizzled LDS
+// tile with global_load_lds_dwordx4: each instruction moves 64 lanes x 16 bytes to a contiguous
+// 1 KB run of LDS (lane l at byte 16 l), so the swizzle is applied on the global side by choosing
+// which chunk each lane fetches.  `src(row)` returns the global address of element 0 of a tile
+// row; rows are clamped by the caller.  The copy is tracked by vmcnt; wait with
+// lds_copy_wait() before a barrier.  Waves split the tile's 1 KB runs: wave w issues runs
+// w, w + nwaves, ...
+template <int D, int ROWS, typename RowPtr>
+__device__ __forceinline__ void tile_copy_async(f16 *tile, int nwaves, RowPtr src) {
+    constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    constexpr int RUNS = ROWS * CPR / 64;      // 1 KB runs per tile
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int run = w; run < RUNS; run += nwaves) {
+        const int c = run * 64 + lane;         // physical chunk index in the tile
+        const int row = c / CPR;
+        const int logical = (c % CPR) ^ swz<D>(row);
+        const f16 *g = src(row) + 8 * logical;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                         (__attribute__((address_space(3))) void *)(tile + run * 512),
+                                         16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void lds_copy_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     bf16x8 z;
 #pragma unroll

@@ -17,8 +17,12 @@
 //     so each lane of a wave owns one query: the row max needs one cross-half exchange and the
 //     O^T accumulator is rescaled with a per-lane factor;
 //   * P^T stays in registers and is the k operand of O^T += V^T P^T; key rows of the first
-//     product are fed in row_perm order so the V^T operand is one 16-byte LDS read per lane;
-//   * K_rot and V tiles of 64 keys are staged in LDS (V transposed) and read by all 4 waves;
+//     product are fed in row_perm order so each lane's 8 keys of the V^T operand are
+//     consecutive, read with two transposing LDS loads (ds_read_b64_tr_b16);
+//   * K_rot and V tiles of 64 keys (both fp16, written by the prologue pass) stream into
+//     double-buffered swizzled row-major LDS tiles (no padding, no transposed copy) with
+//     asynchronous global->LDS copies, so the next tile loads while the current one is
+//     computed and no registers are spent on staging;
 //   * online softmax in the exp2 domain with scale * log2(e) folded into the scores;
 //   * Q is rotated in the prologue from the per-call (cos, sin) table; K comes pre-rotated;
 //   * operands are fp16 (the bf16 inputs convert exactly; rotated values, P keep 3 more bits
@@ -33,7 +37,7 @@ using namespace pkd;
 struct FwdArgs {
     const bf16 *q;        // [T, hq, D]
     const f16 *krot;      // [T, hkv, D] fp16
-    const bf16 *v;        // [T, hkv, D]
+    const f16 *v;         // [T, hkv, D] fp16 copy of v
     const float2 *rope;   // [T, D/2] (cos, sin)
     const int32_t *items; // [n_items, 8] longest first
     const int32_t *pos;   // [T]
@@ -59,13 +63,11 @@ __device__ void fwd_zero_tile(const FwdArgs &a, int tile, int h) {
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     constexpr int BK = 64;        // keys per LDS tile
-    constexpr int KP = D + 8;     // lds_k row pitch (bf16): rows start 4 banks apart
-    constexpr int VP = BK + 8;    // lds_vt row pitch
     constexpr int NKK = D / 16;   // k-steps of the score product
     constexpr int NDB = D / 32;   // 32-row blocks of O^T
     constexpr int NMB = BK / 32;  // 32-key blocks per tile
-    __shared__ __attribute__((aligned(16))) f16 lds_k[BK * KP];
-    __shared__ __attribute__((aligned(16))) f16 lds_vt[D * VP];
+    __shared__ __attribute__((aligned(16))) f16 lds_k[2][BK * D];   // double-buffered tiles
+    __shared__ __attribute__((aligned(16))) f16 lds_v[2][BK * D];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n32 = lane & 31, hb = lane >> 5;
@@ -121,26 +123,27 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
 
     const int kb_hi = ((q_end - 1) / BK) * BK;
     const int kb_lo = (kv_start / BK) * BK;
-    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= BK) {
+
+    // K_rot / V tiles stream into double-buffered swizzled LDS tiles with asynchronous
+    // global->LDS copies: tile t+1 is in flight while tile t is computed, one barrier per tile.
+    // Rows past T are clamped to row T-1 (finite data; the causal mask zeroes their weight).
+    auto issue_tile = [&](int k0, int buf) {
+        tile_copy_async<D, BK>(lds_k[buf], 4, [&](int row) {
+            return a.krot + ((int64_t)min((int64_t)(k0 + row), T - 1) * a.hkv + kvh) * D;
+        });
+        tile_copy_async<D, BK>(lds_v[buf], 4, [&](int row) {
+            return a.v + ((int64_t)min((int64_t)(k0 + row), T - 1) * a.hkv + kvh) * D;
+        });
+    };
+
+    issue_tile(kb_hi, 0);
+    int buf = 0;
+    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= BK, buf ^= 1) {
+        lds_copy_wait();
         __syncthreads();
-        // K_rot tile -> lds_k [BK][D] (rows past T are zero)
-        for (int e = tid; e < BK * (D / 8); e += 256) {
-            const int row = e / (D / 8), ch = e % (D / 8);
-            const int64_t j = k0 + row;
-            const f16x8 val = j < T ? load_f16x8(a.krot + (j * a.hkv + kvh) * D + ch * 8) : zero_f16x8();
-            store_f16x8(lds_k + row * KP + ch * 8, val);
-        }
-        // V tile -> lds_vt [D][BK] (transposed), two keys per 32-bit LDS store
-        for (int e = tid; e < (BK / 2) * (D / 8); e += 256) {
-            const int kp = e % (BK / 2), ch = e / (BK / 2);
-            const int64_t j0 = k0 + 2 * kp;
-            const f16x8 v0 = bf16x8_to_f16x8(j0 < T ? load_bf16x8(a.v + (j0 * a.hkv + kvh) * D + ch * 8) : zero_bf16x8());
-            const f16x8 v1 = bf16x8_to_f16x8(j0 + 1 < T ? load_bf16x8(a.v + ((j0 + 1) * a.hkv + kvh) * D + ch * 8) : zero_bf16x8());
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                *reinterpret_cast<uint32_t *>(lds_vt + (ch * 8 + s) * VP + 2 * kp) = pack_f16x2(v0[s], v1[s]);
-        }
-        __syncthreads();
+        if (k0 - BK >= kb_lo) issue_tile(k0 - BK, buf ^ 1);
+        const f16 *tk = lds_k[buf];
+        const f16 *tv = lds_v[buf];
         if (!wave_active) continue;
         if (k0 > wq_last) continue;            // every key is after every query of the wave
         if (k0 + BK - 1 < wlo_min) continue;   // every key is before the wave's first sequence
@@ -151,9 +154,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
             s[mb] = zero_f32x16();
-            const f16 *krow = lds_k + (32 * mb + row_perm(n32)) * KP + 8 * hb;
+            const int krow = 32 * mb + row_perm(n32);
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) s[mb] = mfma32(load_f16x8(krow + 16 * kk), qf[kk], s[mb]);
+            for (int kk = 0; kk < NKK; ++kk)
+                s[mb] = mfma32(tile_row8<D>(tk, krow, 16 * kk + 8 * hb), qf[kk], s[mb]);
         }
         float tmax = -INFINITY;
 #pragma unroll
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] *= alpha;
 
-        // O^T (d x queries) += V^T (d x keys) * P^T (keys x queries)
+        // O^T (d x queries) += V^T (d x keys) * P^T (keys x queries); V^T read transposed
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
@@ -196,9 +200,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
                 f16x8 pb;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) pb[x] = (f16)s[mb][8 * e + x];
-                const f16 *vrow = lds_vt + n32 * VP + 32 * mb + 16 * e + 8 * hb;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) o[db] = mfma32(load_f16x8(vrow + 32 * db * VP), pb, o[db]);
+                for (int db = 0; db < NDB; ++db)
+                    o[db] = mfma32(tile_a_tr<D>(tv, 32 * mb + 16 * e, 32 * db), pb, o[db]);
             }
         }
     }
@@ -232,7 +236,7 @@ hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, co
     FwdArgs a;
     a.q = (const bf16 *)q;
     a.krot = (const f16 *)krot;
-    a.v = (const bf16 *)v;
+    a.v = (const f16 *)v;
     a.rope = (const float2 *)rope;
     a.items = m.fwd_items;
     a.pos = m.pos;

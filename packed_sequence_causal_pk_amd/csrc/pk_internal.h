@@ -33,10 +33,10 @@ MetaLayout meta_layout(int32_t n_seqs, int64_t total_tokens);
 
 // Byte layout of the attention workspaces.
 struct FwdWorkspace {
-    size_t krot, rope, total;
+    size_t krot, vh, rope, total;
 };
 struct BwdWorkspace {
-    size_t qrot, krot, rope, dsum, blockmax, scale, total;
+    size_t qrot, krot, vh, rope, dsum, blockmax, scale, total;
 };
 FwdWorkspace fwd_workspace(int64_t T, int hq, int hkv, int d);
 BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d);
@@ -52,12 +52,13 @@ struct RopeArgs {
     int hq, hkv, d;
     float rope_base;
 };
-hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, void *krot, void *rope, hipStream_t s);
+hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, const void *v, void *krot, void *vh,
+                           void *rope, hipStream_t s);
 // Blocks of the per-token prologue/epilogue kernels (one thread per token and 4 rotation pairs).
 unsigned prep_blocks(int64_t T, int d);
-hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *out,
-                           const void *dout, void *qrot, void *krot, void *rope, float *dsum,
-                           float *blockmax, float *scale, hipStream_t s);
+hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *v,
+                           const void *out, const void *dout, void *qrot, void *krot, void *vh,
+                           void *rope, float *dsum, float *blockmax, float *scale, hipStream_t s);
 
 struct AttnShape {
     int64_t T;

@@ -11,7 +11,8 @@
 // [MV] "UnSloth极速微调：底层CUDA优化带来的变革", and read by the attention kernels instead of
 // evaluating sin/cos in their loops.
 //
-// Rotated q and k are written as fp16, the matrix-core operand format of the attention kernels.
+// Rotated q and k, and v, are written as fp16, the matrix-core operand format of the attention
+// kernels, so those can copy tiles straight into LDS.
 // The backward prologue also records max|dout| per block; k_bwd_scale turns it into a power of
 // two sigma with max|dout| * sigma in [1, 2), so the backward's fp16 gradient operands (dout and
 // dS, both scaled by sigma, unscaled exactly at the end) stay inside fp16's range whatever the
@@ -61,6 +62,16 @@ __device__ __forceinline__ void store4(f16 *p, const float x[4]) {
     *reinterpret_cast<uint2 *>(p) = raw;
 }
 
+// Copy 4 + 4 elements of one head row as fp16 (no rotation).
+template <int D>
+__device__ __forceinline__ void convert_row(const bf16 *__restrict__ src, f16 *__restrict__ dst, int c) {
+    float x1[4], x2[4];
+    load4(src + 4 * c, x1);
+    load4(src + D / 2 + 4 * c, x2);
+    store4(dst + 4 * c, x1);
+    store4(dst + D / 2 + 4 * c, x2);
+}
+
 // Rotate 4 pairs of one head row: row points at the head's element 0.
 template <int D>
 __device__ __forceinline__ void rotate_row(const bf16 *__restrict__ src, f16 *__restrict__ dst,
@@ -81,7 +92,9 @@ template <int D>
 __global__ __launch_bounds__(256) void k_fwd_prep(const int32_t *__restrict__ pos, int64_t T,
                                                   int hkv, float base,
                                                   const bf16 *__restrict__ k,
+                                                  const bf16 *__restrict__ v,
                                                   f16 *__restrict__ krot,
+                                                  f16 *__restrict__ vh,
                                                   float2 *__restrict__ table) {
     constexpr int G = D / 8;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -93,6 +106,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep(const int32_t *__restrict__ po
     for (int h = 0; h < hkv; ++h) {
         const int64_t off = (t * hkv + h) * D;
         rotate_row<D>(k + off, krot + off, c, cs, sn);
+        convert_row<D>(v + off, vh + off, c);
     }
 }
 
@@ -101,10 +115,12 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ po
                                                   int hq, int hkv, float base,
                                                   const bf16 *__restrict__ q,
                                                   const bf16 *__restrict__ k,
+                                                  const bf16 *__restrict__ v,
                                                   const bf16 *__restrict__ out,
                                                   const bf16 *__restrict__ dout,
                                                   f16 *__restrict__ qrot,
                                                   f16 *__restrict__ krot,
+                                                  f16 *__restrict__ vh,
                                                   float2 *__restrict__ table,
                                                   float *__restrict__ dsum,
                                                   float *__restrict__ blockmax) {
@@ -123,6 +139,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ po
         for (int h = 0; h < hkv; ++h) {
             const int64_t off = (t * hkv + h) * D;
             rotate_row<D>(k + off, krot + off, c, cs, sn);
+            convert_row<D>(v + off, vh + off, c);
         }
         for (int h = 0; h < hq; ++h) {
             const int64_t off = (t * hq + h) * D;
@@ -182,31 +199,31 @@ namespace pk {
 
 unsigned prep_blocks(int64_t T, int d) { return (unsigned)((T * (d / 8) + 255) / 256); }
 
-hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, void *krot, void *rope,
-                           hipStream_t s) {
+hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, const void *v, void *krot, void *vh,
+                           void *rope, hipStream_t s) {
     const unsigned g = prep_blocks(r.T, r.d);
     if (r.d == 128)
         k_fwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hkv, r.rope_base, (const bf16 *)k,
-                                           (f16 *)krot, (float2 *)rope);
+                                           (const bf16 *)v, (f16 *)krot, (f16 *)vh, (float2 *)rope);
     else
         k_fwd_prep<64><<<g, 256, 0, s>>>(r.pos, r.T, r.hkv, r.rope_base, (const bf16 *)k,
-                                          (f16 *)krot, (float2 *)rope);
+                                          (const bf16 *)v, (f16 *)krot, (f16 *)vh, (float2 *)rope);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *out,
-                           const void *dout, void *qrot, void *krot, void *rope, float *dsum,
-                           float *blockmax, float *scale, hipStream_t s) {
+hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *v,
+                           const void *out, const void *dout, void *qrot, void *krot, void *vh,
+                           void *rope, float *dsum, float *blockmax, float *scale, hipStream_t s) {
     const unsigned g = prep_blocks(r.T, r.d);
     if (r.d == 128)
         k_bwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
-                                           (const bf16 *)k, (const bf16 *)out,
-                                           (const bf16 *)dout, (f16 *)qrot, (f16 *)krot,
+                                           (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
+                                           (const bf16 *)dout, (f16 *)qrot, (f16 *)krot, (f16 *)vh,
                                            (float2 *)rope, dsum, blockmax);
     else
         k_bwd_prep<64><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
-                                          (const bf16 *)k, (const bf16 *)out,
-                                          (const bf16 *)dout, (f16 *)qrot, (f16 *)krot,
+                                          (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
+                                          (const bf16 *)dout, (f16 *)qrot, (f16 *)krot, (f16 *)vh,
                                           (float2 *)rope, dsum, blockmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
