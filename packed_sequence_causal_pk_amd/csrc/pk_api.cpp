@@ -82,9 +82,11 @@ BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d) {
     w.qrot = off; off += align256((size_t)T * hq * d * 2);
     w.krot = off; off += align256((size_t)T * hkv * d * 2);
     w.vh = off; off += align256((size_t)T * hkv * d * 2);
+    w.dout16 = off; off += align256((size_t)T * hq * d * 2);
     w.rope = off; off += align256((size_t)T * (d / 2) * 8);
     w.dsum = off; off += align256((size_t)T * hq * 4);
-    w.blockmax = off; off += align256((size_t)prep_blocks(T, d) * 4);
+    w.lse2 = off; off += align256((size_t)T * hq * 4);
+    w.blockmax = off; off += align256((size_t)dmax_blocks(T, hq, d) * 4);
     w.scale = off; off += align256(2 * 4);
     w.total = off;
     return w;
@@ -236,27 +238,28 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     char *w = static_cast<char *>(ws);
     float *dsum = reinterpret_cast<float *>(w + W.dsum);
+    float *lse2 = reinterpret_cast<float *>(w + W.lse2);
     float *blockmax = reinterpret_cast<float *>(w + W.blockmax);
     float *scale = reinterpret_cast<float *>(w + W.scale);
     pk::RopeArgs ra{meta->pos, T, hq, hkv, d, rope_base};
     hipError_t e;
     {
         ProfScope ps(PK_K_BWD_PREP, s);
-        e = pk::launch_bwd_prep(ra, q, k, v, out, dout, w + W.qrot, w + W.krot, w + W.vh,
-                                w + W.rope, dsum, blockmax, scale, s);
+        e = pk::launch_bwd_prep(ra, q, k, v, out, dout, lse, w + W.qrot, w + W.krot, w + W.vh,
+                                w + W.dout16, w + W.rope, dsum, lse2, blockmax, scale, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
     {
         ProfScope ps(PK_K_BWD, s);
-        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, dout, lse, dsum, scale,
-                           w + W.rope, dq, dk, dv, 0, s);
+        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
+                           scale, w + W.rope, dq, dk, dv, 0, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     {
         ProfScope ps(PK_K_BWD_DQ, s);
-        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, dout, lse, dsum, scale,
-                           w + W.rope, dq, dk, dv, 1, s);
+        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
+                           scale, w + W.rope, dq, dk, dv, 1, s);
     }
     return hip_status(e);
 }

@@ -14,7 +14,10 @@
 //                  32 keys each; K_rot and V of those keys are the k operands of S = Q K^T and
 //                  dP = dO V^T (v_mfma_f32_32x32x16_f16), dK^T and dV^T accumulate in registers
 //                  over every query block AND every query head of the GQA group (so the group
-//                  sum is free), and dK, dV are written once.
+//                  sum is free), and dK, dV are written once.  Query blocks of 64 rows stream
+//                  into double-buffered swizzled LDS tiles by asynchronous global->LDS copies;
+//                  the transposed operands of dV^T += dO^T P and dK^T += Q^T dS are read with
+//                  ds_read_b64_tr_b16 from the same row-major tiles.
 //   k_attn_bwd_q   one workgroup per forward work item (128 queries) x query head, laid out like
 //                  the forward: S^T = K Q^T and dP^T = V dO^T give each lane one query, so its
 //                  lse and D are per-lane scalars; dQ^T += K^T dS^T accumulates in registers and
@@ -39,9 +42,9 @@ struct BwdArgs {
     const f16 *qrot;      // [T, hq, D] fp16
     const f16 *krot;      // [T, hkv, D] fp16
     const f16 *v;         // [T, hkv, D] fp16 copy of v
-    const bf16 *dout;     // [T, hq, D]
-    const float *lse;     // [hq, T]
-    const float *dsum;    // [hq, T]
+    const f16 *dout16;    // [T, hq, D] sigma * dout, fp16
+    const float *lse2;    // [hq, T] lse * log2(e)
+    const float *dsum;    // [hq, T] sigma * rowsum(dout * out)
     const float *dscale;  // {sigma, 1/sigma}
     const float2 *rope;   // [T, D/2]
     const int32_t *items; // [n_items, 8] longest first (backward list for _kv, forward for _q)
@@ -61,15 +64,11 @@ struct BwdArgs {
 template <int D>
 struct KvSmem {
     static constexpr int BQ = 64;        // query rows per block
-    static constexpr int QP = D + 8;     // row-major Q / dO pitch
-    static constexpr int TP = BQ + 8;    // transposed Q / dO pitch
-    f16 q[BQ * QP];
-    f16 dO[BQ * QP];
-    f16 qt[D * TP];
-    f16 dOt[D * TP];
-    float lse[BQ];   // lse * log2(e); +inf for rows past the item
-    float dd[BQ];    // D_i * sigma
-    int lo[BQ];      // first key of the row's sequence; INT_MAX past the item
+    f16 q[2][BQ * D];    // swizzled row-major Q_rot blocks (double-buffered)
+    f16 dO[2][BQ * D];   // swizzled row-major sigma * dout blocks
+    float lse2[2][BQ];   // lse * log2(e) of the block's rows
+    float dd[2][BQ];     // sigma * D_i
+    int pos[2][BQ];      // position of each row inside its sequence
 };
 
 template <int D>
@@ -86,69 +85,27 @@ __device__ void kv_zero_tile(const BwdArgs &a, int tile, int kvh) {
     }
 }
 
-// Per-thread share of one staged query block, loaded from global memory one iteration ahead so
-// the loads overlap the current block's products.
+// Start the asynchronous copy of one query block (rows [qb, qb + BQ) of head h, clamped to
+// T - 1) into buffer `buf`: Q_rot and sigma * dout tiles, and the per-row lse2, dd and pos.
 template <int D>
-struct KvPrefetch {
-    static constexpr int N = (KvSmem<D>::BQ / 2) * (D / 8) / 256;  // row pairs x 8 columns
-    uint4 q[2 * N];   // Q_rot, fp16 bits
-    uint4 g[2 * N];   // dout, bf16 bits
-    float lse, dd;
-    int lo;
-};
-
-template <int D>
-__device__ __forceinline__ void kv_prefetch(const BwdArgs &a, int h, int qb, int q_end,
-                                            KvPrefetch<D> &pf) {
+__device__ __forceinline__ void kv_issue_block(const BwdArgs &a, KvSmem<D> &sm, int buf, int h,
+                                               int qb) {
     using S = KvSmem<D>;
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int u = 0; u < KvPrefetch<D>::N; ++u) {
-        const int e = threadIdx.x + 256 * u;
-        const int rp = e % (S::BQ / 2), ch = e / (S::BQ / 2);
-        const int i0 = qb + 2 * rp;
-        const int64_t o0 = ((int64_t)i0 * a.hq + h) * D + ch * 8;
-        const int64_t o1 = o0 + (int64_t)a.hq * D;
-        pf.q[2 * u] = i0 < q_end ? *reinterpret_cast<const uint4 *>(a.qrot + o0) : z;
-        pf.q[2 * u + 1] = i0 + 1 < q_end ? *reinterpret_cast<const uint4 *>(a.qrot + o1) : z;
-        pf.g[2 * u] = i0 < q_end ? *reinterpret_cast<const uint4 *>(a.dout + o0) : z;
-        pf.g[2 * u + 1] = i0 + 1 < q_end ? *reinterpret_cast<const uint4 *>(a.dout + o1) : z;
-    }
-    if (threadIdx.x < S::BQ) {
-        const int i = qb + threadIdx.x;
-        const bool ok = i < q_end;
-        pf.lse = ok ? a.lse[(int64_t)h * a.T + i] : INFINITY;
-        pf.dd = ok ? a.dsum[(int64_t)h * a.T + i] : 0.f;
-        pf.lo = ok ? i - a.pos[i] : INT_MAX;
-    }
-}
-
-// Write a prefetched block into LDS: Q_rot and sigma * dout as fp16, row-major and transposed.
-template <int D>
-__device__ __forceinline__ void kv_stage(const KvPrefetch<D> &pf, float sigma, KvSmem<D> &sm) {
-    using S = KvSmem<D>;
-#pragma unroll
-    for (int u = 0; u < KvPrefetch<D>::N; ++u) {
-        const int e = threadIdx.x + 256 * u;
-        const int rp = e % (S::BQ / 2), ch = e / (S::BQ / 2);
-        const f16x8 q0 = __builtin_bit_cast(f16x8, pf.q[2 * u]);
-        const f16x8 q1 = __builtin_bit_cast(f16x8, pf.q[2 * u + 1]);
-        const f16x8 g0 = bf16x8_to_f16x8(__builtin_bit_cast(bf16x8, pf.g[2 * u]), sigma);
-        const f16x8 g1 = bf16x8_to_f16x8(__builtin_bit_cast(bf16x8, pf.g[2 * u + 1]), sigma);
-        store_f16x8(sm.q + (2 * rp) * S::QP + ch * 8, q0);
-        store_f16x8(sm.q + (2 * rp + 1) * S::QP + ch * 8, q1);
-        store_f16x8(sm.dO + (2 * rp) * S::QP + ch * 8, g0);
-        store_f16x8(sm.dO + (2 * rp + 1) * S::QP + ch * 8, g1);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            *reinterpret_cast<uint32_t *>(sm.qt + (ch * 8 + x) * S::TP + 2 * rp) = pack_f16x2(q0[x], q1[x]);
-            *reinterpret_cast<uint32_t *>(sm.dOt + (ch * 8 + x) * S::TP + 2 * rp) = pack_f16x2(g0[x], g1[x]);
-        }
-    }
-    if (threadIdx.x < S::BQ) {
-        sm.lse[threadIdx.x] = pf.lse * kLog2e;
-        sm.dd[threadIdx.x] = pf.dd * sigma;
-        sm.lo[threadIdx.x] = pf.lo;
+    const int64_t last = a.T - 1;
+    tile_copy_async<D, S::BQ>(sm.q[buf], 4, [&](int row) {
+        return a.qrot + ((int64_t)min((int64_t)(qb + row), last) * a.hq + h) * D;
+    });
+    tile_copy_async<D, S::BQ>(sm.dO[buf], 4, [&](int row) {
+        return a.dout16 + ((int64_t)min((int64_t)(qb + row), last) * a.hq + h) * D;
+    });
+    if (threadIdx.x < 64) {  // one wave: 64 rows x 4 bytes per array
+        const int64_t i = min((int64_t)(qb + threadIdx.x), last);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a.lse2 + (int64_t)h * a.T + i),
+                                         (__attribute__((address_space(3))) void *)sm.lse2[buf], 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a.dsum + (int64_t)h * a.T + i),
+                                         (__attribute__((address_space(3))) void *)sm.dd[buf], 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a.pos + i),
+                                         (__attribute__((address_space(3))) void *)sm.pos[buf], 4, 0, 0);
     }
 }
 
@@ -168,7 +125,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
         return;
     }
     const int kv_start = it[0], kv_end = it[1], q_start = it[2], q_end = it[3];
-    const float sigma = a.dscale[0], inv_sigma = a.dscale[1];
+    const float inv_sigma = a.dscale[1];
 
     const int j = kv_start + 32 * w + n32;  // this lane's key
     const bool kvalid = j < kv_end;
@@ -178,8 +135,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
 
     const int nqb = (q_end - q_start + BQ - 1) / BQ;
     const int n_iter = a.group * nqb;
-    KvPrefetch<D> pf;
-    kv_prefetch<D>(a, kvh * a.group, q_start, q_end, pf);
+    kv_issue_block<D>(a, sm, 0, kvh * a.group, q_start);
 
     // K_rot and V of this lane's key, as k operands (d in [16kk + 8hb, +8))
     f16x8 kf[NKK], vf[NKK];
@@ -200,45 +156,54 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
     }
     const float sl2 = a.scale * kLog2e;
 
-    for (int itn = 0; itn < n_iter; ++itn) {
+    int buf = 0;
+    for (int itn = 0; itn < n_iter; ++itn, buf ^= 1) {
         const int hh = itn / nqb;
         const int qb = q_start + (itn - hh * nqb) * BQ;
-        __syncthreads();
-        kv_stage<D>(pf, sigma, sm);
+        lds_copy_wait();
         __syncthreads();
         if (itn + 1 < n_iter) {
             const int hn = (itn + 1) / nqb;
-            kv_prefetch<D>(a, kvh * a.group + hn, q_start + (itn + 1 - hn * nqb) * BQ, q_end, pf);
+            kv_issue_block<D>(a, sm, buf ^ 1, kvh * a.group + hn, q_start + (itn + 1 - hn * nqb) * BQ);
         }
         if (!wave_active) continue;
         const int nrows = min(BQ, q_end - qb);
+        const f16 *tq = sm.q[buf];
+        const f16 *tg = sm.dO[buf];
+        const float *plse = sm.lse2[buf];
+        const float *pdd = sm.dd[buf];
+        const int *ppos = sm.pos[buf];
 #pragma unroll
         for (int qm = 0; qm < 2; ++qm) {
             // rows [qb + 32qm, +32) of the block against this wave's 32 keys
             const int r0 = 32 * qm;
             const int hrows = min(32, nrows - r0);
-            if (hrows <= 0 || qb + r0 + hrows - 1 < wk0 || sm.lo[r0] > wk_last) continue;
-            const bool need_mask = !(qb + r0 >= wk0 + 31 && sm.lo[r0 + hrows - 1] <= wk0);
+            if (hrows <= 0) continue;
+            if (qb + r0 + hrows - 1 < wk0 || qb + r0 - ppos[r0] > wk_last) continue;
+            const int rl = r0 + hrows - 1;
+            const bool need_mask = !(hrows == 32 && qb + r0 >= wk0 + 31 && qb + rl - ppos[rl] <= wk0);
             f32x16 sp = zero_f32x16(), dp = zero_f32x16();
             {
                 const int row = r0 + row_perm(n32);
-                const f16 *qrow = sm.q + row * S::QP + 8 * hb;
-                const f16 *grow = sm.dO + row * S::QP + 8 * hb;
 #pragma unroll
                 for (int kk = 0; kk < NKK; ++kk) {
-                    sp = mfma32(load_f16x8(qrow + 16 * kk), kf[kk], sp);
-                    dp = mfma32(load_f16x8(grow + 16 * kk), vf[kk], dp);
+                    sp = mfma32(tile_row8<D>(tq, row, 16 * kk + 8 * hb), kf[kk], sp);
+                    dp = mfma32(tile_row8<D>(tg, row, 16 * kk + 8 * hb), vf[kk], dp);
                 }
             }
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const int row = r0 + row_perm(acc_row(rr, hb));
-                float p = exp2f(sp[rr] * sl2 - sm.lse[row]);
-                if (need_mask) p = (j >= sm.lo[row] && j <= qb + row) ? p : 0.f;
+                float p = exp2f(sp[rr] * sl2 - plse[row]);
+                if (need_mask) {
+                    const int i = qb + row;
+                    p = (row < nrows && j >= i - ppos[row] && j <= i) ? p : 0.f;
+                }
                 sp[rr] = p;
-                dp[rr] = p * (dp[rr] - sm.dd[row]);
+                dp[rr] = p * (dp[rr] - pdd[row]);
             }
-            // dV^T += dO^T P,  dK^T += Q^T dS  (queries are the k dimension)
+            // dV^T += dO^T P,  dK^T += Q^T dS  (queries are the k dimension; the transposed
+            // operands are read straight from the row-major blocks)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 f16x8 pb, sb;
@@ -247,12 +212,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
                     pb[x] = (f16)sp[8 * e + x];
                     sb[x] = (f16)dp[8 * e + x];
                 }
-                const int col = r0 + 16 * e + 8 * hb;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const int drow = 32 * db + n32;
-                    dva[db] = mfma32(load_f16x8(sm.dOt + drow * S::TP + col), pb, dva[db]);
-                    dka[db] = mfma32(load_f16x8(sm.qt + drow * S::TP + col), sb, dka[db]);
+                    dva[db] = mfma32(tile_a_tr<D>(tg, r0 + 16 * e, 32 * db), pb, dva[db]);
+                    dka[db] = mfma32(tile_a_tr<D>(tq, r0 + 16 * e, 32 * db), sb, dka[db]);
                 }
             }
         }
@@ -324,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     }
     const int q_start = it[0], q_end = it[1], kv_start = it[2];
     const int64_t T = a.T;
-    const float sigma = a.dscale[0], inv_sigma = a.dscale[1];
+    const float inv_sigma = a.dscale[1];
 
     // this lane's query and its wave's query range
     const int i = q_start + 32 * w + n32;
@@ -336,8 +299,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     const int wq_last = min(wq0 + 31, q_end - 1);
     const int wlo_min = wave_active ? wq0 - a.pos[wq0] : 0;
     const int wlo_max = wave_active ? wq_last - a.pos[wq_last] : 0;
-    const float lse2 = qvalid ? a.lse[(int64_t)h * T + i] * kLog2e : INFINITY;
-    const float dd = qvalid ? a.dsum[(int64_t)h * T + i] * sigma : 0.f;
+    const float lse2 = qvalid ? a.lse2[(int64_t)h * T + i] : INFINITY;
+    const float dd = qvalid ? a.dsum[(int64_t)h * T + i] : 0.f;
 
     // Q_rot and sigma * dout of this lane's query as k operands (d in [16kk + 8hb, +8))
     f16x8 qf[NKK], gf[NKK];
@@ -346,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             qf[kk] = qvalid ? load_f16x8(a.qrot + row + 16 * kk) : zero_f16x8();
-            gf[kk] = qvalid ? bf16x8_to_f16x8(load_bf16x8(a.dout + row + 16 * kk), sigma) : zero_f16x8();
+            gf[kk] = qvalid ? load_f16x8(a.dout16 + row + 16 * kk) : zero_f16x8();
         }
     }
     f32x16 acc[NDB];
@@ -451,15 +414,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
 namespace pk {
 
 hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
-                      const void *krot, const void *v, const void *dout, const float *lse,
+                      const void *krot, const void *v, const void *dout16, const float *lse2,
                       const float *dsum, const float *scale, const void *rope, float *dq,
                       float *dk, float *dv, int which, hipStream_t s) {
     BwdArgs a;
     a.qrot = (const f16 *)qrot;
     a.krot = (const f16 *)krot;
     a.v = (const f16 *)v;
-    a.dout = (const bf16 *)dout;
-    a.lse = lse;
+    a.dout16 = (const f16 *)dout16;
+    a.lse2 = lse2;
     a.dsum = dsum;
     a.dscale = scale;
     a.rope = (const float2 *)rope;

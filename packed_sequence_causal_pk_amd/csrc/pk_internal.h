@@ -36,7 +36,7 @@ struct FwdWorkspace {
     size_t krot, vh, rope, total;
 };
 struct BwdWorkspace {
-    size_t qrot, krot, vh, rope, dsum, blockmax, scale, total;
+    size_t qrot, krot, vh, dout16, rope, dsum, lse2, blockmax, scale, total;
 };
 FwdWorkspace fwd_workspace(int64_t T, int hq, int hkv, int d);
 BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d);
@@ -56,9 +56,12 @@ hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, const void *v, void
                            void *rope, hipStream_t s);
 // Blocks of the per-token prologue/epilogue kernels (one thread per token and 4 rotation pairs).
 unsigned prep_blocks(int64_t T, int d);
+// Blocks of the max|dout| reduction (at most 1024).
+unsigned dmax_blocks(int64_t T, int hq, int d);
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *v,
-                           const void *out, const void *dout, void *qrot, void *krot, void *vh,
-                           void *rope, float *dsum, float *blockmax, float *scale, hipStream_t s);
+                           const void *out, const void *dout, const float *lse, void *qrot,
+                           void *krot, void *vh, void *dout16, void *rope, float *dsum,
+                           float *lse2, float *blockmax, float *scale, hipStream_t s);
 
 struct AttnShape {
     int64_t T;
@@ -67,8 +70,9 @@ struct AttnShape {
 };
 hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, const void *krot,
                       const void *v, const void *rope, void *out, float *lse, hipStream_t s);
+// dout16 = sigma * dout (fp16), dsum = sigma * rowsum(dout * out), lse2 = lse * log2(e).
 hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
-                      const void *krot, const void *v, const void *dout, const float *lse,
+                      const void *krot, const void *v, const void *dout16, const float *lse2,
                       const float *dsum, const float *scale, const void *rope, float *dq,
                       float *dk, float *dv, int which /* 0: dK, dV; 1: dQ */, hipStream_t s);
 

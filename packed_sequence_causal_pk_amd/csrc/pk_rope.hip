@@ -11,16 +11,19 @@
 // [MV] "UnSloth极速微调：底层CUDA优化带来的变革", and read by the attention kernels instead of
 // evaluating sin/cos in their loops.
 //
-// Rotated q and k, and v, are written as fp16, the matrix-core operand format of the attention
-// kernels, so those can copy tiles straight into LDS.
-// The backward prologue also records max|dout| per block; k_bwd_scale turns it into a power of
-// two sigma with max|dout| * sigma in [1, 2), so the backward's fp16 gradient operands (dout and
-// dS, both scaled by sigma, unscaled exactly at the end) stay inside fp16's range whatever the
-// magnitude of the incoming gradient.
+// Rotated q and k, v, and the scaled dout are written as fp16, the matrix-core operand format of
+// the attention kernels, so those can copy tiles straight into LDS.  The backward prologue first
+// reduces max|dout| (k_bwd_dmax); k_bwd_scale turns it into a power of two sigma with
+// max|dout| * sigma in [1, 2), so the backward's fp16 gradient operands (dout and dS, both scaled
+// by sigma, unscaled exactly at the end) stay inside fp16's range whatever the magnitude of the
+// incoming gradient.  k_bwd_prep then writes sigma * dout, sigma * rowsum(dout * out) and
+// lse * log2(e) next to the rotated tensors.
 //
 // Thread layout of the two per-token kernels: one thread per (token t, group c of 4 rotation pairs);
 // the thread owns elements d in [4c, 4c+4) and their partners d + D/2 for every head, so each
 // rotation stays inside one thread and a token's D/8 threads read each half-row contiguously.
+#include <algorithm>
+
 #include "pk_internal.h"
 #include "pk_device.h"
 
@@ -110,6 +113,31 @@ __global__ __launch_bounds__(256) void k_fwd_prep(const int32_t *__restrict__ po
     }
 }
 
+// max|dout| per block over the flattened [T * hq * d] tensor, 8 elements per thread step.
+__global__ __launch_bounds__(256) void k_bwd_dmax(const bf16 *__restrict__ dout, int64_t n8,
+                                                  float *__restrict__ blockmax) {
+    __shared__ float s_max[4];
+    float amax = 0.f;
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n8; c += (int64_t)gridDim.x * 256) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(dout + 8 * c);
+        const bf16 *b = reinterpret_cast<const bf16 *>(&raw);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf((float)b[k]));
+    }
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        blockmax[blockIdx.x] = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+}
+
+// Store 4 floats as fp16 after scaling.
+__device__ __forceinline__ void store4s(f16 *p, const float x[4], float scale) {
+    const float y[4] = {x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale};
+    store4(p, y);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ pos, int64_t T,
                                                   int hq, int hkv, float base,
@@ -118,54 +146,50 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ po
                                                   const bf16 *__restrict__ v,
                                                   const bf16 *__restrict__ out,
                                                   const bf16 *__restrict__ dout,
+                                                  const float *__restrict__ lse,
+                                                  const float *__restrict__ dscale,
                                                   f16 *__restrict__ qrot,
                                                   f16 *__restrict__ krot,
                                                   f16 *__restrict__ vh,
+                                                  f16 *__restrict__ dout16,
                                                   float2 *__restrict__ table,
                                                   float *__restrict__ dsum,
-                                                  float *__restrict__ blockmax) {
+                                                  float *__restrict__ lse2) {
     constexpr int G = D / 8;
-    __shared__ float s_max[4];
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t t = gid / G;
     const int c = (int)(gid % G);
-    // The G threads of a token share a wave and agree on `active`, so the shuffle reduction
-    // below only mixes lanes of one token.
-    const bool active = t < T;
-    float amax = 0.f;
-    if (active) {
-        float cs[4], sn[4];
-        rope_factors<D>(pos, t, c, base, table, cs, sn);
-        for (int h = 0; h < hkv; ++h) {
-            const int64_t off = (t * hkv + h) * D;
-            rotate_row<D>(k + off, krot + off, c, cs, sn);
-            convert_row<D>(v + off, vh + off, c);
-        }
-        for (int h = 0; h < hq; ++h) {
-            const int64_t off = (t * hq + h) * D;
-            rotate_row<D>(q + off, qrot + off, c, cs, sn);
-            float o1[4], o2[4], g1[4], g2[4];
-            load4(out + off + 4 * c, o1);
-            load4(out + off + D / 2 + 4 * c, o2);
-            load4(dout + off + 4 * c, g1);
-            load4(dout + off + D / 2 + 4 * c, g2);
-            float part = 0.f;
+    // The G threads of a token share a wave and all exit here together, so the shuffle
+    // reduction below only mixes lanes of one token.
+    if (t >= T) return;
+    const float sigma = dscale[0];
+    float cs[4], sn[4];
+    rope_factors<D>(pos, t, c, base, table, cs, sn);
+    for (int h = 0; h < hkv; ++h) {
+        const int64_t off = (t * hkv + h) * D;
+        rotate_row<D>(k + off, krot + off, c, cs, sn);
+        convert_row<D>(v + off, vh + off, c);
+    }
+    for (int h = 0; h < hq; ++h) {
+        const int64_t off = (t * hq + h) * D;
+        rotate_row<D>(q + off, qrot + off, c, cs, sn);
+        float o1[4], o2[4], g1[4], g2[4];
+        load4(out + off + 4 * c, o1);
+        load4(out + off + D / 2 + 4 * c, o2);
+        load4(dout + off + 4 * c, g1);
+        load4(dout + off + D / 2 + 4 * c, g2);
+        store4s(dout16 + off + 4 * c, g1, sigma);
+        store4s(dout16 + off + D / 2 + 4 * c, g2, sigma);
+        float part = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                part += o1[kk] * g1[kk] + o2[kk] * g2[kk];
-                amax = fmaxf(amax, fmaxf(fabsf(g1[kk]), fabsf(g2[kk])));
-            }
+        for (int kk = 0; kk < 4; ++kk) part += o1[kk] * g1[kk] + o2[kk] * g2[kk];
 #pragma unroll
-            for (int s = G / 2; s > 0; s >>= 1) part += __shfl_xor(part, s, 64);
-            if (c == 0) dsum[(int64_t)h * T + t] = part;
+        for (int s = G / 2; s > 0; s >>= 1) part += __shfl_xor(part, s, 64);
+        if (c == 0) {
+            dsum[(int64_t)h * T + t] = part * sigma;
+            lse2[(int64_t)h * T + t] = lse[(int64_t)h * T + t] * pkd::kLog2e;
         }
     }
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
-    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        blockmax[blockIdx.x] = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
 }
 
 // One workgroup: sigma = 2^e with max|dout| * sigma in [1, 2) (sigma = 1 when the maximum is 0
@@ -199,6 +223,11 @@ namespace pk {
 
 unsigned prep_blocks(int64_t T, int d) { return (unsigned)((T * (d / 8) + 255) / 256); }
 
+unsigned dmax_blocks(int64_t T, int hq, int d) {
+    const int64_t n8 = T * hq * d / 8;
+    return (unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, (n8 + 255) / 256));
+}
+
 hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, const void *v, void *krot, void *vh,
                            void *rope, hipStream_t s) {
     const unsigned g = prep_blocks(r.T, r.d);
@@ -212,22 +241,27 @@ hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, const void *v, void
 }
 
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *v,
-                           const void *out, const void *dout, void *qrot, void *krot, void *vh,
-                           void *rope, float *dsum, float *blockmax, float *scale, hipStream_t s) {
+                           const void *out, const void *dout, const float *lse, void *qrot,
+                           void *krot, void *vh, void *dout16, void *rope, float *dsum,
+                           float *lse2, float *blockmax, float *scale, hipStream_t s) {
+    const int64_t n8 = r.T * r.hq * r.d / 8;
+    const unsigned nb = dmax_blocks(r.T, r.hq, r.d);
+    k_bwd_dmax<<<nb, 256, 0, s>>>((const bf16 *)dout, n8, blockmax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_bwd_scale<<<1, 256, 0, s>>>(blockmax, (int)nb, scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned g = prep_blocks(r.T, r.d);
     if (r.d == 128)
         k_bwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
                                            (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
-                                           (const bf16 *)dout, (f16 *)qrot, (f16 *)krot, (f16 *)vh,
-                                           (float2 *)rope, dsum, blockmax);
+                                           (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
+                                           (f16 *)vh, (f16 *)dout16, (float2 *)rope, dsum, lse2);
     else
         k_bwd_prep<64><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
                                           (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
-                                          (const bf16 *)dout, (f16 *)qrot, (f16 *)krot, (f16 *)vh,
-                                          (float2 *)rope, dsum, blockmax);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    k_bwd_scale<<<1, 256, 0, s>>>(blockmax, (int)g, scale);
+                                          (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
+                                          (f16 *)vh, (f16 *)dout16, (float2 *)rope, dsum, lse2);
     return hipGetLastError();
 }
 
