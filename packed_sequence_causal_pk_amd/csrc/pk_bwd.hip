@@ -116,7 +116,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
     constexpr int NKK = D / 16, NDB = D / 32;
     __shared__ __attribute__((aligned(16))) S sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets bounds live in SGPRs
     const int n32 = lane & 31, hb = lane >> 5;
     const int r = blockIdx.x / a.hkv, kvh = blockIdx.x % a.hkv;
     const int32_t *it = a.items + (int64_t)r * PK_ITEM_FIELDS;
@@ -179,9 +180,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
             const int r0 = 32 * qm;
             const int hrows = min(32, nrows - r0);
             if (hrows <= 0) continue;
-            if (qb + r0 + hrows - 1 < wk0 || qb + r0 - ppos[r0] > wk_last) continue;
             const int rl = r0 + hrows - 1;
-            const bool need_mask = !(hrows == 32 && qb + r0 >= wk0 + 31 && qb + rl - ppos[rl] <= wk0);
+            const int lo_first = __builtin_amdgcn_readfirstlane(qb + r0 - ppos[r0]);
+            const int lo_last = __builtin_amdgcn_readfirstlane(qb + rl - ppos[rl]);
+            if (qb + r0 + hrows - 1 < wk0 || lo_first > wk_last) continue;
+            const bool need_mask = !(hrows == 32 && qb + r0 >= wk0 + 31 && lo_last <= wk0);
             f32x16 sp = zero_f32x16(), dp = zero_f32x16();
             {
                 const int row = r0 + row_perm(n32);
@@ -191,14 +194,19 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
                     dp = mfma32(tile_row8<D>(tg, row, 16 * kk + 8 * hb), vf[kk], dp);
                 }
             }
+            if (need_mask) {  // uniform branch: boundary / diagonal blocks only
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int row = r0 + row_perm(acc_row(rr, hb));
+                    const int i = qb + row;
+                    const bool keep = (row < nrows) & (j >= i - ppos[row]) & (j <= i);  // no short circuit
+                    sp[rr] = keep ? sp[rr] : -INFINITY;
+                }
+            }
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const int row = r0 + row_perm(acc_row(rr, hb));
-                float p = exp2f(sp[rr] * sl2 - plse[row]);
-                if (need_mask) {
-                    const int i = qb + row;
-                    p = (row < nrows && j >= i - ppos[row] && j <= i) ? p : 0.f;
-                }
+                const float p = exp2f(fmaf(sp[rr], sl2, -plse[row]));
                 sp[rr] = p;
                 dp[rr] = p * (dp[rr] - pdd[row]);
             }
@@ -276,7 +284,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) f16 lds_k[2][BK * D];   // double-buffered tiles
     __shared__ __attribute__((aligned(16))) f16 lds_v[2][BK * D];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets bounds live in SGPRs
     const int n32 = lane & 31, hb = lane >> 5;
     const int r = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
     const int kvh = h / a.group;
@@ -297,8 +306,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     const int wq0 = q_start + 32 * w;
     const bool wave_active = wq0 < q_end;
     const int wq_last = min(wq0 + 31, q_end - 1);
-    const int wlo_min = wave_active ? wq0 - a.pos[wq0] : 0;
-    const int wlo_max = wave_active ? wq_last - a.pos[wq_last] : 0;
+    const int wlo_min = __builtin_amdgcn_readfirstlane(wave_active ? wq0 - a.pos[wq0] : 0);
+    const int wlo_max = __builtin_amdgcn_readfirstlane(wave_active ? wq_last - a.pos[wq_last] : 0);
     const float lse2 = qvalid ? a.lse2[(int64_t)h * T + i] : INFINITY;
     const float dd = qvalid ? a.dsum[(int64_t)h * T + i] : 0.f;
 
@@ -357,15 +366,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
                 dp[mb] = mfma32(tile_row8<D>(tv, krow, 16 * kk + 8 * hb), gf[kk], dp[mb]);
             }
         }
+        if (need_mask) {  // uniform branch: boundary / diagonal tiles only
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int jj = k0 + 32 * mb + row_perm(acc_row(rr, hb));
+                    const bool keep = qvalid & (jj >= lo_i) & (jj <= i);
+                    sc[mb][rr] = keep ? sc[mb][rr] : -INFINITY;
+                }
+        }
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                float p = exp2f(sc[mb][rr] * sl2 - lse2);
-                if (need_mask) {
-                    const int jj = k0 + 32 * mb + row_perm(acc_row(rr, hb));
-                    p = (qvalid && jj >= lo_i && jj <= i) ? p : 0.f;
-                }
+                const float p = exp2f(fmaf(sc[mb][rr], sl2, -lse2));
                 dp[mb][rr] = p * (dp[mb][rr] - dd);
             }
         }

@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) f16 lds_k[2][BK * D];   // double-buffered tiles
     __shared__ __attribute__((aligned(16))) f16 lds_v[2][BK * D];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets bounds live in SGPRs
     const int n32 = lane & 31, hb = lane >> 5;
     const int r = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
     const int kvh = h / a.group;
@@ -88,8 +89,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     const int wq0 = q_start + 32 * w;
     const bool wave_active = wq0 < q_end;
     const int wq_last = min(wq0 + 31, q_end - 1);
-    const int wlo_min = wave_active ? wq0 - a.pos[wq0] : 0;
-    const int wlo_max = wave_active ? wq_last - a.pos[wq_last] : 0;
+    const int wlo_min = __builtin_amdgcn_readfirstlane(wave_active ? wq0 - a.pos[wq0] : 0);
+    const int wlo_max = __builtin_amdgcn_readfirstlane(wave_active ? wq_last - a.pos[wq_last] : 0);
 
     // Q fragments (k operand of S^T = K Q^T), rotated in registers.  Chunk kk holds
     // d in [16kk + 8hb, +8); chunk kk + NKK/2 holds the RoPE partners d + D/2.
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
         }
     }
 
-    float m = -INFINITY;  // running max of this query's scores (log2 domain)
+    float m = -INFINITY;  // running max of this query's raw scores q.k
     float l = 0.f;        // running sum of exp2(s - m) over this lane's half of the keys
     f32x16 o[NDB];
 #pragma unroll
@@ -159,31 +160,35 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
             for (int kk = 0; kk < NKK; ++kk)
                 s[mb] = mfma32(tile_row8<D>(tk, krow, 16 * kk + 8 * hb), qf[kk], s[mb]);
         }
+        // Online softmax in the exp2 domain.  The running max is kept on the raw scores; the
+        // scale * log2(e) factor is folded into one FMA per score: p = exp2(s*c - m*c).
+        // Masking runs only on tiles that straddle a boundary or the diagonal (a uniform branch).
+        if (need_mask) {
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int j = k0 + 32 * mb + row_perm(acc_row(rr, hb));
+                    const bool keep = qvalid & (j >= lo_i) & (j <= i);
+                    s[mb][rr] = keep ? s[mb][rr] : -INFINITY;
+                }
+        }
         float tmax = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
+        for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                float x = s[mb][rr] * a.scale_log2;
-                if (need_mask) {
-                    const int j = k0 + 32 * mb + row_perm(acc_row(rr, hb));
-                    x = (qvalid && j >= lo_i && j <= i) ? x : -INFINITY;
-                }
-                s[mb][rr] = x;
-                tmax = fmaxf(tmax, x);
-            }
-        }
+            for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, s[mb][rr]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float m_new = fmaxf(m, tmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m - m_use);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new * a.scale_log2;
+        const float alpha = exp2f(m * a.scale_log2 - m_use);   // m = -inf gives 0
         m = m_new;
         float psum = 0.f;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                const float p = exp2f(s[mb][rr] - m_use);
+                const float p = exp2f(fmaf(s[mb][rr], a.scale_log2, -m_use));
                 s[mb][rr] = p;
                 psum += p;
             }
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
                 *reinterpret_cast<uint2 *>(orow + d) = raw;
             }
         }
-        if (hb == 0) a.lse[(int64_t)h * T + i] = (m + log2f(l_tot)) * kLn2;
+        if (hb == 0) a.lse[(int64_t)h * T + i] = (m * a.scale_log2 + log2f(l_tot)) * kLn2;
     }
 }
 
