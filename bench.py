@@ -39,12 +39,50 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-target-s", type=float, default=15.0,
                    help="approximate CPU seconds for the oracle sample")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="run a plain device copy of this many MiB before warmup (HBM counter "
+                        "calibration under rocprofv3 --pmc)")
     return p.parse_args()
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_attn_bwd_kv_qwen14b_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "packed_sequence_causal_pk_amd", "csrc", f)
+                  for f in ("pk_bwd.hip", "pk_device.h")]
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dK/dV kernel from the committed rocprofv3 counter summary,
+    or None when the summary is missing or was taken on different kernel source."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("machine:"):
+            for kv in line.split()[1:]:
+                k, _, v = kv.partition("=")
+                fields[k] = v
+    if fields.get("source_digest") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, lengths, target_s):
-    """Time the float64 oracle (as it is) on whole sequences of layer 0, one KV-head group,
-    adding sequences (shortest first) until about target_s seconds of work."""
+    """Time the float64 oracle (as it is) on whole sequences of layer 0, one KV-head group at a
+    time (KV head 0 first), adding sequences shortest first until about target_s seconds."""
     import numpy as np
     from oracle import pk_oracle as O
     from packed_sequence_causal_pk_amd import synth
@@ -53,25 +91,32 @@ def cpu_baseline(w, lengths, target_s):
     cu = np.concatenate([[0], np.cumsum(lengths)])
     order = np.argsort(lengths, kind="stable")
     done_flops, done_s, chosen = 0, 0.0, []
-    for s in order:
-        idx = np.arange(cu[s], cu[s + 1])
-        n = len(idx)
-        heads = list(range(w.group))  # KV head 0 and its query heads
-        t0 = time.perf_counter()
-        O.attn_fwd(q[idx], k[idx], v[idx], [n], w.softmax_scale, w.rope_base, heads=heads)
-        O.attn_bwd(q[idx], k[idx], v[idx], do[idx], [n], w.softmax_scale, w.rope_base, kv_heads=[0])
-        done_s += time.perf_counter() - t0
-        f, b = O.attn_flops([n], w.group, w.head_dim)
-        done_flops += f + b
-        chosen.append(int(n))
+    for kvh in range(w.hkv):
+        heads = [kvh * w.group + x for x in range(w.group)]
+        for s in order:
+            idx = np.arange(cu[s], cu[s + 1])
+            n = len(idx)
+            t0 = time.perf_counter()
+            O.attn_fwd(q[idx], k[idx], v[idx], [n], w.softmax_scale, w.rope_base, heads=heads)
+            O.attn_bwd(q[idx], k[idx], v[idx], do[idx], [n], w.softmax_scale, w.rope_base,
+                       kv_heads=[kvh])
+            done_s += time.perf_counter() - t0
+            f, b = O.attn_flops([n], w.group, w.head_dim)
+            done_flops += f + b
+            chosen.append((kvh, int(n)))
+            if done_s >= target_s:
+                break
         if done_s >= target_s:
             break
     cores = len(os.sched_getaffinity(0))
+    groups = sorted(set(c[0] for c in chosen))
     return {
         "value": done_flops / done_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-        "sample": "layer 0, KV head 0 with its %d query heads, %d whole sequences (lengths %s) of "
-                  "the pack; fwd+bwd float64 numpy, %.1f s" % (w.group, len(chosen), chosen, done_s),
-        "seconds": done_s,
+        "sample": "layer 0, KV heads %s each with its %d query heads, %d (KV head, sequence) "
+                  "pairs of the pack (whole sequences, shortest first), fwd+bwd float64 numpy, "
+                  "%.1f s; TFLOP/s counts the same algorithmic FLOPs as the GPU value"
+                  % (groups, w.group, len(chosen), done_s),
+        "seconds": round(done_s, 2),
     }
 
 
@@ -113,6 +158,15 @@ def main():
     ws_f = pk.fwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
     ws_b = pk.bwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
     meta0.close()
+    if args.calibrate_copy_mib > 0:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("bench: calibration copy of %d bytes done twice" % nbytes, file=sys.stderr, flush=True)
+        del src, dst
     torch.cuda.synchronize()
     print("bench: %s, T=%d, %d layers, hq/hkv/d=%d/%d/%d" % (args.workload, T, L, w.hq, w.hkv, w.head_dim),
           file=sys.stderr, flush=True)
@@ -197,7 +251,8 @@ def main():
         "roofline": {
             "kernel": kernel_names[dominant],
             "bound": "mfma", "achieved": round(achieved[dominant], 2), "peak": PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved[dominant] / PEAK_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(achieved[dominant] / PEAK_TFLOPS, 4),
+            "traffic": measured_traffic() if dominant == "bwd" else None,
         },
     }
     if not args.no_cpu_baseline:

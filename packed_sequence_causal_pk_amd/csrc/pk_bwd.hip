@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const int row = r0 + row_perm(acc_row(rr, hb));
-                const float p = exp2f(fmaf(sp[rr], sl2, -plse[row]));
+                const float p = fast_exp2(fmaf(sp[rr], sl2, -plse[row]));
                 sp[rr] = p;
                 dp[rr] = p * (dp[rr] - pdd[row]);
             }
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
         for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                const float p = exp2f(fmaf(sc[mb][rr], sl2, -lse2));
+                const float p = fast_exp2(fmaf(sc[mb][rr], sl2, -lse2));
                 dp[mb][rr] = p * (dp[mb][rr] - dd);
             }
         }

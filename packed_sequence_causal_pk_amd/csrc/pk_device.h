@@ -32,6 +32,10 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// 2^x with the bare v_exp_f32 (results below 2^-126 flush to zero, which a softmax weight can
+// afford); exp2f would add a denormal-range fix-up of four more instructions per call.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Row permutation (swap bits 2 and 3 of the row index inside a 32-row block).  Feeding the first
 // operand of a product whose result is reused as the k operand of a second product in this
 // order makes each lane's 8 k values of the second product consecutive rows, so that operand

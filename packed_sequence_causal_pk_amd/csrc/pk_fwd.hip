@@ -116,8 +116,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
         }
     }
 
-    float m = -INFINITY;  // running max of this query's raw scores q.k
-    float l = 0.f;        // running sum of exp2(s - m) over this lane's half of the keys
+    float mref = -INFINITY;  // reference max of this query's scaled scores (log2 domain)
+    float l = 0.f;           // running sum of exp2(s*c - mref) over this lane's half of the keys
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = zero_f32x16();
@@ -178,24 +178,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, s[mb][rr]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m, tmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new * a.scale_log2;
-        const float alpha = exp2f(m * a.scale_log2 - m_use);   // m = -inf gives 0
-        m = m_new;
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.scale_log2;
+        // Lazy rescaling: the reference max mref (log2 domain) only moves when a row's max
+        // exceeds it by more than 8, so p = exp2(s*c - mref) <= 256 (exact enough in fp32 and
+        // fp16) and the O rescale is skipped for the whole wave on most tiles.
+        const bool bump = tmax > mref + 8.f;
+        if (__builtin_amdgcn_ballot_w64(bump)) {
+            const float mnew = bump ? tmax : mref;
+            const float alpha = fast_exp2(mref - mnew);   // mref = -inf gives 0
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+            mref = mnew;
+        }
+        const float m_use = mref == -INFINITY ? 0.f : mref;
         float psum = 0.f;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                const float p = exp2f(fmaf(s[mb][rr], a.scale_log2, -m_use));
+                const float p = fast_exp2(fmaf(s[mb][rr], a.scale_log2, -m_use));
                 s[mb][rr] = p;
                 psum += p;
             }
         }
-        l = l * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        l += psum;
 
         // O^T (d x queries) += V^T (d x keys) * P^T (keys x queries); V^T read transposed
 #pragma unroll
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
                 *reinterpret_cast<uint2 *>(orow + d) = raw;
             }
         }
-        if (hb == 0) a.lse[(int64_t)h * T + i] = (m * a.scale_log2 + log2f(l_tot)) * kLn2;
+        if (hb == 0) a.lse[(int64_t)h * T + i] = (mref + log2f(l_tot)) * kLn2;
     }
 }
 
