@@ -31,6 +31,8 @@
 // operands are fp16 with fp32 accumulation; dout enters scaled by the power of two sigma the
 // prologue chose (max|dout| * sigma in [1, 2)), so dP and dS are sigma-scaled and the results
 // are unscaled exactly by 1/sigma when written.
+#include <type_traits>
+
 #include "pk_internal.h"
 #include "pk_device.h"
 
@@ -64,11 +66,11 @@ struct BwdArgs {
 template <int D>
 struct KvSmem {
     static constexpr int BQ = 64;        // query rows per block
-    f16 q[2][BQ * D];    // swizzled row-major Q_rot blocks (double-buffered)
-    f16 dO[2][BQ * D];   // swizzled row-major sigma * dout blocks
-    float lse2[2][BQ];   // lse * log2(e) of the block's rows
+    float lse2[2][BQ];   // lse * log2(e) of the block's rows (double-buffered like the tiles)
     float dd[2][BQ];     // sigma * D_i
     int pos[2][BQ];      // position of each row inside its sequence
+    f16 q[2][BQ * D];    // swizzled row-major Q_rot blocks
+    f16 dO[2][BQ * D];   // swizzled row-major sigma * dout blocks
 };
 
 template <int D>
@@ -85,12 +87,28 @@ __device__ void kv_zero_tile(const BwdArgs &a, int tile, int kvh) {
     }
 }
 
-// Start the asynchronous copy of one query block (rows [qb, qb + BQ) of head h, clamped to
-// T - 1) into buffer `buf`: Q_rot and sigma * dout tiles, and the per-row lse2, dd and pos.
+// Start the asynchronous copy of one query block (rows [qb, qb + BQ) of head h) into buffer
+// `buf`: Q_rot and sigma * dout tiles, and the per-row lse2, dd and pos.  A block whose rows all
+// exist is addressed by scalar bases and the precomputed lane offset `loff`; the last block of a
+// pack clamps its rows to T - 1 lane by lane (their weights are masked to zero).
 template <int D>
 __device__ __forceinline__ void kv_issue_block(const BwdArgs &a, KvSmem<D> &sm, int buf, int h,
-                                               int qb) {
+                                               int qb, uint32_t loff) {
     using S = KvSmem<D>;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (qb + S::BQ <= a.T) {
+        const int64_t rs = (int64_t)a.hq * D;
+        const int64_t first = ((int64_t)qb * a.hq + h) * D;
+        tile_copy_async_whole<D, S::BQ>(sm.q[buf], a.qrot + first, rs, loff);
+        tile_copy_async_whole<D, S::BQ>(sm.dO[buf], a.dout16 + first, rs, loff);
+        if (w == 0) {  // one wave: 64 rows x 4 bytes per array
+            lds_dma_s<4>(a.lse2 + (int64_t)h * a.T + qb, 4u * lane, lds_addr(sm.lse2[buf]));
+            lds_dma_s<4>(a.dsum + (int64_t)h * a.T + qb, 4u * lane, lds_addr(sm.dd[buf]));
+            lds_dma_s<4>(a.pos + qb, 4u * lane, lds_addr(sm.pos[buf]));
+        }
+        return;
+    }
     const int64_t last = a.T - 1;
     tile_copy_async<D, S::BQ>(sm.q[buf], 4, [&](int row) {
         return a.qrot + ((int64_t)min((int64_t)(qb + row), last) * a.hq + h) * D;
@@ -98,14 +116,23 @@ __device__ __forceinline__ void kv_issue_block(const BwdArgs &a, KvSmem<D> &sm, 
     tile_copy_async<D, S::BQ>(sm.dO[buf], 4, [&](int row) {
         return a.dout16 + ((int64_t)min((int64_t)(qb + row), last) * a.hq + h) * D;
     });
-    if (threadIdx.x < 64) {  // one wave: 64 rows x 4 bytes per array
-        const int64_t i = min((int64_t)(qb + threadIdx.x), last);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a.lse2 + (int64_t)h * a.T + i),
-                                         (__attribute__((address_space(3))) void *)sm.lse2[buf], 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a.dsum + (int64_t)h * a.T + i),
-                                         (__attribute__((address_space(3))) void *)sm.dd[buf], 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(a.pos + i),
-                                         (__attribute__((address_space(3))) void *)sm.pos[buf], 4, 0, 0);
+    if (w == 0) {
+        const int64_t i = min((int64_t)(qb + lane), last);
+        lds_dma<4>(a.lse2 + (int64_t)h * a.T + i, lds_addr(sm.lse2[buf]));
+        lds_dma<4>(a.dsum + (int64_t)h * a.T + i, lds_addr(sm.dd[buf]));
+        lds_dma<4>(a.pos + i, lds_addr(sm.pos[buf]));
+    }
+}
+
+// 8 consecutive floats (or ints) of a per-row LDS array as two 16-byte reads.
+template <typename T>
+__device__ __forceinline__ void lds_row8(const T *p, T (&out)[8]) {
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    const v4 x = reinterpret_cast<const v4 *>(p)[0], y = reinterpret_cast<const v4 *>(p)[1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        out[c] = x[c];
+        out[4 + c] = y[c];
     }
 }
 
@@ -114,6 +141,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
     using S = KvSmem<D>;
     constexpr int BQ = S::BQ;
     constexpr int NKK = D / 16, NDB = D / 32;
+    constexpr uint32_t HALF = 32 * D * 2;    // bytes from row 0 to row 32 of a tile
     __shared__ __attribute__((aligned(16))) S sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -136,7 +164,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
 
     const int nqb = (q_end - q_start + BQ - 1) / BQ;
     const int n_iter = a.group * nqb;
-    kv_issue_block<D>(a, sm, 0, kvh * a.group, q_start);
+    const uint32_t loff = tile_copy_lane_off<D>((int64_t)a.hq * D);
+    kv_issue_block<D>(a, sm, 0, kvh * a.group, q_start, loff);
 
     // K_rot and V of this lane's key, as k operands (d in [16kk + 8hb, +8))
     f16x8 kf[NKK], vf[NKK];
@@ -146,6 +175,29 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
         for (int kk = 0; kk < NKK; ++kk) {
             kf[kk] = kvalid ? load_f16x8(a.krot + row + 16 * kk) : zero_f16x8();
             vf[kk] = kvalid ? load_f16x8(a.v + row + 16 * kk) : zero_f16x8();
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            settle(kf[kk]);
+            settle(vf[kk]);
+        }
+    }
+
+    // Per-lane byte offsets inside a tile, fixed for the whole kernel so that every LDS read in
+    // the loop is a register plus an immediate:
+    //   aoff[kk]     row operand chunk of tile row row_perm(n32) (rows 32.. add HALF)
+    //   toff[db][x]  the two ds_read_b64_tr_b16 of the transposed operand of columns 32 db ..
+    uint32_t aoff[NKK], toff[NDB][2];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) aoff[kk] = 2 * tile_off<D>(row_perm(n32), 16 * kk + 8 * hb);
+    {
+        const int jj = lane & 15, g = lane >> 4;
+        const int tr = 8 * (g >> 1) + (jj >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = 32 * db + 16 * (g & 1) + 4 * (jj & 3);
+            toff[db][0] = 2 * tile_off<D>(tr, col);
+            toff[db][1] = 2 * tile_off<D>(tr + 4, col);
         }
     }
 
@@ -157,61 +209,46 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
     }
     const float sl2 = a.scale * kLog2e;
 
-    int buf = 0;
-    for (int itn = 0; itn < n_iter; ++itn, buf ^= 1) {
-        const int hh = itn / nqb;
-        const int qb = q_start + (itn - hh * nqb) * BQ;
-        lds_copy_wait();
-        __syncthreads();
-        if (itn + 1 < n_iter) {
-            const int hn = (itn + 1) / nqb;
-            kv_issue_block<D>(a, sm, buf ^ 1, kvh * a.group + hn, q_start + (itn + 1 - hn * nqb) * BQ);
-        }
-        if (!wave_active) continue;
+    // One 64-row block held in buffer BUF.  Result register rr of the 32x32 products of half hf
+    // belongs to block row 32 hf + 8 hb + (rr % 8) + 16 (rr / 8) (the row_perm order of the row
+    // operand), so each lane's per-row values are two runs of 8 consecutive rows.
+    auto block = [&](auto bufc, int qb) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
+        const char *cq = reinterpret_cast<const char *>(sm.q[BUF]);
+        const char *cg = reinterpret_cast<const char *>(sm.dO[BUF]);
         const int nrows = min(BQ, q_end - qb);
-        const f16 *tq = sm.q[buf];
-        const f16 *tg = sm.dO[buf];
-        const float *plse = sm.lse2[buf];
-        const float *pdd = sm.dd[buf];
-        const int *ppos = sm.pos[buf];
+        auto row_op = [&](const char *t, int kk, int hf) {
+            return *reinterpret_cast<const f16x8 *>(t + aoff[kk] + hf * HALF);
+        };
+        auto tr_op = [&](const char *t, int k0, int db) {  // transposed operand, tile rows k0..
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            typedef short s16x8 __attribute__((ext_vector_type(8)));
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + toff[db][0] + 2 * D * k0));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + toff[db][1] + 2 * D * k0));
+            return __builtin_bit_cast(f16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // P and dS of half hf from its S and dP, then dV^T += dO^T P and dK^T += Q^T dS (queries
+        // are the k dimension; the transposed operands come straight from the row-major tiles)
+        auto finish = [&](int hf, f32x16 &sp, f32x16 &dp) __attribute__((always_inline)) {
+            float lv[16], dv[16];
 #pragma unroll
-        for (int qm = 0; qm < 2; ++qm) {
-            // rows [qb + 32qm, +32) of the block against this wave's 32 keys
-            const int r0 = 32 * qm;
-            const int hrows = min(32, nrows - r0);
-            if (hrows <= 0) continue;
-            const int rl = r0 + hrows - 1;
-            const int lo_first = __builtin_amdgcn_readfirstlane(qb + r0 - ppos[r0]);
-            const int lo_last = __builtin_amdgcn_readfirstlane(qb + rl - ppos[rl]);
-            if (qb + r0 + hrows - 1 < wk0 || lo_first > wk_last) continue;
-            const bool need_mask = !(hrows == 32 && qb + r0 >= wk0 + 31 && lo_last <= wk0);
-            f32x16 sp = zero_f32x16(), dp = zero_f32x16();
-            {
-                const int row = r0 + row_perm(n32);
+            for (int e = 0; e < 2; ++e) {
+                float t8[8], u8[8];
+                lds_row8(&sm.lse2[BUF][32 * hf + 16 * e + 8 * hb], t8);
+                lds_row8(&sm.dd[BUF][32 * hf + 16 * e + 8 * hb], u8);
 #pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    sp = mfma32(tile_row8<D>(tq, row, 16 * kk + 8 * hb), kf[kk], sp);
-                    dp = mfma32(tile_row8<D>(tg, row, 16 * kk + 8 * hb), vf[kk], dp);
-                }
-            }
-            if (need_mask) {  // uniform branch: boundary / diagonal blocks only
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int row = r0 + row_perm(acc_row(rr, hb));
-                    const int i = qb + row;
-                    const bool keep = (row < nrows) & (j >= i - ppos[row]) & (j <= i);  // no short circuit
-                    sp[rr] = keep ? sp[rr] : -INFINITY;
+                for (int x = 0; x < 8; ++x) {
+                    lv[8 * e + x] = t8[x];
+                    dv[8 * e + x] = u8[x];
                 }
             }
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                const int row = r0 + row_perm(acc_row(rr, hb));
-                const float p = fast_exp2(fmaf(sp[rr], sl2, -plse[row]));
+                const float p = fast_exp2(fmaf(sp[rr], sl2, -lv[rr]));
                 sp[rr] = p;
-                dp[rr] = p * (dp[rr] - pdd[row]);
+                dp[rr] = p * (dp[rr] - dv[rr]);
             }
-            // dV^T += dO^T P,  dK^T += Q^T dS  (queries are the k dimension; the transposed
-            // operands are read straight from the row-major blocks)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 f16x8 pb, sb;
@@ -222,11 +259,64 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
                 }
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    dva[db] = mfma32(tile_a_tr<D>(tg, r0 + 16 * e, 32 * db), pb, dva[db]);
-                    dka[db] = mfma32(tile_a_tr<D>(tq, r0 + 16 * e, 32 * db), sb, dka[db]);
+                    dva[db] = mfma32(tr_op(cg, 32 * hf + 16 * e, db), pb, dva[db]);
+                    dka[db] = mfma32(tr_op(cq, 32 * hf + 16 * e, db), sb, dka[db]);
                 }
             }
+        };
+
+        // Each 32-row half is skipped when it sees none of the wave's keys and masked
+        // element-wise only when it sees some but not all of them (uniform branches).
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int r0 = 32 * hf;
+            const int hrows = min(32, nrows - r0);
+            if (hrows <= 0) continue;
+            const int rl = r0 + hrows - 1;
+            const int lo_first = __builtin_amdgcn_readfirstlane(qb + r0 - sm.pos[BUF][r0]);
+            const int lo_last = __builtin_amdgcn_readfirstlane(qb + rl - sm.pos[BUF][rl]);
+            if (qb + rl < wk0 || lo_first > wk_last) continue;
+            const bool need_mask = !(hrows == 32 && qb + r0 >= wk0 + 31 && lo_last <= wk0);
+            f32x16 sp = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                sp = mfma32(row_op(cq, kk, hf), kf[kk], sp);
+                dp = mfma32(row_op(cg, kk, hf), vf[kk], dp);
+            }
+            if (need_mask) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    int p8[8];
+                    lds_row8(&sm.pos[BUF][r0 + 16 * e + 8 * hb], p8);
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) {
+                        const int row = r0 + 16 * e + 8 * hb + x;
+                        const int i = qb + row;
+                        const bool keep = (row < nrows) & (j >= i - p8[x]) & (j <= i);  // no short circuit
+                        sp[8 * e + x] = keep ? sp[8 * e + x] : -INFINITY;
+                    }
+                }
+            }
+            finish(hf, sp, dp);
         }
+    };
+
+    // the loop is unrolled by two so that the buffer of each step is a compile-time constant
+    auto step = [&](auto bufc, int itn) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
+        const int hh = itn / nqb;
+        const int qb = q_start + (itn - hh * nqb) * BQ;
+        lds_copy_wait();
+        __syncthreads();
+        if (itn + 1 < n_iter) {
+            const int hn = (itn + 1) / nqb;
+            kv_issue_block<D>(a, sm, BUF ^ 1, kvh * a.group + hn, q_start + (itn + 1 - hn * nqb) * BQ, loff);
+        }
+        if (wave_active) block(bufc, qb);
+    };
+    for (int itn = 0; itn < n_iter; itn += 2) {
+        step(std::integral_constant<int, 0>(), itn);
+        if (itn + 1 < n_iter) step(std::integral_constant<int, 1>(), itn + 1);
     }
 
     // epilogue: dV as is; dK = R(-theta) (scale * dK_rot); both unscaled by 1/sigma
@@ -320,6 +410,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
             qf[kk] = qvalid ? load_f16x8(a.qrot + row + 16 * kk) : zero_f16x8();
             gf[kk] = qvalid ? load_f16x8(a.dout16 + row + 16 * kk) : zero_f16x8();
         }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            settle(qf[kk]);
+            settle(gf[kk]);
+        }
+        settle(lse2);
+        settle(dd);
+        settle(lo_i);
     }
     f32x16 acc[NDB];
 #pragma unroll

@@ -95,6 +95,26 @@ __device__ __forceinline__ f16x8 tile_a_tr(const f16 *tile, int k0, int m0) {
     return __builtin_bit_cast(f16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// One global_load_lds per lane: `BYTES` (4 or 16) bytes from global address g land in LDS at
+// byte lds + BYTES * lane (lds is the wave-uniform LDS offset, passed through M0).  The load is
+// written as inline assembly on purpose: the compiler cannot tell which LDS bytes the builtin form
+// writes, so after it it makes the first LDS read of ANY buffer wait for every outstanding copy,
+// which would serialise a double-buffered prefetch with the compute on the other buffer.  The
+// copies stay counted by vmcnt; lds_copy_wait() followed by a barrier publishes them.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void *g, uint32_t lds) {
+    static_assert(BYTES == 4 || BYTES == 16, "global_load_lds moves 4 or 16 bytes per lane");
+    if constexpr (BYTES == 16)
+        asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+    else
+        asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
+// LDS byte offset of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
 // Asynchronous copy of one row-major [rows x D] fp16 tile from global memory into a swizzled LDS
 // tile with global_load_lds_dwordx4: each instruction moves 64 lanes x 16 bytes to a contiguous
 // 1 KB run of LDS (lane l at byte 16 l), so the swizzle is applied on the global side by choosing
@@ -107,18 +127,59 @@ __device__ __forceinline__ void tile_copy_async(f16 *tile, int nwaves, RowPtr sr
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
     constexpr int RUNS = ROWS * CPR / 64;      // 1 KB runs per tile
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t base = lds_addr(tile);
     for (int run = w; run < RUNS; run += nwaves) {
         const int c = run * 64 + lane;         // physical chunk index in the tile
         const int row = c / CPR;
         const int logical = (c % CPR) ^ swz<D>(row);
-        const f16 *g = src(row) + 8 * logical;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                         (__attribute__((address_space(3))) void *)(tile + run * 512),
-                                         16, 0, 0);
+        lds_dma<16>(src(row) + 8 * logical, base + 1024u * run);
     }
 }
 
+// Same load with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset (the
+// saddr form), so a caller can advance the base with scalar arithmetic only.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma_s(const void *base, uint32_t lane_off, uint32_t lds) {
+    static_assert(BYTES == 4 || BYTES == 16, "global_load_lds moves 4 or 16 bytes per lane");
+    if constexpr (BYTES == 16)
+        asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(lds) : "memory");
+    else
+        asm volatile("global_load_lds_dword %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// Copies by 4 waves with every tile row present: lane offset (bytes, from element 0 of the tile's
+// first row) of the 16 bytes this lane fetches in its wave's first 1 KB run, for rows that are
+// `row_stride` halves apart.  Wave w issues runs w, w + 4, ...; run w + 4t starts 4t * (64 / (D/8))
+// rows further down, a multiple of 16 rows, so the swizzled chunk of the lane is the same in every
+// run and only the wave-uniform base moves.
+template <int D>
+__device__ __forceinline__ uint32_t tile_copy_lane_off(int64_t row_stride) {
+    constexpr int CPR = D / 8, RPR = 64 / CPR;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int row = w * RPR + lane / CPR;
+    const int chunk = (lane % CPR) ^ swz<D>(row);
+    return (uint32_t)(((int64_t)row * row_stride + 8 * chunk) * 2);
+}
+
+template <int D, int ROWS>
+__device__ __forceinline__ void tile_copy_async_whole(f16 *tile, const f16 *base, int64_t row_stride,
+                                                      uint32_t lane_off) {
+    constexpr int CPR = D / 8, RPR = 64 / CPR, RUNS = ROWS * CPR / 64;
+    static_assert(RUNS % 4 == 0, "runs are split evenly over 4 waves");
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lds = lds_addr(tile) + 1024u * w;
+#pragma unroll
+    for (int t = 0; t < RUNS / 4; ++t)
+        lds_dma_s<16>(base + (int64_t)(4 * RPR * t) * row_stride, lane_off, lds + 4096u * t);
+}
+
 __device__ __forceinline__ void lds_copy_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Make the compiler complete the pending global load of x here.  Used on values loaded before a
+// loop that keeps asynchronous LDS copies in flight: left alone, the compiler's wait for such a
+// value sits inside the loop, where a full vmcnt wait would also drain those copies.
+template <typename T>
+__device__ __forceinline__ void settle(const T &x) { asm volatile("" ::"v"(x)); }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     bf16x8 z;
