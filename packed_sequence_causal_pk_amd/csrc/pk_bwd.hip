@@ -190,16 +190,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
     uint32_t aoff[NKK], toff[NDB][2];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) aoff[kk] = 2 * tile_off<D>(row_perm(n32), 16 * kk + 8 * hb);
-    {
-        const int jj = lane & 15, g = lane >> 4;
-        const int tr = 8 * (g >> 1) + (jj >> 2);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const int col = 32 * db + 16 * (g & 1) + 4 * (jj & 3);
-            toff[db][0] = 2 * tile_off<D>(tr, col);
-            toff[db][1] = 2 * tile_off<D>(tr + 4, col);
-        }
-    }
+    tile_tr_offsets<D>(toff);
 
     f32x16 dka[NDB], dva[NDB];
 #pragma unroll
@@ -221,12 +212,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
             return *reinterpret_cast<const f16x8 *>(t + aoff[kk] + hf * HALF);
         };
         auto tr_op = [&](const char *t, int k0, int db) {  // transposed operand, tile rows k0..
-            typedef short s16x4 __attribute__((ext_vector_type(4)));
-            typedef short s16x8 __attribute__((ext_vector_type(8)));
-            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + toff[db][0] + 2 * D * k0));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + toff[db][1] + 2 * D * k0));
-            return __builtin_bit_cast(f16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            return tile_tr_at(t, toff[db], 2 * D * k0);
         };
         // P and dS of half hf from its S and dP, then dV^T += dO^T P and dK^T += Q^T dS (queries
         // are the k dimension; the transposed operands come straight from the row-major tiles)
@@ -427,29 +413,28 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     const int kb_hi = ((q_end - 1) / BK) * BK;
     const int kb_lo = (kv_start / BK) * BK;
 
+    // Per-lane LDS byte offsets, fixed for the kernel: aoff[kk] is the 16-byte chunk of key row
+    // row_perm(n32) for d in [16kk + 8hb, +8) (rows 32.. add 64 D bytes); toff the K^T reads.
+    uint32_t aoff[NKK], toff[NDB][2];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) aoff[kk] = 2 * tile_off<D>(row_perm(n32), 16 * kk + 8 * hb);
+    tile_tr_offsets<D>(toff);
+    const uint32_t loff = tile_copy_lane_off<D>((int64_t)a.hkv * D);
+
     // K_rot / V tiles stream into double-buffered swizzled LDS tiles with asynchronous
     // global->LDS copies (rows past T clamped to T-1; their weight is masked to zero)
     auto issue_tile = [&](int k0, int buf) {
-        tile_copy_async<D, BK>(lds_k[buf], 4, [&](int row) {
-            return a.krot + ((int64_t)min((int64_t)(k0 + row), T - 1) * a.hkv + kvh) * D;
-        });
-        tile_copy_async<D, BK>(lds_v[buf], 4, [&](int row) {
-            return a.v + ((int64_t)min((int64_t)(k0 + row), T - 1) * a.hkv + kvh) * D;
-        });
+        tile_issue<D, BK>(lds_k[buf], a.krot, a.hkv, kvh, k0, T, loff);
+        tile_issue<D, BK>(lds_v[buf], a.v, a.hkv, kvh, k0, T, loff);
     };
 
-    issue_tile(kb_hi, 0);
-    int buf = 0;
-    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= BK, buf ^= 1) {
-        lds_copy_wait();
-        __syncthreads();
-        if (k0 - BK >= kb_lo) issue_tile(k0 - BK, buf ^ 1);
-        if (!wave_active) continue;
-        if (k0 > wq_last) continue;            // every key is after every query of the wave
-        if (k0 + BK - 1 < wlo_min) continue;   // every key is before the wave's first sequence
+    auto tile = [&](auto bufc, int k0) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
+        if (k0 > wq_last) return;            // every key is after every query of the wave
+        if (k0 + BK - 1 < wlo_min) return;   // every key is before the wave's first sequence
         const bool need_mask = !(k0 + BK - 1 <= wq0 && k0 >= wlo_max);
-        const f16 *tk = lds_k[buf];
-        const f16 *tv = lds_v[buf];
+        const char *tk = reinterpret_cast<const char *>(lds_k[BUF]);
+        const char *tv = reinterpret_cast<const char *>(lds_v[BUF]);
 
         // S^T = K Q^T and dP^T = V dO^T (keys x queries), key rows in row_perm order
         f32x16 sc[NMB], dp[NMB];
@@ -457,13 +442,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
         for (int mb = 0; mb < NMB; ++mb) {
             sc[mb] = zero_f32x16();
             dp[mb] = zero_f32x16();
-            const int krow = 32 * mb + row_perm(n32);
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                sc[mb] = mfma32(tile_row8<D>(tk, krow, 16 * kk + 8 * hb), qf[kk], sc[mb]);
-                dp[mb] = mfma32(tile_row8<D>(tv, krow, 16 * kk + 8 * hb), gf[kk], dp[mb]);
-            }
         }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+                sc[mb] = mfma32(*reinterpret_cast<const f16x8 *>(tk + aoff[kk] + 64 * D * mb), qf[kk], sc[mb]);
+                dp[mb] = mfma32(*reinterpret_cast<const f16x8 *>(tv + aoff[kk] + 64 * D * mb), gf[kk], dp[mb]);
+            }
         if (need_mask) {  // uniform branch: boundary / diagonal tiles only
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
@@ -492,9 +478,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
                 for (int x = 0; x < 8; ++x) sb[x] = (f16)dp[mb][8 * e + x];
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    acc[db] = mfma32(tile_a_tr<D>(tk, 32 * mb + 16 * e, 32 * db), sb, acc[db]);
+                    acc[db] = mfma32(tile_tr_at(tk, toff[db], 2 * D * (32 * mb + 16 * e)), sb, acc[db]);
             }
         }
+    };
+
+    // the loop is unrolled by two so that the buffer of each step is a compile-time constant
+    auto step = [&](auto bufc, int k0) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
+        lds_copy_wait();
+        __syncthreads();
+        if (k0 - BK >= kb_lo) issue_tile(k0 - BK, BUF ^ 1);
+        if (wave_active) tile(bufc, k0);
+    };
+    issue_tile(kb_hi, 0);
+    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= 2 * BK) {
+        step(std::integral_constant<int, 0>(), k0);
+        if (k0 - BK >= kb_lo) step(std::integral_constant<int, 1>(), k0 - BK);
     }
 
     // epilogue: dQ = R(-theta) (scale / sigma * dQ_rot), written once

@@ -173,6 +173,49 @@ __device__ __forceinline__ void tile_copy_async_whole(f16 *tile, const f16 *base
         lds_dma_s<16>(base + (int64_t)(4 * RPR * t) * row_stride, lane_off, lds + 4096u * t);
 }
 
+// Asynchronous copy of rows [row0, row0 + ROWS) of head h of a [T, H, D] fp16 tensor into a
+// swizzled LDS tile by 4 waves.  Tiles whose rows all exist take the scalar-addressed path
+// (lane_off from tile_copy_lane_off<D>(H * D)); a tile that runs past T clamps its rows to T - 1
+// lane by lane, and the caller masks those rows.
+template <int D, int ROWS>
+__device__ __forceinline__ void tile_issue(f16 *tile, const f16 *x, int H, int h, int row0, int64_t T,
+                                           uint32_t lane_off) {
+    const int64_t stride = (int64_t)H * D;
+    if (row0 + ROWS <= T) {
+        tile_copy_async_whole<D, ROWS>(tile, x + (int64_t)row0 * stride + (int64_t)h * D, stride, lane_off);
+    } else {
+        tile_copy_async<D, ROWS>(tile, 4, [&](int row) {
+            return x + min((int64_t)(row0 + row), T - 1) * stride + (int64_t)h * D;
+        });
+    }
+}
+
+// Per-lane byte offsets of the two ds_read_b64_tr_b16 that make up the transposed operand of
+// columns [32 db, +32) and tile rows [0, 16) (the layout of tile_a_tr with k0 = 0, m0 = 32 db):
+// rows k0 + 16 t add 32 D t bytes, the swizzle being periodic in 16 rows.
+template <int D>
+__device__ __forceinline__ void tile_tr_offsets(uint32_t (&off)[D / 32][2]) {
+    const int lane = threadIdx.x & 63, jj = lane & 15, g = lane >> 4;
+    const int r = 8 * (g >> 1) + (jj >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const int col = 32 * db + 16 * (g & 1) + 4 * (jj & 3);
+        off[db][0] = 2 * tile_off<D>(r, col);
+        off[db][1] = 2 * tile_off<D>(r + 4, col);
+    }
+}
+
+// Transposed operand from a tile at LDS bytes `t`, rows k0.. (k0 multiple of 16), columns of
+// the offsets `off` (from tile_tr_offsets).
+__device__ __forceinline__ f16x8 tile_tr_at(const char *t, const uint32_t (&off)[2], int byte_k0) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + off[0] + byte_k0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + off[1] + byte_k0));
+    return __builtin_bit_cast(f16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ void lds_copy_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Make the compiler complete the pending global load of x here.  Used on values loaded before a

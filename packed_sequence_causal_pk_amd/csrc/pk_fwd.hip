@@ -27,6 +27,8 @@
 //   * Q is rotated in the prologue from the per-call (cos, sin) table; K comes pre-rotated;
 //   * operands are fp16 (the bf16 inputs convert exactly; rotated values, P keep 3 more bits
 //     than bf16), accumulators and the softmax state fp32.
+#include <type_traits>
+
 #include "pk_internal.h"
 #include "pk_device.h"
 
@@ -125,41 +127,40 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     const int kb_hi = ((q_end - 1) / BK) * BK;
     const int kb_lo = (kv_start / BK) * BK;
 
+    // Per-lane LDS byte offsets, fixed for the kernel, so that every tile read in the loop is a
+    // register plus an immediate: aoff[kk] is the 16-byte chunk of key row row_perm(n32) for
+    // d in [16kk + 8hb, +8) (rows 32.. add 64 D bytes); toff are the transposed V^T reads.
+    uint32_t aoff[NKK], toff[NDB][2];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) aoff[kk] = 2 * tile_off<D>(row_perm(n32), 16 * kk + 8 * hb);
+    tile_tr_offsets<D>(toff);
+    const uint32_t loff = tile_copy_lane_off<D>((int64_t)a.hkv * D);
+
     // K_rot / V tiles stream into double-buffered swizzled LDS tiles with asynchronous
     // global->LDS copies: tile t+1 is in flight while tile t is computed, one barrier per tile.
     // Rows past T are clamped to row T-1 (finite data; the causal mask zeroes their weight).
     auto issue_tile = [&](int k0, int buf) {
-        tile_copy_async<D, BK>(lds_k[buf], 4, [&](int row) {
-            return a.krot + ((int64_t)min((int64_t)(k0 + row), T - 1) * a.hkv + kvh) * D;
-        });
-        tile_copy_async<D, BK>(lds_v[buf], 4, [&](int row) {
-            return a.v + ((int64_t)min((int64_t)(k0 + row), T - 1) * a.hkv + kvh) * D;
-        });
+        tile_issue<D, BK>(lds_k[buf], a.krot, a.hkv, kvh, k0, T, loff);
+        tile_issue<D, BK>(lds_v[buf], a.v, a.hkv, kvh, k0, T, loff);
     };
 
-    issue_tile(kb_hi, 0);
-    int buf = 0;
-    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= BK, buf ^= 1) {
-        lds_copy_wait();
-        __syncthreads();
-        if (k0 - BK >= kb_lo) issue_tile(k0 - BK, buf ^ 1);
-        const f16 *tk = lds_k[buf];
-        const f16 *tv = lds_v[buf];
-        if (!wave_active) continue;
-        if (k0 > wq_last) continue;            // every key is after every query of the wave
-        if (k0 + BK - 1 < wlo_min) continue;   // every key is before the wave's first sequence
+    auto tile = [&](auto bufc, int k0) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
+        const char *tk = reinterpret_cast<const char *>(lds_k[BUF]);
+        const char *tv = reinterpret_cast<const char *>(lds_v[BUF]);
+        if (k0 > wq_last) return;            // every key is after every query of the wave
+        if (k0 + BK - 1 < wlo_min) return;   // every key is before the wave's first sequence
         const bool need_mask = !(k0 + BK - 1 <= wq0 && k0 >= wlo_max);
 
         // S^T (keys x queries), key rows in row_perm order
         f32x16 s[NMB];
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-            s[mb] = zero_f32x16();
-            const int krow = 32 * mb + row_perm(n32);
+        for (int mb = 0; mb < NMB; ++mb) s[mb] = zero_f32x16();
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                s[mb] = mfma32(tile_row8<D>(tk, krow, 16 * kk + 8 * hb), qf[kk], s[mb]);
-        }
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+                s[mb] = mfma32(*reinterpret_cast<const f16x8 *>(tk + aoff[kk] + 64 * D * mb), qf[kk], s[mb]);
         // Online softmax in the exp2 domain.  The running max is kept on the raw scores; the
         // scale * log2(e) factor is folded into one FMA per score: p = exp2(s*c - m*c).
         // Masking runs only on tiles that straddle a boundary or the diagonal (a uniform branch).
@@ -214,9 +215,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
                 for (int x = 0; x < 8; ++x) pb[x] = (f16)s[mb][8 * e + x];
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    o[db] = mfma32(tile_a_tr<D>(tv, 32 * mb + 16 * e, 32 * db), pb, o[db]);
+                    o[db] = mfma32(tile_tr_at(tv, toff[db], 2 * D * (32 * mb + 16 * e)), pb, o[db]);
             }
         }
+    };
+
+    // the loop is unrolled by two so that the buffer of each step is a compile-time constant
+    auto step = [&](auto bufc, int k0) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
+        lds_copy_wait();
+        __syncthreads();
+        if (k0 - BK >= kb_lo) issue_tile(k0 - BK, BUF ^ 1);
+        if (wave_active) tile(bufc, k0);
+    };
+    issue_tile(kb_hi, 0);
+    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= 2 * BK) {
+        step(std::integral_constant<int, 0>(), k0);
+        if (k0 - BK >= kb_lo) step(std::integral_constant<int, 1>(), k0 - BK);
     }
 
     // epilogue: O = O^T / l, lse = ln(sum) of the scaled scores
