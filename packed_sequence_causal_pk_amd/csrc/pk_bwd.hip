@@ -71,6 +71,9 @@ struct KvSmem {
     int pos[2][BQ];      // position of each row inside its sequence
     f16 q[2][BQ * D];    // swizzled row-major Q_rot blocks
     f16 dO[2][BQ * D];   // swizzled row-major sigma * dout blocks
+    // P of the current block handed from the P waves to the dS waves: [key wave][half][chunk c]
+    // [lane][4] holds result registers 4c..4c+3 of that lane (conflict-free 16-byte accesses)
+    float xp[4][2][4][64][4];
 };
 
 template <int D>
@@ -88,39 +91,29 @@ __device__ void kv_zero_tile(const BwdArgs &a, int tile, int kvh) {
 }
 
 // Start the asynchronous copy of one query block (rows [qb, qb + BQ) of head h) into buffer
-// `buf`: Q_rot and sigma * dout tiles, and the per-row lse2, dd and pos.  A block whose rows all
-// exist is addressed by scalar bases and the precomputed lane offset `loff`; the last block of a
-// pack clamps its rows to T - 1 lane by lane (their weights are masked to zero).
+// `buf` by the workgroup's 8 waves: Q_rot and sigma * dout tiles, and the per-row lse2, dd and
+// pos.  A block whose rows all exist is addressed by scalar bases and the precomputed lane offset
+// `loff`; the last block of a pack clamps its rows to T - 1 lane by lane (their weights are
+// masked to zero).
 template <int D>
 __device__ __forceinline__ void kv_issue_block(const BwdArgs &a, KvSmem<D> &sm, int buf, int h,
                                                int qb, uint32_t loff) {
     using S = KvSmem<D>;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (qb + S::BQ <= a.T) {
-        const int64_t rs = (int64_t)a.hq * D;
-        const int64_t first = ((int64_t)qb * a.hq + h) * D;
-        tile_copy_async_whole<D, S::BQ>(sm.q[buf], a.qrot + first, rs, loff);
-        tile_copy_async_whole<D, S::BQ>(sm.dO[buf], a.dout16 + first, rs, loff);
-        if (w == 0) {  // one wave: 64 rows x 4 bytes per array
+    tile_issue<D, S::BQ, 8>(sm.q[buf], a.qrot, a.hq, h, qb, a.T, loff);
+    tile_issue<D, S::BQ, 8>(sm.dO[buf], a.dout16, a.hq, h, qb, a.T, loff);
+    if (w == 0) {  // one wave: 64 rows x 4 bytes per array
+        if (qb + S::BQ <= a.T) {
             lds_dma_s<4>(a.lse2 + (int64_t)h * a.T + qb, 4u * lane, lds_addr(sm.lse2[buf]));
             lds_dma_s<4>(a.dsum + (int64_t)h * a.T + qb, 4u * lane, lds_addr(sm.dd[buf]));
             lds_dma_s<4>(a.pos + qb, 4u * lane, lds_addr(sm.pos[buf]));
+        } else {
+            const int64_t i = min((int64_t)(qb + lane), a.T - 1);
+            lds_dma<4>(a.lse2 + (int64_t)h * a.T + i, lds_addr(sm.lse2[buf]));
+            lds_dma<4>(a.dsum + (int64_t)h * a.T + i, lds_addr(sm.dd[buf]));
+            lds_dma<4>(a.pos + i, lds_addr(sm.pos[buf]));
         }
-        return;
-    }
-    const int64_t last = a.T - 1;
-    tile_copy_async<D, S::BQ>(sm.q[buf], 4, [&](int row) {
-        return a.qrot + ((int64_t)min((int64_t)(qb + row), last) * a.hq + h) * D;
-    });
-    tile_copy_async<D, S::BQ>(sm.dO[buf], 4, [&](int row) {
-        return a.dout16 + ((int64_t)min((int64_t)(qb + row), last) * a.hq + h) * D;
-    });
-    if (w == 0) {
-        const int64_t i = min((int64_t)(qb + lane), last);
-        lds_dma<4>(a.lse2 + (int64_t)h * a.T + i, lds_addr(sm.lse2[buf]));
-        lds_dma<4>(a.dsum + (int64_t)h * a.T + i, lds_addr(sm.dd[buf]));
-        lds_dma<4>(a.pos + i, lds_addr(sm.pos[buf]));
     }
 }
 
@@ -136,8 +129,19 @@ __device__ __forceinline__ void lds_row8(const T *p, T (&out)[8]) {
     }
 }
 
+// The work of one (key tile, KV head) item is split by role over 8 waves; waves w and w + 4 own
+// the same 32 keys and share a SIMD:
+//   P waves (0..3)   S = Q K^T, the mask, P = exp2(S scale log2e - lse2), hand P over in LDS,
+//                    dV^T += dO^T P;
+//   dS waves (4..7)  dP = dO V^T, dS = P (dP - D) with P from LDS, dK^T += Q^T dS.
+// Each role holds one operand (K_rot or V) and one accumulator (dV or dK), so a wave needs
+// about half the registers of doing both, two waves fit on every SIMD, and every product
+// accumulates in ordinary VGPRs.  Per 64-row block the waves meet at two barriers:
+//   B0: block data in LDS  ->  S, P (P waves) | dP (dS waves)  ->  B1: P in LDS  ->
+//   dV (P waves) | dS, dK (dS waves)
+// so each SIMD runs one wave's products while the other does its element-wise work.
 template <int D>
-__global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
     using S = KvSmem<D>;
     constexpr int BQ = S::BQ;
     constexpr int NKK = D / 16, NDB = D / 32;
@@ -145,7 +149,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) S sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets bounds live in SGPRs
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets bounds live in SGPRs
+    const int w = wv & 3;                                     // key sub-tile of this wave
+    const bool p_role = wv < 4;
     const int n32 = lane & 31, hb = lane >> 5;
     const int r = blockIdx.x / a.hkv, kvh = blockIdx.x % a.hkv;
     const int32_t *it = a.items + (int64_t)r * PK_ITEM_FIELDS;
@@ -164,23 +170,22 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
 
     const int nqb = (q_end - q_start + BQ - 1) / BQ;
     const int n_iter = a.group * nqb;
-    const uint32_t loff = tile_copy_lane_off<D>((int64_t)a.hq * D);
-    kv_issue_block<D>(a, sm, 0, kvh * a.group, q_start, loff);
+    const uint32_t loff = tile_copy_lane_off<D, 8>((int64_t)a.hq * D);
+    // iteration itn: head (itn / nqb) of the group, query block (itn % nqb)
+    auto iter_row = [&](int itn) { return q_start + (itn % nqb) * BQ; };
+    auto iter_head = [&](int itn) { return kvh * a.group + itn / nqb; };
+    kv_issue_block<D>(a, sm, 0, iter_head(0), iter_row(0), loff);
 
-    // K_rot and V of this lane's key, as k operands (d in [16kk + 8hb, +8))
-    f16x8 kf[NKK], vf[NKK];
+    // this role's operand of this lane's key: K_rot (P waves) or V (dS waves), as k operands
+    // (d in [16kk + 8hb, +8))
+    f16x8 kvf[NKK];
     {
+        const f16 *src = p_role ? a.krot : a.v;
         const int64_t row = ((int64_t)(kvalid ? j : kv_start) * a.hkv + kvh) * D + 8 * hb;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            kf[kk] = kvalid ? load_f16x8(a.krot + row + 16 * kk) : zero_f16x8();
-            vf[kk] = kvalid ? load_f16x8(a.v + row + 16 * kk) : zero_f16x8();
-        }
+        for (int kk = 0; kk < NKK; ++kk) kvf[kk] = kvalid ? load_f16x8(src + row + 16 * kk) : zero_f16x8();
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            settle(kf[kk]);
-            settle(vf[kk]);
-        }
+        for (int kk = 0; kk < NKK; ++kk) settle(kvf[kk]);
     }
 
     // Per-lane byte offsets inside a tile, fixed for the whole kernel so that every LDS read in
@@ -192,15 +197,16 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
     for (int kk = 0; kk < NKK; ++kk) aoff[kk] = 2 * tile_off<D>(row_perm(n32), 16 * kk + 8 * hb);
     tile_tr_offsets<D>(toff);
 
-    f32x16 dka[NDB], dva[NDB];
+    f32x16 acc[NDB];   // dV^T (P waves) or dK_rot^T (dS waves): d rows x this wave's 32 keys
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        dka[db] = zero_f32x16();
-        dva[db] = zero_f32x16();
-    }
+    for (int db = 0; db < NDB; ++db) acc[db] = zero_f32x16();
     const float sl2 = a.scale * kLog2e;
 
-    // One 64-row block held in buffer BUF.  Result register rr of the 32x32 products of half hf
+    // The main loop, instantiated once per role so that each role's code and registers are
+    // its own.
+    auto main_loop = [&](auto rolec) __attribute__((always_inline)) {
+    constexpr bool p_role = decltype(rolec)::value;
+    // One 64-row block in buffer BUF.  Result register rr of the 32x32 products of half hf
     // belongs to block row 32 hf + 8 hb + (rr % 8) + 16 (rr / 8) (the row_perm order of the row
     // operand), so each lane's per-row values are two runs of 8 consecutive rows.
     auto block = [&](auto bufc, int qb) __attribute__((always_inline)) {
@@ -211,132 +217,192 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_kv(BwdArgs a) {
         auto row_op = [&](const char *t, int kk, int hf) {
             return *reinterpret_cast<const f16x8 *>(t + aoff[kk] + hf * HALF);
         };
-        auto tr_op = [&](const char *t, int k0, int db) {  // transposed operand, tile rows k0..
-            return tile_tr_at(t, toff[db], 2 * D * k0);
-        };
-        // P and dS of half hf from its S and dP, then dV^T += dO^T P and dK^T += Q^T dS (queries
-        // are the k dimension; the transposed operands come straight from the row-major tiles)
-        auto finish = [&](int hf, f32x16 &sp, f32x16 &dp) __attribute__((always_inline)) {
-            float lv[16], dv[16];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                float t8[8], u8[8];
-                lds_row8(&sm.lse2[BUF][32 * hf + 16 * e + 8 * hb], t8);
-                lds_row8(&sm.dd[BUF][32 * hf + 16 * e + 8 * hb], u8);
-#pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    lv[8 * e + x] = t8[x];
-                    dv[8 * e + x] = u8[x];
-                }
-            }
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const float p = fast_exp2(fmaf(sp[rr], sl2, -lv[rr]));
-                sp[rr] = p;
-                dp[rr] = p * (dp[rr] - dv[rr]);
-            }
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                f16x8 pb, sb;
-#pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    pb[x] = (f16)sp[8 * e + x];
-                    sb[x] = (f16)dp[8 * e + x];
-                }
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    dva[db] = mfma32(tr_op(cg, 32 * hf + 16 * e, db), pb, dva[db]);
-                    dka[db] = mfma32(tr_op(cq, 32 * hf + 16 * e, db), sb, dka[db]);
-                }
-            }
-        };
-
-        // Each 32-row half is skipped when it sees none of the wave's keys and masked
-        // element-wise only when it sees some but not all of them (uniform branches).
+        // Per-half visibility (uniform): a half is skipped when it has no item rows or sees none
+        // of this wave's keys, and masked element-wise unless all 32 rows see all 32 keys.  Both
+        // roles of a key sub-tile reach the same decisions from the same LDS data.
+        bool run[2], masked[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int r0 = 32 * hf;
             const int hrows = min(32, nrows - r0);
-            if (hrows <= 0) continue;
-            const int rl = r0 + hrows - 1;
+            const int rl = r0 + max(hrows, 1) - 1;
             const int lo_first = __builtin_amdgcn_readfirstlane(qb + r0 - sm.pos[BUF][r0]);
             const int lo_last = __builtin_amdgcn_readfirstlane(qb + rl - sm.pos[BUF][rl]);
-            if (qb + rl < wk0 || lo_first > wk_last) continue;
-            const bool need_mask = !(hrows == 32 && qb + r0 >= wk0 + 31 && lo_last <= wk0);
-            f32x16 sp = zero_f32x16(), dp = zero_f32x16();
+            run[hf] = wave_active && hrows > 0 && qb + rl >= wk0 && lo_first <= wk_last;
+            masked[hf] = !(hrows == 32 && qb + r0 >= wk0 + 31 && lo_last <= wk0);
+        }
+
+        f32x16 sp[2];       // P waves: S then P; dS waves: dP
+        f16x8 pb[2][2];     // fp16 k operands of the second products: P (P waves) or dS (dS waves)
+        // the first product of half hf: S = Q K^T (P waves) or dP = dO V^T (dS waves)
+        auto scores = [&](int hf) __attribute__((always_inline)) {
+            const char *t = p_role ? cq : cg;
+            sp[hf] = zero_f32x16();
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                sp = mfma32(row_op(cq, kk, hf), kf[kk], sp);
-                dp = mfma32(row_op(cg, kk, hf), vf[kk], dp);
-            }
-            if (need_mask) {
+            for (int kk = 0; kk < NKK; ++kk) sp[hf] = mfma32(row_op(t, kk, hf), kvf[kk], sp[hf]);
+        };
+        // P waves: P = exp2(S scale log2e - lse2) (masked when asked), stored for the dS waves
+        // and kept as fp16 operands
+        auto softmax = [&](int hf, bool msk) __attribute__((always_inline)) {
+            float4 *xp = reinterpret_cast<float4 *>(&sm.xp[w][hf][0][lane][0]);
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    int p8[8];
-                    lds_row8(&sm.pos[BUF][r0 + 16 * e + 8 * hb], p8);
+            for (int e = 0; e < 2; ++e) {
+                const int r8 = 32 * hf + 16 * e + 8 * hb;   // first row of this lane's 8
+                float lv[8];
+                lds_row8(&sm.lse2[BUF][r8], lv);
+                int p8[8];
+                if (msk) lds_row8(&sm.pos[BUF][r8], p8);
 #pragma unroll
-                    for (int x = 0; x < 8; ++x) {
-                        const int row = r0 + 16 * e + 8 * hb + x;
-                        const int i = qb + row;
-                        const bool keep = (row < nrows) & (j >= i - p8[x]) & (j <= i);  // no short circuit
-                        sp[8 * e + x] = keep ? sp[8 * e + x] : -INFINITY;
+                for (int x = 0; x < 8; ++x) {
+                    float sv = sp[hf][8 * e + x];
+                    if (msk) {
+                        const int i = qb + r8 + x;
+                        const bool keep = (r8 + x < nrows) & (j >= i - p8[x]) & (j <= i);  // no short circuit
+                        sv = keep ? sv : -INFINITY;
                     }
+                    const float p = fast_exp2(fmaf(sv, sl2, -lv[x]));
+                    sp[hf][8 * e + x] = p;
+                    pb[hf][e][x] = (f16)p;
                 }
+                xp[(2 * e) * 64] = make_float4(sp[hf][8 * e], sp[hf][8 * e + 1], sp[hf][8 * e + 2], sp[hf][8 * e + 3]);
+                xp[(2 * e + 1) * 64] = make_float4(sp[hf][8 * e + 4], sp[hf][8 * e + 5], sp[hf][8 * e + 6], sp[hf][8 * e + 7]);
             }
-            finish(hf, sp, dp);
+        };
+        // dS waves: dS = P (dP - D) with P from the P waves, as fp16 operands
+        auto dscore = [&](int hf) __attribute__((always_inline)) {
+            const float4 *xp = reinterpret_cast<const float4 *>(&sm.xp[w][hf][0][lane][0]);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r8 = 32 * hf + 16 * e + 8 * hb;
+                float dv[8];
+                lds_row8(&sm.dd[BUF][r8], dv);
+                const float4 p0 = xp[(2 * e) * 64], p1 = xp[(2 * e + 1) * 64];
+                const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+                for (int x = 0; x < 8; ++x) pb[hf][e][x] = (f16)(pv[x] * (sp[hf][8 * e + x] - dv[x]));
+            }
+        };
+        // the second product of half hf: dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves);
+        // queries are the k dimension and the transposed operand comes straight from the tile
+        auto grads = [&](int hf) __attribute__((always_inline)) {
+            const char *t = p_role ? cg : cq;
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    acc[db] = mfma32(tile_tr_at(t, toff[db], 2 * D * (32 * hf + 16 * e)), pb[hf][e], acc[db]);
+        };
+
+        // Blocks where both halves run (and, for the P waves, need no mask) take straight-line
+        // code whose LDS reads are issued ahead of their products; the rest go half by half.
+        const bool both = run[0] & run[1];
+        const bool fast = both & (!p_role | (!masked[0] & !masked[1]));
+        if (fast) {
+            scores(0);
+            scores(1);
+            __builtin_amdgcn_sched_group_barrier(0x100, NKK, 0);       // one half's operands ahead
+#pragma unroll
+            for (int m = 0; m < NKK; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NKK, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (p_role) {
+                softmax(0, false);
+                softmax(1, false);
+            }
+        } else {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                if (!run[hf]) continue;
+                scores(hf);
+                if (p_role) softmax(hf, masked[hf]);
+            }
+        }
+        __syncthreads();   // B1: P of both halves is in LDS
+        if (both) {
+            if (!p_role) {
+                dscore(0);
+                dscore(1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            grads(0);
+            grads(1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);         // 4 transposed operands ahead
+#pragma unroll
+            for (int m = 0; m < 4 * NDB - 4; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        } else {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                if (!run[hf]) continue;
+                if (!p_role) dscore(hf);
+                grads(hf);
+            }
         }
     };
 
     // the loop is unrolled by two so that the buffer of each step is a compile-time constant
     auto step = [&](auto bufc, int itn) __attribute__((always_inline)) {
         constexpr int BUF = decltype(bufc)::value;
-        const int hh = itn / nqb;
-        const int qb = q_start + (itn - hh * nqb) * BQ;
+        const int qb = iter_row(itn);
         lds_copy_wait();
-        __syncthreads();
-        if (itn + 1 < n_iter) {
-            const int hn = (itn + 1) / nqb;
-            kv_issue_block<D>(a, sm, BUF ^ 1, kvh * a.group + hn, q_start + (itn + 1 - hn * nqb) * BQ, loff);
-        }
-        if (wave_active) block(bufc, qb);
+        __syncthreads();   // B0: this block is in LDS; every wave is done with the other buffer
+        if (itn + 1 < n_iter) kv_issue_block<D>(a, sm, BUF ^ 1, iter_head(itn + 1), iter_row(itn + 1), loff);
+        block(bufc, qb);
     };
     for (int itn = 0; itn < n_iter; itn += 2) {
         step(std::integral_constant<int, 0>(), itn);
         if (itn + 1 < n_iter) step(std::integral_constant<int, 1>(), itn + 1);
     }
 
-    // epilogue: dV as is; dK = R(-theta) (scale * dK_rot); both unscaled by 1/sigma
+    };
+    if (wv < 4)
+        main_loop(std::true_type());
+    else
+        main_loop(std::false_type());
+
+    // epilogue: P waves write dV; dS waves write dK = R(-theta) (scale * dK_rot); both
+    // unscaled by 1/sigma
     if (kvalid) {
-        float *dvrow = a.dv + ((int64_t)j * a.hkv + kvh) * D;
-        float *dkrow = a.dk + ((int64_t)j * a.hkv + kvh) * D;
-        const float2 *cs = a.rope + (int64_t)j * (D / 2);
-        const float kscale = a.scale * inv_sigma;
+        const int64_t rowoff = ((int64_t)j * a.hkv + kvh) * D;
+        if (p_role) {
+            float *dvrow = a.dv + rowoff;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int d = 32 * db + 8 * g4 + 4 * hb;
-                *reinterpret_cast<float4 *>(dvrow + d) =
-                    make_float4(dva[db][4 * g4] * inv_sigma, dva[db][4 * g4 + 1] * inv_sigma,
-                                dva[db][4 * g4 + 2] * inv_sigma, dva[db][4 * g4 + 3] * inv_sigma);
-            }
-#pragma unroll
-        for (int db = 0; db < NDB / 2; ++db)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int d = 32 * db + 8 * g4 + 4 * hb;  // first half; partner d + D/2
-                float y1[4], y2[4];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const float2 f = cs[d + x];
-                    const float x1 = dka[db][4 * g4 + x] * kscale;
-                    const float x2 = dka[db + NDB / 2][4 * g4 + x] * kscale;
-                    y1[x] = x1 * f.x + x2 * f.y;
-                    y2[x] = x2 * f.x - x1 * f.y;
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d = 32 * db + 8 * g4 + 4 * hb;
+                    *reinterpret_cast<float4 *>(dvrow + d) =
+                        make_float4(acc[db][4 * g4] * inv_sigma, acc[db][4 * g4 + 1] * inv_sigma,
+                                    acc[db][4 * g4 + 2] * inv_sigma, acc[db][4 * g4 + 3] * inv_sigma);
                 }
-                *reinterpret_cast<float4 *>(dkrow + d) = make_float4(y1[0], y1[1], y1[2], y1[3]);
-                *reinterpret_cast<float4 *>(dkrow + d + D / 2) = make_float4(y2[0], y2[1], y2[2], y2[3]);
-            }
+        } else {
+            float *dkrow = a.dk + rowoff;
+            const float2 *cs = a.rope + (int64_t)j * (D / 2);
+            const float kscale = a.scale * inv_sigma;
+#pragma unroll
+            for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d = 32 * db + 8 * g4 + 4 * hb;  // first half; partner d + D/2
+                    float y1[4], y2[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const float2 f = cs[d + x];
+                        const float x1 = acc[db][4 * g4 + x] * kscale;
+                        const float x2 = acc[db + NDB / 2][4 * g4 + x] * kscale;
+                        y1[x] = x1 * f.x + x2 * f.y;
+                        y2[x] = x2 * f.x - x1 * f.y;
+                    }
+                    *reinterpret_cast<float4 *>(dkrow + d) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+                    *reinterpret_cast<float4 *>(dkrow + d + D / 2) = make_float4(y2[0], y2[1], y2[2], y2[3]);
+                }
+        }
     }
 }
 
@@ -363,7 +429,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets bounds live in SGPRs
     const int n32 = lane & 31, hb = lane >> 5;
-    const int r = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
+    int r, h;
+    item_head_of_block(blockIdx.x, a.hq, a.hkv, r, h);
     const int kvh = h / a.group;
     const int32_t *it = a.items + (int64_t)r * PK_ITEM_FIELDS;
     if (a.hdr[0] != 0) {
@@ -553,9 +620,9 @@ hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
         a.items = m.bwd_items;
         const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hkv;
         if (sh.d == 128)
-            k_attn_bwd_kv<128><<<grid, 256, 0, s>>>(a);
+            k_attn_bwd_kv<128><<<grid, 512, 0, s>>>(a);
         else
-            k_attn_bwd_kv<64><<<grid, 256, 0, s>>>(a);
+            k_attn_bwd_kv<64><<<grid, 512, 0, s>>>(a);
     } else {
         a.items = m.fwd_items;
         const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hq;

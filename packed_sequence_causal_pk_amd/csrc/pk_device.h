@@ -47,6 +47,25 @@ __device__ __forceinline__ int row_perm(int m) {
 // Row of 32x32 result register r for a lane in half hb (before any permutation).
 __device__ __forceinline__ int acc_row(int r, int hb) { return 8 * (r >> 2) + 4 * hb + (r & 3); }
 
+// Workgroup b of a grid of n_items x hq -> (work item r, query head h).  Workgroups are handed
+// to the 8 XCDs round-robin (b runs on XCD b % 8), each XCD with its own L2.  When the KV heads
+// split evenly over the XCDs, the query heads that share a KV head get consecutive slots of one
+// XCD, so the K/V tiles they all read are fetched into that L2 once; items keep their
+// longest-first order.  Otherwise the plain item-major, head-minor order is used.
+__device__ __forceinline__ void item_head_of_block(int b, int hq, int hkv, int &r, int &h) {
+    constexpr int NX = 8;
+    if (hkv % NX == 0) {
+        const int group = hq / hkv, per = hq / NX;   // query heads per XCD per item
+        const int x = b % NX, m = b / NX;
+        r = m / per;
+        const int t = m % per;
+        h = (x + NX * (t / group)) * group + t % group;
+    } else {
+        r = b / hq;
+        h = b % hq;
+    }
+}
+
 // ---- Swizzled row-major fp16 LDS tiles ------------------------------------------------------
 // A tile holds rows of D halves with no padding; the 16-byte chunk c of row r is stored at chunk
 // position c ^ swz(r).  Two read patterns are conflict-free on the 64 LDS banks:
@@ -147,44 +166,45 @@ __device__ __forceinline__ void lds_dma_s(const void *base, uint32_t lane_off, u
         asm volatile("global_load_lds_dword %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(lds) : "memory");
 }
 
-// Copies by 4 waves with every tile row present: lane offset (bytes, from element 0 of the tile's
+// Copies by NW waves with every tile row present: lane offset (bytes, from element 0 of the tile's
 // first row) of the 16 bytes this lane fetches in its wave's first 1 KB run, for rows that are
-// `row_stride` halves apart.  Wave w issues runs w, w + 4, ...; run w + 4t starts 4t * (64 / (D/8))
-// rows further down, a multiple of 16 rows, so the swizzled chunk of the lane is the same in every
-// run and only the wave-uniform base moves.
-template <int D>
+// `row_stride` halves apart.  Wave w issues runs w, w + NW, ...; run w + NW t starts
+// NW t * (64 / (D/8)) rows further down, a multiple of 16 rows, so the swizzled chunk of the lane
+// is the same in every run and only the wave-uniform base moves.
+template <int D, int NW = 4>
 __device__ __forceinline__ uint32_t tile_copy_lane_off(int64_t row_stride) {
     constexpr int CPR = D / 8, RPR = 64 / CPR;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    static_assert((NW * RPR) % 16 == 0, "swizzle period");
+    const int lane = threadIdx.x & 63, w = (threadIdx.x >> 6) % NW;
     const int row = w * RPR + lane / CPR;
     const int chunk = (lane % CPR) ^ swz<D>(row);
     return (uint32_t)(((int64_t)row * row_stride + 8 * chunk) * 2);
 }
 
-template <int D, int ROWS>
+template <int D, int ROWS, int NW = 4>
 __device__ __forceinline__ void tile_copy_async_whole(f16 *tile, const f16 *base, int64_t row_stride,
                                                       uint32_t lane_off) {
     constexpr int CPR = D / 8, RPR = 64 / CPR, RUNS = ROWS * CPR / 64;
-    static_assert(RUNS % 4 == 0, "runs are split evenly over 4 waves");
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    static_assert(RUNS % NW == 0, "runs are split evenly over the waves");
+    const int w = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % NW);
     const uint32_t lds = lds_addr(tile) + 1024u * w;
 #pragma unroll
-    for (int t = 0; t < RUNS / 4; ++t)
-        lds_dma_s<16>(base + (int64_t)(4 * RPR * t) * row_stride, lane_off, lds + 4096u * t);
+    for (int t = 0; t < RUNS / NW; ++t)
+        lds_dma_s<16>(base + (int64_t)(NW * RPR * t) * row_stride, lane_off, lds + 1024u * NW * t);
 }
 
 // Asynchronous copy of rows [row0, row0 + ROWS) of head h of a [T, H, D] fp16 tensor into a
-// swizzled LDS tile by 4 waves.  Tiles whose rows all exist take the scalar-addressed path
-// (lane_off from tile_copy_lane_off<D>(H * D)); a tile that runs past T clamps its rows to T - 1
-// lane by lane, and the caller masks those rows.
-template <int D, int ROWS>
+// swizzled LDS tile by NW waves.  Tiles whose rows all exist take the scalar-addressed path
+// (lane_off from tile_copy_lane_off<D, NW>(H * D)); a tile that runs past T clamps its rows to
+// T - 1 lane by lane, and the caller masks those rows.
+template <int D, int ROWS, int NW = 4>
 __device__ __forceinline__ void tile_issue(f16 *tile, const f16 *x, int H, int h, int row0, int64_t T,
                                            uint32_t lane_off) {
     const int64_t stride = (int64_t)H * D;
     if (row0 + ROWS <= T) {
-        tile_copy_async_whole<D, ROWS>(tile, x + (int64_t)row0 * stride + (int64_t)h * D, stride, lane_off);
+        tile_copy_async_whole<D, ROWS, NW>(tile, x + (int64_t)row0 * stride + (int64_t)h * D, stride, lane_off);
     } else {
-        tile_copy_async<D, ROWS>(tile, 4, [&](int row) {
+        tile_copy_async<D, ROWS>(tile, NW, [&](int row) {
             return x + min((int64_t)(row0 + row), T - 1) * stride + (int64_t)h * D;
         });
     }

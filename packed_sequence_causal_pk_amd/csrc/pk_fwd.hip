@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets bounds live in SGPRs
     const int n32 = lane & 31, hb = lane >> 5;
-    const int r = blockIdx.x / a.hq, h = blockIdx.x % a.hq;
+    int r, h;
+    item_head_of_block(blockIdx.x, a.hq, a.hkv, r, h);
     const int kvh = h / a.group;
     const int32_t *it = a.items + (int64_t)r * PK_ITEM_FIELDS;
     if (a.hdr[0] != 0) {
