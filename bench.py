@@ -10,9 +10,12 @@ Prints ONE JSON line.  `value` is algorithmic fwd+bwd TFLOP/s over the timed ste
 (4*hq*d*P + 10*hq*d*P per layer, P = kept query/key pairs), `roofline` reports the dominant
 kernel (the backward) against the chip's dense 16-bit matrix peak, timed per launch with HIP
 events recorded by the library on its stream, and `cpu_baseline` times the float64 CPU oracle on
-a bounded sample of the same workload.
+a bounded sample of the same workload.  `other_workloads` adds short runs (3 steps) of the other
+seeded packs with their arithmetic intensity and the fraction of the attainable roofline
+min(peak, intensity x HBM bandwidth) they reach.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen14b] [--no-cpu-baseline]
+                    [--no-sweep]
 """
 from __future__ import annotations
 
@@ -27,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "packed causal attn fwd+bwd TFLOP/s + tokens/s per layer; % bf16 MFMA peak"
 PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 matrix peak (256 CUs x 4096 flop/clk x 2.4 GHz)
+MEASURED_MFMA_TFLOPS = 2440.5   # v_mfma_f32_32x32x16_f16 microbenchmark on the same part (8 waves/CU)
 HBM_GBS = 8000.0
 
 
@@ -37,6 +41,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="qwen14b")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the short runs of the other packs reported under other_workloads")
     p.add_argument("--cpu-target-s", type=float, default=15.0,
                    help="approximate CPU seconds for the oracle sample")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -101,7 +107,7 @@ def cpu_baseline(w, lengths, target_s):
             O.attn_bwd(q[idx], k[idx], v[idx], do[idx], [n], w.softmax_scale, w.rope_base,
                        kv_heads=[kvh])
             done_s += time.perf_counter() - t0
-            f, b = O.attn_flops([n], w.group, w.head_dim)
+            f, b = attn_flops([n], w.group, w.head_dim)
             done_flops += f + b
             chosen.append((kvh, int(n)))
             if done_s >= target_s:
@@ -120,21 +126,31 @@ def cpu_baseline(w, lengths, target_s):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: the path is a single-GPU kernel (see the design notes "
-              "for how it would shard); --gpus %d is not supported" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+def attn_flops(lengths, hq, d):
+    """Algorithmic FLOPs of one layer over the kept (query, key) pairs P = sum n(n+1)/2:
+    forward 2 products (4 hq d P), backward 5 products (10 hq d P, S recomputed once)."""
+    pairs = sum(int(n) * (int(n) + 1) // 2 for n in lengths)
+    return 4 * hq * d * pairs, 10 * hq * d * pairs
 
+
+def min_bytes(w, T):
+    """Compulsory HBM bytes of one layer: forward reads q, k, v and writes out, lse; backward reads
+    q, k, v, out, dout, lse and writes fp32 dq, dk, dv."""
+    qkv = 2 * T * w.head_dim * (w.hq + 2 * w.hkv)
+    fwd = qkv + 2 * T * w.hq * w.head_dim + 4 * T * w.hq
+    bwd = qkv + 4 * T * w.hq * w.head_dim + 4 * T * w.hq + 4 * T * w.head_dim * (w.hq + 2 * w.hkv)
+    return fwd + bwd
+
+
+def measure(name, steps, warmup, calibrate_mib=0):
+    """Time `steps` steps (after `warmup`) of one workload; returns the timings and shapes."""
     import torch
 
     import packed_sequence_causal_pk_amd as pk
-    from oracle import pk_oracle as O
     from packed_sequence_causal_pk_amd import synth
 
-    w = synth.WORKLOADS[args.workload]
-    lengths = synth.pack_lengths(args.workload)
+    w = synth.WORKLOADS[name]
+    lengths = synth.pack_lengths(name)
     T, L = w.total_tokens, w.layers
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -158,8 +174,8 @@ def main():
     ws_f = pk.fwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
     ws_b = pk.bwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
     meta0.close()
-    if args.calibrate_copy_mib > 0:
-        nbytes = args.calibrate_copy_mib << 20
+    if calibrate_mib > 0:
+        nbytes = calibrate_mib << 20
         src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(2):
@@ -168,7 +184,7 @@ def main():
         print("bench: calibration copy of %d bytes done twice" % nbytes, file=sys.stderr, flush=True)
         del src, dst
     torch.cuda.synchronize()
-    print("bench: %s, T=%d, %d layers, hq/hkv/d=%d/%d/%d" % (args.workload, T, L, w.hq, w.hkv, w.head_dim),
+    print("bench: %s, T=%d, %d layers, hq/hkv/d=%d/%d/%d" % (name, T, L, w.hq, w.hkv, w.head_dim),
           file=sys.stderr, flush=True)
 
     def step():
@@ -181,10 +197,10 @@ def main():
                         w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws_b)
         return meta
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    print("bench: warmup done", file=sys.stderr, flush=True)
+    print("bench: %s warmup done" % name, file=sys.stderr, flush=True)
 
     pk.prof_reset()
     pk.prof_enable(True)
@@ -192,43 +208,79 @@ def main():
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
-    metas = [step() for _ in range(args.steps)]
+    metas = [step() for _ in range(steps)]
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     pk.prof_enable(False)
     del metas
-    step_ms = ev0.elapsed_time(ev1) / args.steps
+    step_ms = ev0.elapsed_time(ev1) / steps
     kern = {}
-    for name in ("meta", "fwd_prep", "fwd", "bwd_prep", "bwd", "bwd_dq"):
-        ms, n = pk.prof_query(name)
-        kern[name] = {"total_ms": ms, "launches": n, "avg_us": 1000.0 * ms / max(n, 1)}
-    print("bench: timed %d steps, %.2f ms/step (wall %.2f s)" % (args.steps, step_ms, wall),
+    for kn in ("meta", "fwd_prep", "fwd", "bwd_prep", "bwd", "bwd_dq"):
+        ms, n = pk.prof_query(kn)
+        kern[kn] = {"total_ms": ms, "launches": n, "avg_us": 1000.0 * ms / max(n, 1)}
+    print("bench: %s timed %d steps, %.2f ms/step (wall %.2f s)" % (name, steps, step_ms, wall),
           file=sys.stderr, flush=True)
-
-    fwd_flops, bwd_flops = O.attn_flops(lengths, w.hq, w.head_dim)
+    del layers, dq, dk, dv, ws_f, ws_b
+    torch.cuda.empty_cache()
+    fwd_flops, bwd_flops = attn_flops(lengths, w.hq, w.head_dim)
     layer_ms = step_ms / L
-    tflops = (fwd_flops + bwd_flops) * L / (step_ms * 1e-3) / 1e12
+    return {"w": w, "lengths": lengths, "T": T, "L": L, "steps": steps, "step_ms": step_ms,
+            "layer_ms": layer_ms, "kern": kern, "fwd_flops": fwd_flops, "bwd_flops": bwd_flops,
+            "tflops": (fwd_flops + bwd_flops) * L / (step_ms * 1e-3) / 1e12}
+
+
+def summary(m):
+    """Per-layer figures of one measured workload."""
+    k, steps, L = m["kern"], m["steps"], m["L"]
+    fwd_ms = (k["fwd_prep"]["total_ms"] + k["fwd"]["total_ms"]) / steps / L
+    bwd_ms = (k["bwd_prep"]["total_ms"] + k["bwd"]["total_ms"] + k["bwd_dq"]["total_ms"]) / steps / L
+    ai = (m["fwd_flops"] + m["bwd_flops"]) / min_bytes(m["w"], m["T"])
+    attainable = min(PEAK_TFLOPS, ai * HBM_GBS / 1000.0)
+    return {
+        "tflops": round(m["tflops"], 2),
+        "pct_bf16_peak": round(100.0 * m["tflops"] / PEAK_TFLOPS, 2),
+        "pct_measured_mfma_peak": round(100.0 * m["tflops"] / MEASURED_MFMA_TFLOPS, 2),
+        "tokens_per_s_per_layer": round(m["T"] / (m["layer_ms"] * 1e-3), 1),
+        "ms_per_layer_fwd_bwd": round(m["layer_ms"], 4),
+        "ms_per_layer_fwd": round(fwd_ms, 4),
+        "fwd_tflops": round(m["fwd_flops"] / (fwd_ms * 1e-3) / 1e12, 2),
+        "ms_per_layer_bwd": round(bwd_ms, 4),
+        "bwd_tflops": round(m["bwd_flops"] / (bwd_ms * 1e-3) / 1e12, 2),
+        "arithmetic_intensity_flop_per_byte": round(ai, 1),
+        "attainable_tflops": round(attainable, 1),
+        "frac_of_attainable": round(m["tflops"] / attainable, 4),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path is a single-GPU kernel (see the design notes "
+              "for how it would shard); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    m = measure(args.workload, args.steps, args.warmup, args.calibrate_copy_mib)
+    w, lengths, T, L, kern = m["w"], m["lengths"], m["T"], m["L"], m["kern"]
+    s = summary(m)
+
     # algorithmic FLOPs of each attention kernel over the kept pairs P: the forward's 2 products;
     # the key-outer backward's S, dP, dV, dK (4 products); the query-outer backward's dQ product
     # (its recomputed S and dP are counted once already, in the key-outer kernel)
-    unit = fwd_flops // 2
+    unit = m["fwd_flops"] // 2
     algo = {"fwd": 2 * unit, "bwd": 4 * unit, "bwd_dq": unit}
     achieved = {k: algo[k] / (kern[k]["avg_us"] * 1e-6) / 1e12 for k in algo}
     dominant = max(algo, key=lambda k: kern[k]["avg_us"])
-    per_layer_fwd_ms = (kern["fwd_prep"]["total_ms"] + kern["fwd"]["total_ms"]) / args.steps / L
-    per_layer_bwd_ms = (kern["bwd_prep"]["total_ms"] + kern["bwd"]["total_ms"]
-                        + kern["bwd_dq"]["total_ms"]) / args.steps / L
     kernel_names = {"fwd": "k_attn_fwd (forward)", "bwd": "k_attn_bwd_kv (backward dK, dV)",
                     "bwd_dq": "k_attn_bwd_q (backward dQ)"}
     result = {
         "metric": METRIC,
-        "value": round(tflops, 2),
+        "value": s["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
+        "ms_per_step": round(m["step_ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -240,11 +292,14 @@ def main():
             "layers": L, "step": "build meta once + %d layer forwards + %d layer backwards" % (L, L),
             "io_dtypes": "q/k/v/out/dout bf16, lse/dq/dk/dv fp32",
         },
-        "tokens_per_s_per_layer": round(T / (layer_ms * 1e-3), 1),
-        "pct_bf16_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
-        "ms_per_layer_fwd_bwd": round(layer_ms, 4),
-        "ms_per_layer_fwd": round(per_layer_fwd_ms, 4),
-        "ms_per_layer_bwd": round(per_layer_bwd_ms, 4),
+        "tokens_per_s_per_layer": s["tokens_per_s_per_layer"],
+        "pct_bf16_peak": s["pct_bf16_peak"],
+        "pct_measured_mfma_peak": s["pct_measured_mfma_peak"],
+        "ms_per_layer_fwd_bwd": s["ms_per_layer_fwd_bwd"],
+        "ms_per_layer_fwd": s["ms_per_layer_fwd"],
+        "fwd_tflops": s["fwd_tflops"],
+        "ms_per_layer_bwd": s["ms_per_layer_bwd"],
+        "bwd_tflops": s["bwd_tflops"],
         "build_meta_us": round(kern["meta"]["avg_us"], 2),
         "kernels_avg_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "kernels_algorithmic_tflops": {k: round(v, 2) for k, v in achieved.items()},
@@ -255,6 +310,14 @@ def main():
             "traffic": measured_traffic() if dominant == "bwd" else None,
         },
     }
+    if not args.no_sweep:
+        # the other packs, a few steps each (their own figures; `value` is the workload above)
+        other = {}
+        for name in ("tiny", "llama1b", "qwen06b", "qwen14b", "skewed"):
+            if name == args.workload:
+                continue
+            other[name] = summary(measure(name, 3, 1))
+        result["other_workloads"] = other
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, lengths, args.cpu_target_s)

@@ -16,8 +16,8 @@
 // reduces max|dout| (k_bwd_dmax); k_bwd_scale turns it into a power of two sigma with
 // max|dout| * sigma in [1, 2), so the backward's fp16 gradient operands (dout and dS, both scaled
 // by sigma, unscaled exactly at the end) stay inside fp16's range whatever the magnitude of the
-// incoming gradient.  k_bwd_prep then writes sigma * dout, sigma * rowsum(dout * out) and
-// lse * log2(e) next to the rotated tensors.
+// incoming gradient.  k_rope_table writes the (cos, sin) table and k_bwd_rows then writes the
+// rotated Q and K, V and sigma * dout in fp16, sigma * rowsum(dout * out) and lse * log2(e).
 //
 // Thread layout of the two per-token kernels: one thread per (token t, group c of 4 rotation pairs);
 // the thread owns elements d in [4c, 4c+4) and their partners d + D/2 for every head, so each
@@ -138,9 +138,41 @@ __device__ __forceinline__ void store4s(f16 *p, const float x[4], float scale) {
     store4(p, y);
 }
 
+// The (cos, sin) table alone: one thread per (token, group of 4 rotation pairs).
 template <int D>
-__global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ pos, int64_t T,
-                                                  int hq, int hkv, float base,
+__global__ __launch_bounds__(256) void k_rope_table(const int32_t *__restrict__ pos, int64_t T,
+                                                    float base, float2 *__restrict__ table) {
+    constexpr int G = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = gid / G;
+    if (t >= T) return;
+    float cs[4], sn[4];
+    rope_factors<D>(pos, t, (int)(gid % G), base, table, cs, sn);
+}
+
+// Rotation factors of pairs [8c, 8c + 8) of token t from the table.
+template <int D>
+__device__ __forceinline__ void table8(const float2 *__restrict__ table, int64_t t, int c,
+                                       float cs[8], float sn[8]) {
+    const float4 *f = reinterpret_cast<const float4 *>(table + t * (D / 2) + 8 * c);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float4 x = f[k];
+        cs[2 * k] = x.x;
+        sn[2 * k] = x.y;
+        cs[2 * k + 1] = x.z;
+        sn[2 * k + 1] = x.w;
+    }
+}
+
+// Per-row work of the backward prologue, one thread per (row, group c of 8 rotation pairs): the
+// thread owns elements [8c, 8c + 8) of a head row and their partners + D/2, read and written as
+// 16-byte vectors.  Rows [0, T * hkv) are K rows (rotated) with their V rows (converted); rows
+// [T * hkv, T * (hkv + hq)) are query-head rows: Q rotated, sigma * dout, and the row sums
+// sigma * sum(dout * out) and lse * log2(e).
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
+                                                  const float2 *__restrict__ table,
                                                   const bf16 *__restrict__ q,
                                                   const bf16 *__restrict__ k,
                                                   const bf16 *__restrict__ v,
@@ -152,43 +184,57 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const int32_t *__restrict__ po
                                                   f16 *__restrict__ krot,
                                                   f16 *__restrict__ vh,
                                                   f16 *__restrict__ dout16,
-                                                  float2 *__restrict__ table,
                                                   float *__restrict__ dsum,
                                                   float *__restrict__ lse2) {
-    constexpr int G = D / 8;
+    constexpr int G = D / 16;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t t = gid / G;
     const int c = (int)(gid % G);
-    // The G threads of a token share a wave and all exit here together, so the shuffle
-    // reduction below only mixes lanes of one token.
-    if (t >= T) return;
-    const float sigma = dscale[0];
-    float cs[4], sn[4];
-    rope_factors<D>(pos, t, c, base, table, cs, sn);
-    for (int h = 0; h < hkv; ++h) {
-        const int64_t off = (t * hkv + h) * D;
-        rotate_row<D>(k + off, krot + off, c, cs, sn);
-        convert_row<D>(v + off, vh + off, c);
-    }
-    for (int h = 0; h < hq; ++h) {
-        const int64_t off = (t * hq + h) * D;
-        rotate_row<D>(q + off, qrot + off, c, cs, sn);
-        float o1[4], o2[4], g1[4], g2[4];
-        load4(out + off + 4 * c, o1);
-        load4(out + off + D / 2 + 4 * c, o2);
-        load4(dout + off + 4 * c, g1);
-        load4(dout + off + D / 2 + 4 * c, g2);
-        store4s(dout16 + off + 4 * c, g1, sigma);
-        store4s(dout16 + off + D / 2 + 4 * c, g2, sigma);
-        float part = 0.f;
+    int64_t row = gid / G;
+    const int64_t nkv = T * hkv;
+    float cs[8], sn[8];
+    auto rotate = [&](const bf16 *src, f16 *dst) {
+        const bf16x8 x1 = pkd::load_bf16x8(src + 8 * c), x2 = pkd::load_bf16x8(src + D / 2 + 8 * c);
+        f16x8 y1, y2;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) part += o1[kk] * g1[kk] + o2[kk] * g2[kk];
-#pragma unroll
-        for (int s = G / 2; s > 0; s >>= 1) part += __shfl_xor(part, s, 64);
-        if (c == 0) {
-            dsum[(int64_t)h * T + t] = part * sigma;
-            lse2[(int64_t)h * T + t] = lse[(int64_t)h * T + t] * pkd::kLog2e;
+        for (int e = 0; e < 8; ++e) {
+            const float a1 = (float)x1[e], a2 = (float)x2[e];
+            y1[e] = (f16)(a1 * cs[e] - a2 * sn[e]);
+            y2[e] = (f16)(a2 * cs[e] + a1 * sn[e]);
         }
+        pkd::store_f16x8(dst + 8 * c, y1);
+        pkd::store_f16x8(dst + D / 2 + 8 * c, y2);
+    };
+    if (row < nkv) {
+        table8<D>(table, row / hkv, c, cs, sn);
+        const int64_t off = row * D;
+        rotate(k + off, krot + off);
+        pkd::store_f16x8(vh + off + 8 * c, pkd::bf16x8_to_f16x8(pkd::load_bf16x8(v + off + 8 * c)));
+        pkd::store_f16x8(vh + off + D / 2 + 8 * c,
+                         pkd::bf16x8_to_f16x8(pkd::load_bf16x8(v + off + D / 2 + 8 * c)));
+        return;
+    }
+    row -= nkv;
+    // The G threads of a row are consecutive lanes of one wave and exit together, so the
+    // shuffle reduction below only mixes lanes of one row.
+    if (row >= T * hq) return;
+    const int64_t t = row / hq;
+    const int h = (int)(row % hq);
+    table8<D>(table, t, c, cs, sn);
+    const int64_t off = row * D;
+    rotate(q + off, qrot + off);
+    const float sigma = dscale[0];
+    const bf16x8 o1 = pkd::load_bf16x8(out + off + 8 * c), o2 = pkd::load_bf16x8(out + off + D / 2 + 8 * c);
+    const bf16x8 g1 = pkd::load_bf16x8(dout + off + 8 * c), g2 = pkd::load_bf16x8(dout + off + D / 2 + 8 * c);
+    pkd::store_f16x8(dout16 + off + 8 * c, pkd::bf16x8_to_f16x8(g1, sigma));
+    pkd::store_f16x8(dout16 + off + D / 2 + 8 * c, pkd::bf16x8_to_f16x8(g2, sigma));
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part += (float)o1[e] * (float)g1[e] + (float)o2[e] * (float)g2[e];
+#pragma unroll
+    for (int sh = G / 2; sh > 0; sh >>= 1) part += __shfl_xor(part, sh, 64);
+    if (c == 0) {
+        dsum[(int64_t)h * T + t] = part * sigma;
+        lse2[(int64_t)h * T + t] = lse[(int64_t)h * T + t] * pkd::kLog2e;
     }
 }
 
@@ -251,17 +297,21 @@ hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, cons
     if (e != hipSuccess) return e;
     k_bwd_scale<<<1, 256, 0, s>>>(blockmax, (int)nb, scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const unsigned g = prep_blocks(r.T, r.d);
-    if (r.d == 128)
-        k_bwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
+    const unsigned gt = prep_blocks(r.T, r.d);
+    const unsigned gr = (unsigned)((r.T * (r.hq + r.hkv) * (r.d / 16) + 255) / 256);
+    if (r.d == 128) {
+        k_rope_table<128><<<gt, 256, 0, s>>>(r.pos, r.T, r.rope_base, (float2 *)rope);
+        k_bwd_rows<128><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
+                                            (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
+                                            (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
+                                            (f16 *)vh, (f16 *)dout16, dsum, lse2);
+    } else {
+        k_rope_table<64><<<gt, 256, 0, s>>>(r.pos, r.T, r.rope_base, (float2 *)rope);
+        k_bwd_rows<64><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
                                            (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
                                            (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
-                                           (f16 *)vh, (f16 *)dout16, (float2 *)rope, dsum, lse2);
-    else
-        k_bwd_prep<64><<<g, 256, 0, s>>>(r.pos, r.T, r.hq, r.hkv, r.rope_base, (const bf16 *)q,
-                                          (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
-                                          (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
-                                          (f16 *)vh, (f16 *)dout16, (float2 *)rope, dsum, lse2);
+                                           (f16 *)vh, (f16 *)dout16, dsum, lse2);
+    }
     return hipGetLastError();
 }
 
