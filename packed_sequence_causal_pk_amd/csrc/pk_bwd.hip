@@ -503,46 +503,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
         const char *tk = reinterpret_cast<const char *>(lds_k[BUF]);
         const char *tv = reinterpret_cast<const char *>(lds_v[BUF]);
 
-        // S^T = K Q^T and dP^T = V dO^T (keys x queries), key rows in row_perm order
-        f32x16 sc[NMB], dp[NMB];
+        // per 32-key block mb: S^T = K Q^T and dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-            sc[mb] = zero_f32x16();
-            dp[mb] = zero_f32x16();
-        }
+            f32x16 sc = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                sc[mb] = mfma32(*reinterpret_cast<const f16x8 *>(tk + aoff[kk] + 64 * D * mb), qf[kk], sc[mb]);
-                dp[mb] = mfma32(*reinterpret_cast<const f16x8 *>(tv + aoff[kk] + 64 * D * mb), gf[kk], dp[mb]);
+            for (int kk = 0; kk < NKK; ++kk) {
+                sc = mfma32(*reinterpret_cast<const f16x8 *>(tk + aoff[kk] + 64 * D * mb), qf[kk], sc);
+                dp = mfma32(*reinterpret_cast<const f16x8 *>(tv + aoff[kk] + 64 * D * mb), gf[kk], dp);
             }
-        if (need_mask) {  // uniform branch: boundary / diagonal tiles only
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb)
+            if (need_mask) {
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
                     const int jj = k0 + 32 * mb + row_perm(acc_row(rr, hb));
                     const bool keep = qvalid & (jj >= lo_i) & (jj <= i);
-                    sc[mb][rr] = keep ? sc[mb][rr] : -INFINITY;
+                    sc[rr] = keep ? sc[rr] : -INFINITY;
                 }
-        }
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const float p = fast_exp2(fmaf(sc[mb][rr], sl2, -lse2));
-                dp[mb][rr] = p * (dp[mb][rr] - dd);
             }
-        }
-        // dQ^T (d x queries) += K^T (d x keys) * dS^T (keys x queries); K^T read transposed
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 f16x8 sb;
 #pragma unroll
-                for (int x = 0; x < 8; ++x) sb[x] = (f16)dp[mb][8 * e + x];
+                for (int x = 0; x < 8; ++x) {
+                    const float p = fast_exp2(fmaf(sc[8 * e + x], sl2, -lse2));
+                    sb[x] = (f16)(p * (dp[8 * e + x] - dd));
+                }
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
                     acc[db] = mfma32(tile_tr_at(tk, toff[db], 2 * D * (32 * mb + 16 * e)), sb, acc[db]);
