@@ -142,9 +142,12 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
 const char *pk_status_str(pk_status status);
 
 /* ---- Kernel timing (for benchmarks; off by default) -------------------------------------
- * While enabled, every launch of the library records a pair of HIP events around it on its
- * stream (no synchronisation).  pk_prof_query synchronises on the recorded events and returns
- * the total milliseconds and launch count of one kernel kind since the last reset. */
+ * pk_prof_enable(kinds) takes a bit mask of kernel kinds (bit k = kind k, PK_PROF_ALL for all,
+ * 0 to stop; other values: PK_ERR_INVALID).  While a kind is enabled, each of its launches
+ * records a pair of HIP events around it on its stream (no synchronisation; each record costs
+ * a few microseconds of GPU time, so enable only the kinds to be timed).  pk_prof_query
+ * synchronises on the recorded events and returns the total milliseconds and launch count of
+ * one kernel kind since the last reset. */
 typedef enum pk_kernel_kind {
     PK_K_META = 0,        /* all metadata-build kernels of one pk_build_meta */
     PK_K_FWD_PREP = 1,    /* forward prologue: RoPE table + rotated K */
@@ -154,8 +157,9 @@ typedef enum pk_kernel_kind {
     PK_K_BWD_DQ = 5,      /* backward attention, query-tile outer: dQ */
     PK_K_COUNT = 6
 } pk_kernel_kind;
+#define PK_PROF_ALL ((1 << PK_K_COUNT) - 1)
 
-pk_status pk_prof_enable(int32_t on);
+pk_status pk_prof_enable(int32_t kinds);
 pk_status pk_prof_reset(void);
 pk_status pk_prof_query(int32_t kind, double *total_ms /* host */, int64_t *launches /* host */);
 

@@ -190,8 +190,13 @@ def attn_bwd(meta: PackedMeta, q, k, v, out, lse, dout, softmax_scale: Optional[
     return dq, dk, dv
 
 
-def prof_enable(on: bool = True) -> None:
-    _lib.check("pk_prof_enable", lib().pk_prof_enable(1 if on else 0))
+def prof_enable(on: bool = True, kinds=None) -> None:
+    """Record HIP events around launches of the given kernel kinds (names of KERNEL_KINDS;
+    all when None), or stop recording (on=False)."""
+    mask = 0
+    if on:
+        mask = _lib.PK_PROF_ALL if kinds is None else sum(1 << _lib.KERNEL_KINDS[k] for k in set(kinds))
+    _lib.check("pk_prof_enable", lib().pk_prof_enable(mask))
 
 
 def prof_reset() -> None:

@@ -20,6 +20,7 @@ PK_META_BAD_TOTAL = 2
 PK_K_META, PK_K_FWD_PREP, PK_K_FWD, PK_K_BWD_PREP, PK_K_BWD, PK_K_BWD_DQ = range(6)
 KERNEL_KINDS = {"meta": PK_K_META, "fwd_prep": PK_K_FWD_PREP, "fwd": PK_K_FWD,
                 "bwd_prep": PK_K_BWD_PREP, "bwd": PK_K_BWD, "bwd_dq": PK_K_BWD_DQ}
+PK_PROF_ALL = (1 << len(KERNEL_KINDS)) - 1
 
 # every function pk.h declares, with (restype, argtypes)
 _vp = ctypes.c_void_p

@@ -27,7 +27,7 @@ struct ProfRecord {
     hipEvent_t start, stop;
 };
 struct Prof {
-    bool on = false;
+    uint32_t mask = 0;              // bit k: record launches of kernel kind k
     std::vector<hipEvent_t> pool;   // created once, reused after a reset
     std::vector<ProfRecord> recs;
     size_t used = 0;
@@ -39,7 +39,7 @@ struct ProfScope {
     ProfRecord *rec = nullptr;
     hipStream_t stream;
     ProfScope(int kind, hipStream_t s) : stream(s) {
-        if (!g_prof.on || g_prof.used >= kProfCapacity) return;
+        if (!((g_prof.mask >> kind) & 1u) || g_prof.used >= kProfCapacity) return;
         ProfRecord r;
         r.kind = kind;
         r.start = g_prof.pool[2 * g_prof.used];
@@ -276,8 +276,9 @@ const char *pk_status_str(pk_status status) {
     return "unknown status";
 }
 
-pk_status pk_prof_enable(int32_t on) {
-    if (on && g_prof.pool.empty()) {
+pk_status pk_prof_enable(int32_t kinds) {
+    if (kinds < 0 || kinds > PK_PROF_ALL) return PK_ERR_INVALID;
+    if (kinds && g_prof.pool.empty()) {
         g_prof.pool.resize(2 * kProfCapacity);
         for (auto &ev : g_prof.pool)
             if (hipEventCreate(&ev) != hipSuccess) {
@@ -286,7 +287,7 @@ pk_status pk_prof_enable(int32_t on) {
             }
         g_prof.recs.reserve(kProfCapacity);
     }
-    g_prof.on = on != 0;
+    g_prof.mask = (uint32_t)kinds;
     return PK_OK;
 }
 

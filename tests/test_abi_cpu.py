@@ -74,6 +74,9 @@ def test_status_strings_and_profiler_queries(lib):
     assert _lib.status_str(-99) == "unknown status"
     ms, n = ctypes.c_double(1.0), ctypes.c_int64(1)
     assert lib.pk_prof_query(99, ctypes.byref(ms), ctypes.byref(n)) == _lib.PK_ERR_INVALID
+    assert lib.pk_prof_enable(-1) == _lib.PK_ERR_INVALID
+    assert lib.pk_prof_enable(_lib.PK_PROF_ALL + 1) == _lib.PK_ERR_INVALID
+    assert lib.pk_prof_enable(0) == 0
     assert lib.pk_prof_reset() == 0
     assert lib.pk_prof_query(_lib.PK_K_FWD, ctypes.byref(ms), ctypes.byref(n)) == 0
     assert ms.value == 0.0 and n.value == 0
