@@ -260,27 +260,38 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
                         const bool keep = (r8 + x < nrows) & (j >= i - p8[x]) & (j <= i);  // no short circuit
                         sv = keep ? sv : -INFINITY;
                     }
-                    const float p = fast_exp2(fmaf(sv, sl2, -lv[x]));
-                    sp[hf][8 * e + x] = p;
-                    pb[hf][e][x] = (f16)p;
+                    sp[hf][8 * e + x] = fast_exp2(fmaf(sv, sl2, -lv[x]));
                 }
                 xp[(2 * e) * 64] = make_float4(sp[hf][8 * e], sp[hf][8 * e + 1], sp[hf][8 * e + 2], sp[hf][8 * e + 3]);
                 xp[(2 * e + 1) * 64] = make_float4(sp[hf][8 * e + 4], sp[hf][8 * e + 5], sp[hf][8 * e + 6], sp[hf][8 * e + 7]);
             }
         };
         // dS waves: dS = P (dP - D) with P from the P waves, as fp16 operands
-        auto dscore = [&](int hf) __attribute__((always_inline)) {
-            const float4 *xp = reinterpret_cast<const float4 *>(&sm.xp[w][hf][0][lane][0]);
+        auto dsub = [&](int hf) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int r8 = 32 * hf + 16 * e + 8 * hb;
                 float dv[8];
                 lds_row8(&sm.dd[BUF][r8], dv);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) sp[hf][8 * e + x] -= dv[x];
+            }
+        };
+        auto dscore = [&](int hf) __attribute__((always_inline)) {
+            const float4 *xp = reinterpret_cast<const float4 *>(&sm.xp[w][hf][0][lane][0]);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
                 const float4 p0 = xp[(2 * e) * 64], p1 = xp[(2 * e + 1) * 64];
                 const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-                for (int x = 0; x < 8; ++x) pb[hf][e][x] = (f16)(pv[x] * (sp[hf][8 * e + x] - dv[x]));
+                for (int x = 0; x < 8; ++x) pb[hf][e][x] = (f16)(pv[x] * sp[hf][8 * e + x]);
             }
+        };
+        auto pconv = [&](int hf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int x = 0; x < 8; ++x) pb[hf][e][x] = (f16)sp[hf][8 * e + x];
         };
         // the second product of half hf: dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves);
         // queries are the k dimension and the transposed operand comes straight from the tile
@@ -311,13 +322,19 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
             if (p_role) {
                 softmax(0, false);
                 softmax(1, false);
+            } else {
+                dsub(0);
+                dsub(1);
             }
         } else {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 if (!run[hf]) continue;
                 scores(hf);
-                if (p_role) softmax(hf, masked[hf]);
+                if (p_role)
+                    softmax(hf, masked[hf]);
+                else
+                    dsub(hf);
             }
         }
         __syncthreads();   // B1: P of both halves is in LDS
@@ -325,8 +342,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
             if (!p_role) {
                 dscore(0);
                 dscore(1);
-                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                pconv(0);
+                pconv(1);
             }
+            __builtin_amdgcn_sched_barrier(0);
             grads(0);
             grads(1);
             __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);         // 4 transposed operands ahead
@@ -340,7 +360,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 if (!run[hf]) continue;
-                if (!p_role) dscore(hf);
+                if (!p_role)
+                    dscore(hf);
+                else
+                    pconv(hf);
                 grads(hf);
             }
         }
