@@ -38,7 +38,7 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="qwen14b")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true",
@@ -145,7 +145,7 @@ def min_bytes(w, T):
 KINDS = ("meta", "fwd_prep", "fwd", "bwd_prep", "bwd", "bwd_dq")
 
 
-def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=()):
+def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False):
     """Time `steps` steps (after `warmup`) of one workload, timing the kernel kinds
     `timed_kinds` inside that region; a second, shorter pass times every kind for the
     per-kernel breakdown.  Returns the timings and shapes."""
@@ -202,12 +202,25 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=()):
                         w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws_b)
         return meta
 
+    def step_uncached():
+        # the same step with the metadata rebuilt for every layer call (no reuse across layers)
+        metas = []
+        for x in layers:
+            metas.append(pk.build_meta(lengths_d, T))
+            pk.attn_fwd(metas[-1], x["q"], x["k"], x["v"], w.softmax_scale, w.rope_base,
+                        out=x["out"], lse=x["lse"], workspace=ws_f)
+        for x in reversed(layers):
+            metas.append(pk.build_meta(lengths_d, T))
+            pk.attn_bwd(metas[-1], x["q"], x["k"], x["v"], x["out"], x["lse"], x["do"],
+                        w.softmax_scale, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        return metas
+
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     print("bench: %s warmup done" % name, file=sys.stderr, flush=True)
 
-    def timed(n, kinds):
+    def timed(n, kinds, fn=step):
         """n steps bracketed by events on the stream; the library times the given kernel kinds
         with its own event pairs (each pair costs a few microseconds, so only what is needed)."""
         pk.prof_reset()
@@ -216,7 +229,7 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=()):
         t0 = time.perf_counter()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        metas = [step() for _ in range(n)]
+        metas = [fn() for _ in range(n)]
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -235,12 +248,17 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=()):
     # a second pass times every kernel kind (for the per-kernel breakdown only)
     nb = max(2, steps // 2)
     bd_ms, _, kern = timed(nb, list(KINDS))
+    uncached_ms = None
+    if uncached:
+        for _ in range(2):
+            step_uncached()
+        uncached_ms, _, _ = timed(steps, (), fn=step_uncached)
     del layers, dq, dk, dv, ws_f, ws_b
     torch.cuda.empty_cache()
     fwd_flops, bwd_flops = attn_flops(lengths, w.hq, w.head_dim)
     layer_ms = step_ms / L
     return {"w": w, "lengths": lengths, "T": T, "L": L, "steps": nb, "step_ms": step_ms,
-            "main_kern": main_kern,
+            "main_kern": main_kern, "uncached_step_ms": uncached_ms,
             "layer_ms": layer_ms, "kern": kern, "fwd_flops": fwd_flops, "bwd_flops": bwd_flops,
             "tflops": (fwd_flops + bwd_flops) * L / (step_ms * 1e-3) / 1e12}
 
@@ -265,6 +283,11 @@ def summary(m):
         "arithmetic_intensity_flop_per_byte": round(ai, 1),
         "attainable_tflops": round(attainable, 1),
         "frac_of_attainable": round(m["tflops"] / attainable, 4),
+        **({} if m["uncached_step_ms"] is None else {
+            "uncached_ms_per_step": round(m["uncached_step_ms"], 4),
+            "cached_ms_per_step": round(m["step_ms"], 4),
+            "saved_ms_per_step": round(m["uncached_step_ms"] - m["step_ms"], 4),
+            "meta_rebuilds_per_uncached_step": 2 * m["L"]}),
     }
 
 
@@ -336,7 +359,11 @@ def main():
         for name in ("tiny", "llama1b", "qwen06b", "qwen14b", "skewed"):
             if name == args.workload:
                 continue
-            other[name] = summary(measure(name, 3, 1))
+            # 20 timed steps on the small packs, 5 on the large ones; the multi-layer small
+            # packs also run with the metadata rebuilt per layer call (the uncached mode)
+            small = name in ("tiny", "llama1b", "qwen06b")
+            other[name] = summary(measure(name, 20 if small else 5, 3,
+                                          uncached=name in ("llama1b", "qwen06b")))
         result["other_workloads"] = other
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
