@@ -64,7 +64,7 @@ __device__ void fwd_zero_tile(const FwdArgs &a, int tile, int h) {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
-    constexpr int BK = 64;        // keys per LDS tile
+    constexpr int BK = 32;        // keys per LDS tile
     constexpr int NKK = D / 16;   // k-steps of the score product
     constexpr int NDB = D / 32;   // 32-row blocks of O^T
     constexpr int NMB = BK / 32;  // 32-key blocks per tile
