@@ -238,3 +238,55 @@ def test_autograd_function():
     compare("dq", to_np(tq.grad), dq_ref)
     compare("dk", to_np(tk.grad), dk_ref)
     compare("dv", to_np(tv.grad), dv_ref)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_max_tokens_sampled(d):
+    """A pack of the largest supported size (PK_MAX_TOKENS tokens, lengths U[1, 2048] with every
+    50th sequence of length 1): every
+    64-bit offset and tile index is exercised.  Inputs are seeded N(0,1) tensors drawn on the
+    device and rounded to bf16; a few whole sequences (the first, a long one, the last, and short
+    ones) are copied back and checked against the oracle, and every length-1 sequence of the
+    pack against the closed forms O = V, dQ = dK = 0."""
+    t = 1 << 20   # PK_MAX_TOKENS
+    rng = np.random.default_rng(11)
+    lengths, acc = [], 0
+    while acc < t:
+        x = 1 if len(lengths) % 50 == 25 else int(rng.integers(1, 2048, endpoint=True))
+        lengths.append(x)
+        acc += x
+    lengths[-1] -= acc - t
+    lengths = np.asarray(lengths, np.int32)
+    hq, hkv = 4, 1
+    say("max-size pack: T", t, "sequences", len(lengths), "hq/hkv/d", hq, hkv, d)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234 + d)
+    mk = lambda *s: torch.randn(*s, generator=g, device="cuda").bfloat16()
+    q, k, v, do = mk(t, hq, d), mk(t, hkv, d), mk(t, hkv, d), mk(t, hq, d)
+    meta = pk.build_meta(torch.tensor(lengths, device="cuda"), t)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = pk.attn_fwd(meta, q, k, v, scale)
+    dq, dk, dv = pk.attn_bwd(meta, q, k, v, out, lse, do, scale)
+    torch.cuda.synchronize()
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    longest = int(np.argmax(lengths))
+    seqs = sorted({0, longest, len(lengths) - 1} | set(np.flatnonzero(lengths <= 8)[:20].tolist()))
+    sub_len, idx = _sub_pack(lengths, seqs)
+    tidx = torch.tensor(idx, device="cuda")
+    host = lambda x: x.index_select(0, tidx).float().cpu().numpy().astype(np.float32)
+    qs, ks, vs, dos = host(q), host(k), host(v), host(do)
+    o_ref, lse_ref = O.attn_fwd(qs, ks, vs, sub_len, scale, 1e4)
+    dq_ref, dk_ref, dv_ref = O.attn_bwd(qs, ks, vs, dos, sub_len, scale, 1e4)
+    compare("out", host(out).astype(np.float64), o_ref)
+    compare("lse", lse.index_select(1, tidx).cpu().numpy().astype(np.float64), lse_ref, max_abs=LSE_MAX_ABS)
+    compare("dq", host(dq).astype(np.float64), dq_ref)
+    compare("dk", host(dk).astype(np.float64), dk_ref)
+    compare("dv", host(dv).astype(np.float64), dv_ref)
+    ones = torch.tensor(cu[:-1][lengths == 1], device="cuda")
+    say("length-1 sequences", len(ones))
+    if len(ones):
+        gmap = torch.arange(hq, device="cuda") // (hq // hkv)
+        compare("out1", out.index_select(0, ones).float().cpu().numpy(),
+                v.index_select(0, ones)[:, gmap].float().cpu().numpy())
+        compare("dq1", dq.index_select(0, ones).cpu().numpy(), np.zeros((len(ones), hq, d)))
+        compare("dk1", dk.index_select(0, ones).cpu().numpy(), np.zeros((len(ones), hkv, d)))
