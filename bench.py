@@ -52,8 +52,8 @@ def parse():
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_attn_bwd_kv_qwen14b_hbm_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "packed_sequence_causal_pk_amd", "csrc", f)
-                  for f in ("pk_bwd.hip", "pk_device.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "packed_sequence_causal_pk_amd", f)
+                  for f in ("csrc/pk_bwd.hip", "csrc/pk_device.h", "build.py")]
 
 
 def kernel_source_digest():
