@@ -53,7 +53,7 @@ def parse():
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_attn_bwd_kv_qwen14b_hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "packed_sequence_causal_pk_amd", f)
-                  for f in ("csrc/pk_bwd.hip", "csrc/pk_device.h", "build.py")]
+                  for f in ("csrc/pk_bwd_kv.hip", "csrc/pk_bwd.h", "csrc/pk_device.h", "build.py")]
 
 
 def kernel_source_digest():

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpk.so")
 
-SOURCES = ["pk_api.cpp", "pk_meta.hip", "pk_rope.hip", "pk_fwd.hip", "pk_bwd.hip"]
+SOURCES = ["pk_api.cpp", "pk_meta.hip", "pk_rope.hip", "pk_fwd.hip", "pk_bwd_kv.hip", "pk_bwd_q.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -30,9 +30,10 @@ COMMON_FLAGS = [
 
 # Per-source extra flags.  The dK/dV kernel keeps two waves per SIMD busy with long dependent
 # product chains; the latency-oriented ("max-ilp") machine scheduler orders its loads and
-# products better there (measured: about 2% on the Qwen3-14B-shaped pack), while the
-# forward's three-workgroup-per-CU kernel does better with the default occupancy-oriented one.
-SOURCE_FLAGS = {"pk_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# products better there (measured: about 2% on the Qwen3-14B-shaped pack), while the forward
+# and dQ kernels do better with the default occupancy-oriented one (under max-ilp the dQ kernel
+# spills once its tile reads are issued ahead of their products).
+SOURCE_FLAGS = {"pk_bwd_kv.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def hipcc() -> str:

@@ -252,14 +252,14 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
     {
         ProfScope ps(PK_K_BWD, s);
-        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
-                           scale, w + W.rope, dq, dk, dv, 0, s);
+        e = pk::launch_bwd_kv(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
+                              scale, w + W.rope, dk, dv, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     {
         ProfScope ps(PK_K_BWD_DQ, s);
-        e = pk::launch_bwd(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
-                           scale, w + W.rope, dq, dk, dv, 1, s);
+        e = pk::launch_bwd_q(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
+                             scale, w + W.rope, dq, s);
     }
     return hip_status(e);
 }

@@ -1,0 +1,93 @@
+// Backward attention over a packed batch on gfx950 matrix cores: what the two kernels share.
+//
+// For the loss sum(out * dout) of the forward in pk_fwd.hip, with P the masked softmax,
+// D_i = sum_d dout_i * out_i (computed in the prologue pass), and scores on the rotated Q, K:
+//     dV_j     = sum over the group's heads and queries i of P_ij dout_i
+//     dS_ij    = P_ij (dout_i . v_j - D_i)
+//     dK_rot_j = scale * sum_i dS_ij q_rot_i          dQ_rot_i = scale * sum_j dS_ij k_rot_j
+// and dK, dQ are the inverse rotations of dK_rot, dQ_rot.  This is the softmax calculus of the
+// formula in [UN-2023] "Introducing Unsloth：LLM 训练提速 30 倍", "手动 Autograd" (which derives
+// its gradients by hand), applied to A = softmax(Q K^T / sqrt(d) + M) V.
+//
+// Two kernels, neither with atomics, so every gradient is written exactly once:
+//   k_attn_bwd_kv  one workgroup per backward work item (128 keys) x KV head.  The 4 waves own
+//                  32 keys each; K_rot and V of those keys are the k operands of S = Q K^T and
+//                  dP = dO V^T (v_mfma_f32_32x32x16_f16), dK^T and dV^T accumulate in registers
+//                  over every query block AND every query head of the GQA group (so the group
+//                  sum is free), and dK, dV are written once.  Query blocks of 64 rows stream
+//                  into double-buffered swizzled LDS tiles by asynchronous global->LDS copies;
+//                  the transposed operands of dV^T += dO^T P and dK^T += Q^T dS are read with
+//                  ds_read_b64_tr_b16 from the same row-major tiles.
+//   k_attn_bwd_q   one workgroup per forward work item (128 queries) x query head, laid out like
+//                  the forward: S^T = K Q^T and dP^T = V dO^T give each lane one query, so its
+//                  lse and D are per-lane scalars; dQ^T += K^T dS^T accumulates in registers and
+//                  dQ is rotated back by R(-theta) and written once.
+// Recomputing S and dP in the second kernel costs two extra products; it replaces float atomics
+// on dQ (whose throughput, about 2.6 TB/s on this part, made them slower than the recompute),
+// a zero-fill of dq and a separate inverse-rotation pass.
+//
+// Common to both: the mask is applied element-wise only on tiles that straddle a sequence
+// boundary or the diagonal, and tiles outside a wave's visible range skip their products;
+// operands are fp16 with fp32 accumulation; dout enters scaled by the power of two sigma the
+// prologue chose (max|dout| * sigma in [1, 2)), so dP and dS are sigma-scaled and the results
+// are unscaled exactly by 1/sigma when written.
+//
+// k_attn_bwd_kv lives in pk_bwd_kv.hip and k_attn_bwd_q in pk_bwd_q.hip (separate sources so
+// each can be built with the machine scheduler that suits it).
+#pragma once
+
+#include "pk_internal.h"
+#include "pk_device.h"
+
+namespace pkb {
+
+using namespace pkd;
+
+struct BwdArgs {
+    const f16 *qrot;      // [T, hq, D] fp16
+    const f16 *krot;      // [T, hkv, D] fp16
+    const f16 *v;         // [T, hkv, D] fp16 copy of v
+    const f16 *dout16;    // [T, hq, D] sigma * dout, fp16
+    const float *lse2;    // [hq, T] lse * log2(e)
+    const float *dsum;    // [hq, T] sigma * rowsum(dout * out)
+    const float *dscale;  // {sigma, 1/sigma}
+    const float2 *rope;   // [T, D/2]
+    const int32_t *items; // [n_items, 8] longest first (backward list for _kv, forward for _q)
+    const int32_t *pos;   // [T]
+    const int32_t *hdr;
+    float *dq;            // [T, hq, D]
+    float *dk;            // [T, hkv, D]
+    float *dv;            // [T, hkv, D]
+    int64_t T;
+    int hq, hkv, group;
+    float scale;
+};
+
+inline BwdArgs make_bwd_args(const pk::AttnShape &sh, const pk_meta_s &m, const void *qrot,
+                             const void *krot, const void *v, const void *dout16,
+                             const float *lse2, const float *dsum, const float *scale,
+                             const void *rope, float *dq, float *dk, float *dv) {
+    BwdArgs a;
+    a.qrot = (const f16 *)qrot;
+    a.krot = (const f16 *)krot;
+    a.v = (const f16 *)v;
+    a.dout16 = (const f16 *)dout16;
+    a.lse2 = lse2;
+    a.dsum = dsum;
+    a.dscale = scale;
+    a.rope = (const float2 *)rope;
+    a.items = nullptr;
+    a.pos = m.pos;
+    a.hdr = m.hdr;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.T = sh.T;
+    a.hq = sh.hq;
+    a.hkv = sh.hkv;
+    a.group = sh.hq / sh.hkv;
+    a.scale = sh.scale;
+    return a;
+}
+
+}  // namespace pkb

@@ -1,0 +1,215 @@
+// dQ of the packed attention backward (query-tile outer, recomputing S and dP); the math and
+// the conventions shared with the dK/dV kernel are described in pk_bwd.h.
+#include <type_traits>
+
+#include "pk_bwd.h"
+
+namespace {
+
+using namespace pkd;
+using pkb::BwdArgs;
+
+// ------------------------------------------------------------------------------------------
+// dQ: query-tile outer
+// ------------------------------------------------------------------------------------------
+template <int D>
+__device__ void q_zero_tile(const BwdArgs &a, int tile, int h) {
+    const int64_t r0 = (int64_t)tile * PK_TILE_ROWS;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = threadIdx.x; e < PK_TILE_ROWS * (D / 4); e += blockDim.x) {
+        const int64_t i = r0 + e / (D / 4);
+        if (i < a.T) *reinterpret_cast<float4 *>(a.dq + (i * a.hq + h) * D + (e % (D / 4)) * 4) = z;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
+    constexpr int BK = 64;        // keys per LDS tile
+    constexpr int NKK = D / 16, NDB = D / 32, NMB = BK / 32;
+    __shared__ __attribute__((aligned(16))) f16 lds_k[2][BK * D];   // double-buffered tiles
+    __shared__ __attribute__((aligned(16))) f16 lds_v[2][BK * D];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets bounds live in SGPRs
+    const int n32 = lane & 31, hb = lane >> 5;
+    int r, h;
+    item_head_of_block(blockIdx.x, a.hq, a.hkv, r, h);
+    const int kvh = h / a.group;
+    const int32_t *it = a.items + (int64_t)r * PK_ITEM_FIELDS;
+    if (a.hdr[0] != 0) {
+        q_zero_tile<D>(a, it[7], h);
+        return;
+    }
+    const int q_start = it[0], q_end = it[1], kv_start = it[2];
+    const int64_t T = a.T;
+    const float inv_sigma = a.dscale[1];
+
+    // this lane's query and its wave's query range
+    const int i = q_start + 32 * w + n32;
+    const bool qvalid = i < q_end;
+    const int ii = qvalid ? i : q_start;
+    const int lo_i = qvalid ? i - a.pos[i] : 0;
+    const int wq0 = q_start + 32 * w;
+    const bool wave_active = wq0 < q_end;
+    const int wq_last = min(wq0 + 31, q_end - 1);
+    const int wlo_min = __builtin_amdgcn_readfirstlane(wave_active ? wq0 - a.pos[wq0] : 0);
+    const int wlo_max = __builtin_amdgcn_readfirstlane(wave_active ? wq_last - a.pos[wq_last] : 0);
+    const float lse2 = qvalid ? a.lse2[(int64_t)h * T + i] : INFINITY;
+    const float dd = qvalid ? a.dsum[(int64_t)h * T + i] : 0.f;
+
+    // Q_rot and sigma * dout of this lane's query as k operands (d in [16kk + 8hb, +8))
+    f16x8 qf[NKK], gf[NKK];
+    {
+        const int64_t row = ((int64_t)ii * a.hq + h) * D + 8 * hb;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            qf[kk] = qvalid ? load_f16x8(a.qrot + row + 16 * kk) : zero_f16x8();
+            gf[kk] = qvalid ? load_f16x8(a.dout16 + row + 16 * kk) : zero_f16x8();
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            settle(qf[kk]);
+            settle(gf[kk]);
+        }
+        settle(lse2);
+        settle(dd);
+        settle(lo_i);
+    }
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = zero_f32x16();
+    const float sl2 = a.scale * kLog2e;
+
+    const int kb_hi = ((q_end - 1) / BK) * BK;
+    const int kb_lo = (kv_start / BK) * BK;
+
+    // Per-lane LDS byte offsets, fixed for the kernel: aoff[kk] is the 16-byte chunk of key row
+    // row_perm(n32) for d in [16kk + 8hb, +8) (rows 32.. add 64 D bytes); toff the K^T reads.
+    uint32_t aoff[NKK], toff[NDB][2];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) aoff[kk] = 2 * tile_off<D>(row_perm(n32), 16 * kk + 8 * hb);
+    tile_tr_offsets<D>(toff);
+    const uint32_t loff = tile_copy_lane_off<D>((int64_t)a.hkv * D);
+
+    // K_rot / V tiles stream into double-buffered swizzled LDS tiles with asynchronous
+    // global->LDS copies (rows past T clamped to T-1; their weight is masked to zero)
+    auto issue_tile = [&](int k0, int buf) {
+        tile_issue<D, BK>(lds_k[buf], a.krot, a.hkv, kvh, k0, T, loff);
+        tile_issue<D, BK>(lds_v[buf], a.v, a.hkv, kvh, k0, T, loff);
+    };
+
+    auto tile = [&](auto bufc, int k0) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
+        if (k0 > wq_last) return;            // every key is after every query of the wave
+        if (k0 + BK - 1 < wlo_min) return;   // every key is before the wave's first sequence
+        const bool need_mask = !(k0 + BK - 1 <= wq0 && k0 >= wlo_max);
+        const char *tk = reinterpret_cast<const char *>(lds_k[BUF]);
+        const char *tv = reinterpret_cast<const char *>(lds_v[BUF]);
+
+        // per 32-key block mb: S^T = K Q^T and dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+            f32x16 sc = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                sc = mfma32(*reinterpret_cast<const f16x8 *>(tk + aoff[kk] + 64 * D * mb), qf[kk], sc);
+                dp = mfma32(*reinterpret_cast<const f16x8 *>(tv + aoff[kk] + 64 * D * mb), gf[kk], dp);
+            }
+            // K and V operands issued 2 products ahead of their use
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int m = 0; m < 2 * NKK - 2; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (need_mask) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int jj = k0 + 32 * mb + row_perm(acc_row(rr, hb));
+                    const bool keep = qvalid & (jj >= lo_i) & (jj <= i);
+                    sc[rr] = keep ? sc[rr] : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                f16x8 sb;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const float p = fast_exp2(fmaf(sc[8 * e + x], sl2, -lse2));
+                    sb[x] = (f16)(p * (dp[8 * e + x] - dd));
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    acc[db] = mfma32(tile_tr_at(tk, toff[db], 2 * D * (32 * mb + 16 * e)), sb, acc[db]);
+            }
+            // K^T operands issued two products ahead of their use
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int m = 0; m < 2 * NDB - 2; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+    };
+
+    // the loop is unrolled by two so that the buffer of each step is a compile-time constant
+    auto step = [&](auto bufc, int k0) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
+        lds_copy_wait();
+        __syncthreads();
+        if (k0 - BK >= kb_lo) issue_tile(k0 - BK, BUF ^ 1);
+        if (wave_active) tile(bufc, k0);
+    };
+    issue_tile(kb_hi, 0);
+    for (int k0 = kb_hi; k0 >= kb_lo; k0 -= 2 * BK) {
+        step(std::integral_constant<int, 0>(), k0);
+        if (k0 - BK >= kb_lo) step(std::integral_constant<int, 1>(), k0 - BK);
+    }
+
+    // epilogue: dQ = R(-theta) (scale / sigma * dQ_rot), written once
+    if (qvalid) {
+        float *row = a.dq + ((int64_t)i * a.hq + h) * D;
+        const float2 *cs = a.rope + (int64_t)i * (D / 2);
+        const float qscale = a.scale * inv_sigma;
+#pragma unroll
+        for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = 32 * db + 8 * g4 + 4 * hb;  // first half; partner d + D/2
+                float y1[4], y2[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float2 f = cs[d + x];
+                    const float x1 = acc[db][4 * g4 + x] * qscale;
+                    const float x2 = acc[db + NDB / 2][4 * g4 + x] * qscale;
+                    y1[x] = x1 * f.x + x2 * f.y;
+                    y2[x] = x2 * f.x - x1 * f.y;
+                }
+                *reinterpret_cast<float4 *>(row + d) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+                *reinterpret_cast<float4 *>(row + d + D / 2) = make_float4(y2[0], y2[1], y2[2], y2[3]);
+            }
+    }
+}
+
+}  // namespace
+
+namespace pk {
+
+hipError_t launch_bwd_q(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
+                        const void *krot, const void *v, const void *dout16, const float *lse2,
+                        const float *dsum, const float *scale, const void *rope, float *dq,
+                        hipStream_t s) {
+    BwdArgs a = pkb::make_bwd_args(sh, m, qrot, krot, v, dout16, lse2, dsum, scale, rope, dq,
+                                   nullptr, nullptr);
+    a.items = m.fwd_items;
+    const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hq;
+    if (sh.d == 128)
+        k_attn_bwd_q<128><<<grid, 256, 0, s>>>(a);
+    else
+        k_attn_bwd_q<64><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace pk

@@ -23,7 +23,9 @@
 //     double-buffered swizzled row-major LDS tiles (no padding, no transposed copy) with
 //     asynchronous global->LDS copies, so the next tile loads while the current one is
 //     computed and no registers are spent on staging;
-//   * online softmax in the exp2 domain with scale * log2(e) folded into the scores;
+//   * online softmax in the exp2 domain with scale * log2(e) folded into the scores; the row
+//     sum adds the same fp16-rounded weights that multiply V (v_dot2_f32_f16, two per op);
+//   * LDS operands are issued a few products ahead of the products that take them;
 //   * Q is rotated in the prologue from the per-call (cos, sin) table; K comes pre-rotated;
 //   * operands are fp16 (the bf16 inputs convert exactly; rotated values, P keep 3 more bits
 //     than bf16), accumulators and the softmax state fp32.
@@ -162,6 +164,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
                 s[mb] = mfma32(*reinterpret_cast<const f16x8 *>(tk + aoff[kk] + 64 * D * mb), qf[kk], s[mb]);
+        // K operands issued four products ahead of their use
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int m = 0; m < NKK * NMB - 4; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // Online softmax in the exp2 domain.  The running max is kept on the raw scores; the
         // scale * log2(e) factor is folded into one FMA per score: p = exp2(s*c - m*c).
         // Masking runs only on tiles that straddle a boundary or the diagonal (a uniform branch).
@@ -194,31 +204,46 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
             mref = mnew;
         }
         const float m_use = mref == -INFINITY ? 0.f : mref;
-        float psum = 0.f;
+        // P in fp16 (the k operand of the second product); l sums the same fp16 weights, two at
+        // a time with v_dot2_f32_f16 against (1, 1)
+        f16x8 pb[NMB][2];
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        const f16x2 ones = {(f16)1.0f, (f16)1.0f};
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
+        for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const float p = fast_exp2(fmaf(s[mb][rr], a.scale_log2, -m_use));
-                s[mb][rr] = p;
-                psum += p;
-            }
-        }
-        l += psum;
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int x = 0; x < 8; ++x)
+                    pb[mb][e][x] = (f16)fast_exp2(fmaf(s[mb][8 * e + x], a.scale_log2, -m_use));
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const f16x2 pair = {pb[mb][e][2 * x], pb[mb][e][2 * x + 1]};
+                    l = __builtin_amdgcn_fdot2(pair, ones, l, false);
+                }
 
         // O^T (d x queries) += V^T (d x keys) * P^T (keys x queries); V^T read transposed
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                f16x8 pb;
-#pragma unroll
-                for (int x = 0; x < 8; ++x) pb[x] = (f16)s[mb][8 * e + x];
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    o[db] = mfma32(tile_tr_at(tv, toff[db], 2 * D * (32 * mb + 16 * e)), pb, o[db]);
+                    o[db] = mfma32(tile_tr_at(tv, toff[db], 2 * D * (32 * mb + 16 * e)), pb[mb][e], o[db]);
             }
         }
+        // V^T operands issued two products ahead of their use
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int m = 0; m < 2 * NMB * NDB - 2; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     };
 
     // the loop is unrolled by two so that the buffer of each step is a compile-time constant

@@ -71,9 +71,14 @@ struct AttnShape {
 hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, const void *krot,
                       const void *v, const void *rope, void *out, float *lse, hipStream_t s);
 // dout16 = sigma * dout (fp16), dsum = sigma * rowsum(dout * out), lse2 = lse * log2(e).
-hipError_t launch_bwd(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
-                      const void *krot, const void *v, const void *dout16, const float *lse2,
-                      const float *dsum, const float *scale, const void *rope, float *dq,
-                      float *dk, float *dv, int which /* 0: dK, dV; 1: dQ */, hipStream_t s);
+// launch_bwd_kv writes dk and dv, launch_bwd_q writes dq.
+hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
+                         const void *krot, const void *v, const void *dout16, const float *lse2,
+                         const float *dsum, const float *scale, const void *rope, float *dk,
+                         float *dv, hipStream_t s);
+hipError_t launch_bwd_q(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
+                        const void *krot, const void *v, const void *dout16, const float *lse2,
+                        const float *dsum, const float *scale, const void *rope, float *dq,
+                        hipStream_t s);
 
 }  // namespace pk
