@@ -32,6 +32,18 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Values of lanes l and l ^ 32 combined with one v_permlane32_swap: the swap leaves, in every
+// lane, the pair {x[l], x[l ^ 32]} in its two results, so a symmetric op of the two is the
+// cross-half reduction (no LDS permute and no address arithmetic).
+__device__ __forceinline__ float half_swap_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 2^x with the bare v_exp_f32 (results below 2^-126 flush to zero, which a softmax weight can
 // afford); exp2f would add a denormal-range fix-up of four more instructions per call.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -122,6 +122,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     }
 
     float mref = -INFINITY;  // reference max of this query's scaled scores (log2 domain)
+    float neg_m = 0.f;       // -mref, or 0 while mref is -inf (the exponent offset of p)
+    float thr = -INFINITY;   // (mref + 8) / c: a raw score above it moves the reference
     float l = 0.f;           // running sum of exp2(s*c - mref) over this lane's half of the keys
     f32x16 o[NDB];
 #pragma unroll
@@ -190,20 +192,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, s[mb][rr]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.scale_log2;
+        tmax = half_swap_max(tmax);
         // Lazy rescaling: the reference max mref (log2 domain) only moves when a row's max
         // exceeds it by more than 8, so p = exp2(s*c - mref) <= 256 (exact enough in fp32 and
-        // fp16) and the O rescale is skipped for the whole wave on most tiles.
-        const bool bump = tmax > mref + 8.f;
+        // fp16) and the O rescale is skipped for the whole wave on most tiles.  The test is made
+        // on the raw maximum against a threshold kept with mref, so a tile that does not move it
+        // spends one compare.
+        const bool bump = tmax > thr;
         if (__builtin_amdgcn_ballot_w64(bump)) {
-            const float mnew = bump ? tmax : mref;
+            const float mnew = bump ? tmax * a.scale_log2 : mref;
             const float alpha = fast_exp2(mref - mnew);   // mref = -inf gives 0
             l *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] *= alpha;
             mref = mnew;
+            neg_m = mref == -INFINITY ? 0.f : -mref;
+            thr = (mref + 8.f) / a.scale_log2;
         }
-        const float m_use = mref == -INFINITY ? 0.f : mref;
         // P in fp16 (the k operand of the second product); l sums the same fp16 weights, two at
         // a time with v_dot2_f32_f16 against (1, 1)
         f16x8 pb[NMB][2];
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
             for (int e = 0; e < 2; ++e)
 #pragma unroll
                 for (int x = 0; x < 8; ++x)
-                    pb[mb][e][x] = (f16)fast_exp2(fmaf(s[mb][8 * e + x], a.scale_log2, -m_use));
+                    pb[mb][e][x] = (f16)fast_exp2(fmaf(s[mb][8 * e + x], a.scale_log2, neg_m));
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     }
 
     // epilogue: O = O^T / l, lse = ln(sum) of the scaled scores
-    const float l_tot = l + __shfl_xor(l, 32, 64);
+    const float l_tot = half_swap_sum(l);
     if (qvalid) {
         const float inv = 1.f / l_tot;
         bf16 *orow = a.out + ((int64_t)i * a.hq + h) * D;

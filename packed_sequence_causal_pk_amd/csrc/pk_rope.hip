@@ -118,12 +118,22 @@ __global__ __launch_bounds__(256) void k_bwd_dmax(const bf16 *__restrict__ dout,
                                                   float *__restrict__ blockmax) {
     __shared__ float s_max[4];
     float amax = 0.f;
-    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n8; c += (int64_t)gridDim.x * 256) {
-        const uint4 raw = *reinterpret_cast<const uint4 *>(dout + 8 * c);
+    auto fold = [&](const uint4 &raw) {
         const bf16 *b = reinterpret_cast<const bf16 *>(&raw);
 #pragma unroll
         for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf((float)b[k]));
+    };
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // four independent 16-byte loads in flight per thread, then the remainder one at a time
+    for (; c + 3 * stride < n8; c += 4 * stride) {
+        uint4 raw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) raw[k] = *reinterpret_cast<const uint4 *>(dout + 8 * (c + k * stride));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) fold(raw[k]);
     }
+    for (; c < n8; c += stride) fold(*reinterpret_cast<const uint4 *>(dout + 8 * c));
 #pragma unroll
     for (int s = 32; s > 0; s >>= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
     if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
