@@ -49,7 +49,7 @@ struct BwdArgs {
     const f16 *v;         // [T, hkv, D] fp16 copy of v
     const f16 *dout16;    // [T, hq, D] sigma * dout, fp16
     const float *lse2;    // [hq, T] lse * log2(e)
-    const float *dsum;    // [hq, T] sigma * rowsum(dout * out)
+    const float *dsum;    // [hq, T] -sigma * rowsum(dout * out)
     const float *dscale;  // {sigma, 1/sigma}
     const float2 *rope;   // [T, D/2]
     const int32_t *items; // [n_items, 8] longest first (backward list for _kv, forward for _q)

@@ -16,7 +16,7 @@ template <int D>
 struct KvSmem {
     static constexpr int BQ = 64;        // query rows per block
     float lse2[2][BQ];   // lse * log2(e) of the block's rows (double-buffered like the tiles)
-    float dd[2][BQ];     // sigma * D_i
+    float dd[2][BQ];     // -sigma * D_i
     int pos[2][BQ];      // position of each row inside its sequence
     f16 q[2][BQ * D];    // swizzled row-major Q_rot blocks
     f16 dO[2][BQ * D];   // swizzled row-major sigma * dout blocks
@@ -183,10 +183,22 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
 
         f32x16 sp[2];       // P waves: S then P; dS waves: dP
         f16x8 pb[2][2];     // fp16 k operands of the second products: P (P waves) or dS (dS waves)
-        // the first product of half hf: S = Q K^T (P waves) or dP = dO V^T (dS waves)
+        // the first product of half hf: S = Q K^T (P waves) or dP = dO V^T (dS waves).  The dS
+        // waves start the product from -sigma D of each row (stored negated), so it ends as
+        // sigma (dP - D), the factor that multiplies P in dS.
         auto scores = [&](int hf) __attribute__((always_inline)) {
             const char *t = p_role ? cq : cg;
-            sp[hf] = zero_f32x16();
+            if constexpr (p_role) {
+                sp[hf] = zero_f32x16();
+            } else {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    float dv[8];
+                    lds_row8(&sm.dd[BUF][32 * hf + 16 * e + 8 * hb], dv);
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) sp[hf][8 * e + x] = dv[x];
+                }
+            }
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) sp[hf] = mfma32(row_op(t, kk, hf), kvf[kk], sp[hf]);
         };
@@ -216,16 +228,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
             }
         };
         // dS waves: dS = P (dP - D) with P from the P waves, as fp16 operands
-        auto dsub = [&](int hf) __attribute__((always_inline)) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int r8 = 32 * hf + 16 * e + 8 * hb;
-                float dv[8];
-                lds_row8(&sm.dd[BUF][r8], dv);
-#pragma unroll
-                for (int x = 0; x < 8; ++x) sp[hf][8 * e + x] -= dv[x];
-            }
-        };
         auto dscore = [&](int hf) __attribute__((always_inline)) {
             const float4 *xp = reinterpret_cast<const float4 *>(&sm.xp[w][hf][0][lane][0]);
 #pragma unroll
@@ -268,22 +270,16 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, NKK, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if (p_role) {
+            if constexpr (p_role) {
                 softmax(0, false);
                 softmax(1, false);
-            } else {
-                dsub(0);
-                dsub(1);
             }
         } else {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 if (!run[hf]) continue;
                 scores(hf);
-                if (p_role)
-                    softmax(hf, masked[hf]);
-                else
-                    dsub(hf);
+                if constexpr (p_role) softmax(hf, masked[hf]);
             }
         }
         __syncthreads();   // B1: P of both halves is in LDS

@@ -78,6 +78,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = zero_f32x16();
+    // -sigma D (as stored) in every result register: the dP product starts from it, so it
+    // yields sigma (dP - D) directly
+    f32x16 ndd;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndd[r] = dd;
     const float sl2 = a.scale * kLog2e;
 
     const int kb_hi = ((q_end - 1) / BK) * BK;
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
         // per 32-key block mb: S^T = K Q^T and dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-            f32x16 sc = zero_f32x16(), dp = zero_f32x16();
+            f32x16 sc = zero_f32x16(), dp = ndd;
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 sc = mfma32(*reinterpret_cast<const f16x8 *>(tk + aoff[kk] + 64 * D * mb), qf[kk], sc);
@@ -137,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const float p = fast_exp2(fmaf(sc[8 * e + x], sl2, -lse2));
-                    sb[x] = (f16)(p * (dp[8 * e + x] - dd));
+                    sb[x] = (f16)(p * dp[8 * e + x]);
                 }
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)

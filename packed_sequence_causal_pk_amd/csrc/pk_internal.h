@@ -70,7 +70,7 @@ struct AttnShape {
 };
 hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, const void *krot,
                       const void *v, const void *rope, void *out, float *lse, hipStream_t s);
-// dout16 = sigma * dout (fp16), dsum = sigma * rowsum(dout * out), lse2 = lse * log2(e).
+// dout16 = sigma * dout (fp16), dsum = -sigma * rowsum(dout * out), lse2 = lse * log2(e).
 // launch_bwd_kv writes dk and dv, launch_bwd_q writes dq.
 hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                          const void *krot, const void *v, const void *dout16, const float *lse2,

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
 #pragma unroll
     for (int sh = G / 2; sh > 0; sh >>= 1) part += __shfl_xor(part, sh, 64);
     if (c == 0) {
-        dsum[(int64_t)h * T + t] = part * sigma;
+        dsum[(int64_t)h * T + t] = -part * sigma;   // stored negated: the dP products start from it
         lse2[(int64_t)h * T + t] = lse[(int64_t)h * T + t] * pkd::kLog2e;
     }
 }
