@@ -246,7 +246,8 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     {
         ProfScope ps(PK_K_BWD_PREP, s);
         e = pk::launch_bwd_prep(ra, q, k, v, out, dout, lse, w + W.qrot, w + W.krot, w + W.vh,
-                                w + W.dout16, w + W.rope, dsum, lse2, blockmax, scale, s);
+                                w + W.dout16, w + W.rope, dsum, lse2, blockmax, scale,
+                                softmax_scale * 1.4426950408889634f, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};

@@ -30,7 +30,10 @@
 // boundary or the diagonal, and tiles outside a wave's visible range skip their products;
 // operands are fp16 with fp32 accumulation; dout enters scaled by the power of two sigma the
 // prologue chose (max|dout| * sigma in [1, 2)), so dP and dS are sigma-scaled and the results
-// are unscaled exactly by 1/sigma when written.
+// are unscaled exactly by 1/sigma when written.  Q_rot is stored times scale * log2(e) (one fp16
+// rounding of the scaled value, as precise as rounding Q_rot itself), and the score and dP
+// products start from the per-row values -lse * log2(e) and -sigma D, so they end as the
+// exponent of P and as sigma (dP - D) with no further arithmetic.
 //
 // k_attn_bwd_kv lives in pk_bwd_kv.hip and k_attn_bwd_q in pk_bwd_q.hip (separate sources so
 // each can be built with the machine scheduler that suits it).
@@ -44,11 +47,11 @@ namespace pkb {
 using namespace pkd;
 
 struct BwdArgs {
-    const f16 *qrot;      // [T, hq, D] fp16
+    const f16 *qrot;      // [T, hq, D] fp16, R(q) * scale * log2(e)
     const f16 *krot;      // [T, hkv, D] fp16
     const f16 *v;         // [T, hkv, D] fp16 copy of v
     const f16 *dout16;    // [T, hq, D] sigma * dout, fp16
-    const float *lse2;    // [hq, T] lse * log2(e)
+    const float *lse2;    // [hq, T] -lse * log2(e)
     const float *dsum;    // [hq, T] -sigma * rowsum(dout * out)
     const float *dscale;  // {sigma, 1/sigma}
     const float2 *rope;   // [T, D/2]

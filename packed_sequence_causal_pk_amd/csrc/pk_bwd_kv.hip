@@ -15,7 +15,7 @@ using pkb::BwdArgs;
 template <int D>
 struct KvSmem {
     static constexpr int BQ = 64;        // query rows per block
-    float lse2[2][BQ];   // lse * log2(e) of the block's rows (double-buffered like the tiles)
+    float lse2[2][BQ];   // -lse * log2(e) of the block's rows (double-buffered like the tiles)
     float dd[2][BQ];     // -sigma * D_i
     int pos[2][BQ];      // position of each row inside its sequence
     f16 q[2][BQ * D];    // swizzled row-major Q_rot blocks
@@ -149,7 +149,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
     f32x16 acc[NDB];   // dV^T (P waves) or dK_rot^T (dS waves): d rows x this wave's 32 keys
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = zero_f32x16();
-    const float sl2 = a.scale * kLog2e;
 
     // The main loop, instantiated once per role so that each role's code and registers are
     // its own.
@@ -183,34 +182,30 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
 
         f32x16 sp[2];       // P waves: S then P; dS waves: dP
         f16x8 pb[2][2];     // fp16 k operands of the second products: P (P waves) or dS (dS waves)
-        // the first product of half hf: S = Q K^T (P waves) or dP = dO V^T (dS waves).  The dS
-        // waves start the product from -sigma D of each row (stored negated), so it ends as
-        // sigma (dP - D), the factor that multiplies P in dS.
+        // the first product of half hf: S = Q K^T (P waves) or dP = dO V^T (dS waves).  Each
+        // starts from a per-row value stored negated: the P waves from -lse * log2(e), so with
+        // Q_rot carrying scale * log2(e) the product ends as the exponent of P; the dS waves from
+        // -sigma D, so it ends as sigma (dP - D), the factor that multiplies P in dS.
         auto scores = [&](int hf) __attribute__((always_inline)) {
             const char *t = p_role ? cq : cg;
-            if constexpr (p_role) {
-                sp[hf] = zero_f32x16();
-            } else {
+            const float *init = p_role ? sm.lse2[BUF] : sm.dd[BUF];
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    float dv[8];
-                    lds_row8(&sm.dd[BUF][32 * hf + 16 * e + 8 * hb], dv);
+            for (int e = 0; e < 2; ++e) {
+                float iv[8];
+                lds_row8(&init[32 * hf + 16 * e + 8 * hb], iv);
 #pragma unroll
-                    for (int x = 0; x < 8; ++x) sp[hf][8 * e + x] = dv[x];
-                }
+                for (int x = 0; x < 8; ++x) sp[hf][8 * e + x] = iv[x];
             }
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) sp[hf] = mfma32(row_op(t, kk, hf), kvf[kk], sp[hf]);
         };
-        // P waves: P = exp2(S scale log2e - lse2) (masked when asked), stored for the dS waves
-        // and kept as fp16 operands
+        // P waves: P = exp2(S scale log2e - lse log2e) (masked when asked), stored for the dS
+        // waves
         auto softmax = [&](int hf, bool msk) __attribute__((always_inline)) {
             float4 *xp = reinterpret_cast<float4 *>(&sm.xp[w][hf][0][lane][0]);
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int r8 = 32 * hf + 16 * e + 8 * hb;   // first row of this lane's 8
-                float lv[8];
-                lds_row8(&sm.lse2[BUF][r8], lv);
                 int p8[8];
                 if (msk) lds_row8(&sm.pos[BUF][r8], p8);
 #pragma unroll
@@ -221,7 +216,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
                         const bool keep = (r8 + x < nrows) & (j >= i - p8[x]) & (j <= i);  // no short circuit
                         sv = keep ? sv : -INFINITY;
                     }
-                    sp[hf][8 * e + x] = fast_exp2(fmaf(sv, sl2, -lv[x]));
+                    sp[hf][8 * e + x] = fast_exp2(sv);
                 }
                 xp[(2 * e) * 64] = make_float4(sp[hf][8 * e], sp[hf][8 * e + 1], sp[hf][8 * e + 2], sp[hf][8 * e + 3]);
                 xp[(2 * e + 1) * 64] = make_float4(sp[hf][8 * e + 4], sp[hf][8 * e + 5], sp[hf][8 * e + 6], sp[hf][8 * e + 7]);
@@ -352,7 +347,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
         } else {
             float *dkrow = a.dk + rowoff;
             const float2 *cs = a.rope + (int64_t)j * (D / 2);
-            const float kscale = a.scale * inv_sigma;
+            // Q_rot carries scale * log2(e), so scale * dK_rot = ln(2) * acc
+            const float kscale = kLn2 * inv_sigma;
 #pragma unroll
             for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll

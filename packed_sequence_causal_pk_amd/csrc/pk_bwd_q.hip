@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     const int wq_last = min(wq0 + 31, q_end - 1);
     const int wlo_min = __builtin_amdgcn_readfirstlane(wave_active ? wq0 - a.pos[wq0] : 0);
     const int wlo_max = __builtin_amdgcn_readfirstlane(wave_active ? wq_last - a.pos[wq_last] : 0);
-    const float lse2 = qvalid ? a.lse2[(int64_t)h * T + i] : INFINITY;
+    const float nlse2 = qvalid ? a.lse2[(int64_t)h * T + i] : -INFINITY;   // -lse * log2(e)
     const float dd = qvalid ? a.dsum[(int64_t)h * T + i] : 0.f;
 
     // Q_rot and sigma * dout of this lane's query as k operands (d in [16kk + 8hb, +8))
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
             settle(qf[kk]);
             settle(gf[kk]);
         }
-        settle(lse2);
+        settle(nlse2);
         settle(dd);
         settle(lo_i);
     }
@@ -80,10 +80,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     for (int db = 0; db < NDB; ++db) acc[db] = zero_f32x16();
     // -sigma D (as stored) in every result register: the dP product starts from it, so it
     // yields sigma (dP - D) directly
-    f32x16 ndd;
+    // and -lse * log2(e) likewise for the score product: with Q_rot carrying scale * log2(e) it
+    // ends as the exponent of P
+    f32x16 ndd, nls;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ndd[r] = dd;
-    const float sl2 = a.scale * kLog2e;
+    for (int r = 0; r < 16; ++r) {
+        ndd[r] = dd;
+        nls[r] = nlse2;
+    }
 
     const int kb_hi = ((q_end - 1) / BK) * BK;
     const int kb_lo = (kv_start / BK) * BK;
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
         // per 32-key block mb: S^T = K Q^T and dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-            f32x16 sc = zero_f32x16(), dp = ndd;
+            f32x16 sc = nls, dp = ndd;
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 sc = mfma32(*reinterpret_cast<const f16x8 *>(tk + aoff[kk] + 64 * D * mb), qf[kk], sc);
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
                 f16x8 sb;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
-                    const float p = fast_exp2(fmaf(sc[8 * e + x], sl2, -lse2));
+                    const float p = fast_exp2(sc[8 * e + x]);
                     sb[x] = (f16)(p * dp[8 * e + x]);
                 }
 #pragma unroll

@@ -61,7 +61,7 @@ unsigned dmax_blocks(int64_t T, int hq, int d);
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *v,
                            const void *out, const void *dout, const float *lse, void *qrot,
                            void *krot, void *vh, void *dout16, void *rope, float *dsum,
-                           float *lse2, float *blockmax, float *scale, hipStream_t s);
+                           float *lse2, float *blockmax, float *scale, float qscale, hipStream_t s);
 
 struct AttnShape {
     int64_t T;
@@ -70,7 +70,8 @@ struct AttnShape {
 };
 hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, const void *krot,
                       const void *v, const void *rope, void *out, float *lse, hipStream_t s);
-// dout16 = sigma * dout (fp16), dsum = -sigma * rowsum(dout * out), lse2 = lse * log2(e).
+// qrot = R(q) * softmax_scale * log2(e) (fp16), dout16 = sigma * dout (fp16),
+// dsum = -sigma * rowsum(dout * out), lse2 = -lse * log2(e).
 // launch_bwd_kv writes dk and dv, launch_bwd_q writes dq.
 hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                          const void *krot, const void *v, const void *dout16, const float *lse2,

@@ -178,8 +178,10 @@ __device__ __forceinline__ void table8(const float2 *__restrict__ table, int64_t
 // Per-row work of the backward prologue, one thread per (row, group c of 8 rotation pairs): the
 // thread owns elements [8c, 8c + 8) of a head row and their partners + D/2, read and written as
 // 16-byte vectors.  Rows [0, T * hkv) are K rows (rotated) with their V rows (converted); rows
-// [T * hkv, T * (hkv + hq)) are query-head rows: Q rotated, sigma * dout, and the row sums
-// sigma * sum(dout * out) and lse * log2(e).
+// [T * hkv, T * (hkv + hq)) are query-head rows: Q rotated and multiplied by qscale (the softmax
+// scale times log2(e), so that the backward's score products come out in the exp2 domain),
+// sigma * dout, and the row values -sigma * sum(dout * out) and -lse * log2(e), stored negated
+// because the backward's products start from them.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
                                                   const float2 *__restrict__ table,
@@ -195,21 +197,21 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
                                                   f16 *__restrict__ vh,
                                                   f16 *__restrict__ dout16,
                                                   float *__restrict__ dsum,
-                                                  float *__restrict__ lse2) {
+                                                  float *__restrict__ lse2, float qscale) {
     constexpr int G = D / 16;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int c = (int)(gid % G);
     int64_t row = gid / G;
     const int64_t nkv = T * hkv;
     float cs[8], sn[8];
-    auto rotate = [&](const bf16 *src, f16 *dst) {
+    auto rotate = [&](const bf16 *src, f16 *dst, float mult) {
         const bf16x8 x1 = pkd::load_bf16x8(src + 8 * c), x2 = pkd::load_bf16x8(src + D / 2 + 8 * c);
         f16x8 y1, y2;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float a1 = (float)x1[e], a2 = (float)x2[e];
-            y1[e] = (f16)(a1 * cs[e] - a2 * sn[e]);
-            y2[e] = (f16)(a2 * cs[e] + a1 * sn[e]);
+            y1[e] = (f16)((a1 * cs[e] - a2 * sn[e]) * mult);
+            y2[e] = (f16)((a2 * cs[e] + a1 * sn[e]) * mult);
         }
         pkd::store_f16x8(dst + 8 * c, y1);
         pkd::store_f16x8(dst + D / 2 + 8 * c, y2);
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
     if (row < nkv) {
         table8<D>(table, row / hkv, c, cs, sn);
         const int64_t off = row * D;
-        rotate(k + off, krot + off);
+        rotate(k + off, krot + off, 1.0f);
         pkd::store_f16x8(vh + off + 8 * c, pkd::bf16x8_to_f16x8(pkd::load_bf16x8(v + off + 8 * c)));
         pkd::store_f16x8(vh + off + D / 2 + 8 * c,
                          pkd::bf16x8_to_f16x8(pkd::load_bf16x8(v + off + D / 2 + 8 * c)));
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
     const int h = (int)(row % hq);
     table8<D>(table, t, c, cs, sn);
     const int64_t off = row * D;
-    rotate(q + off, qrot + off);
+    rotate(q + off, qrot + off, qscale);
     const float sigma = dscale[0];
     const bf16x8 o1 = pkd::load_bf16x8(out + off + 8 * c), o2 = pkd::load_bf16x8(out + off + D / 2 + 8 * c);
     const bf16x8 g1 = pkd::load_bf16x8(dout + off + 8 * c), g2 = pkd::load_bf16x8(dout + off + D / 2 + 8 * c);
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
     for (int sh = G / 2; sh > 0; sh >>= 1) part += __shfl_xor(part, sh, 64);
     if (c == 0) {
         dsum[(int64_t)h * T + t] = -part * sigma;   // stored negated: the dP products start from it
-        lse2[(int64_t)h * T + t] = lse[(int64_t)h * T + t] * pkd::kLog2e;
+        lse2[(int64_t)h * T + t] = -lse[(int64_t)h * T + t] * pkd::kLog2e;
     }
 }
 
@@ -299,7 +301,7 @@ hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, const void *v, void
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *v,
                            const void *out, const void *dout, const float *lse, void *qrot,
                            void *krot, void *vh, void *dout16, void *rope, float *dsum,
-                           float *lse2, float *blockmax, float *scale, hipStream_t s) {
+                           float *lse2, float *blockmax, float *scale, float qscale, hipStream_t s) {
     const int64_t n8 = r.T * r.hq * r.d / 8;
     const unsigned nb = dmax_blocks(r.T, r.hq, r.d);
     k_bwd_dmax<<<nb, 256, 0, s>>>((const bf16 *)dout, n8, blockmax);
@@ -314,13 +316,13 @@ hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, cons
         k_bwd_rows<128><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
                                             (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
                                             (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
-                                            (f16 *)vh, (f16 *)dout16, dsum, lse2);
+                                            (f16 *)vh, (f16 *)dout16, dsum, lse2, qscale);
     } else {
         k_rope_table<64><<<gt, 256, 0, s>>>(r.pos, r.T, r.rope_base, (float2 *)rope);
         k_bwd_rows<64><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
                                            (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
                                            (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
-                                           (f16 *)vh, (f16 *)dout16, dsum, lse2);
+                                           (f16 *)vh, (f16 *)dout16, dsum, lse2, qscale);
     }
     return hipGetLastError();
 }
