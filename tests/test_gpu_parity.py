@@ -115,6 +115,35 @@ def test_fwd_bwd_small(case):
     compare("dv", to_np(res["dv"]), dv_ref)
 
 
+SCALE_BASE_CASES = [
+    # (softmax scale as a function of d, RoPE base, d, power-of-two factor on q and k)
+    (lambda d: 1.0 / d, 1e4, 128, 4.0),
+    (lambda d: 0.25, 5e5, 128, 0.5),
+    (lambda d: 2.0 / math.sqrt(d), 1e6, 64, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SCALE_BASE_CASES)))
+def test_softmax_scale_and_rope_base(case):
+    """Softmax scales and RoPE bases other than the workloads' (the kernels fold the scale into
+    their fp16 operands and exponents and read the table built for the base).  The max-abs gate
+    is absolute and was set for scores of unit spread, so q and k are multiplied by a power of
+    two (exact in bf16) that keeps scale * <q, k> near that spread."""
+    scale_of, base, d, f = SCALE_BASE_CASES[case]
+    scale = scale_of(d)
+    say("scale %.6g base %g d %d qk factor %g" % (scale, base, d, f))
+    lens, q, k, v, do = synth.small_problem(400 + case, [300, 1, 170, 45], 4, 2, d)
+    q, k = (q * f).astype(np.float32), (k * f).astype(np.float32)
+    res = run_pk(lens, q, k, v, do, scale, base)
+    o_ref, lse_ref = O.attn_fwd(q, k, v, lens, scale, base)
+    dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, scale, base)
+    compare("out", to_np(res["out"]), o_ref)
+    compare("lse", to_np(res["lse"]), lse_ref, max_abs=LSE_MAX_ABS)
+    compare("dq", to_np(res["dq"]), dq_ref)
+    compare("dk", to_np(res["dk"]), dk_ref)
+    compare("dv", to_np(res["dv"]), dv_ref)
+
+
 @pytest.mark.parametrize("log2_scale", [-24, -12, 10])
 def test_gradient_scale_invariance(log2_scale):
     """dout scaled by 2^e (exact in bf16) gives gradients scaled by 2^e: the backward's fp16
