@@ -168,16 +168,24 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
         // Per-half visibility (uniform): a half is skipped when it has no item rows or sees none
         // of this wave's keys, and masked element-wise unless all 32 rows see all 32 keys.  Both
         // roles of a key sub-tile reach the same decisions from the same LDS data.
+        // (The four position reads are issued together and the tests combined without short
+        // circuits, so the decision costs one LDS round trip and no branches.)
         bool run[2], masked[2];
+        int pfirst[2], plast[2], rlast[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const int r0 = 32 * hf;
+            rlast[hf] = 32 * hf + max(min(32, nrows - 32 * hf), 1) - 1;
+            pfirst[hf] = sm.pos[BUF][32 * hf];
+            plast[hf] = sm.pos[BUF][rlast[hf]];
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int r0 = 32 * hf, rl = rlast[hf];
             const int hrows = min(32, nrows - r0);
-            const int rl = r0 + max(hrows, 1) - 1;
-            const int lo_first = __builtin_amdgcn_readfirstlane(qb + r0 - sm.pos[BUF][r0]);
-            const int lo_last = __builtin_amdgcn_readfirstlane(qb + rl - sm.pos[BUF][rl]);
-            run[hf] = wave_active && hrows > 0 && qb + rl >= wk0 && lo_first <= wk_last;
-            masked[hf] = !(hrows == 32 && qb + r0 >= wk0 + 31 && lo_last <= wk0);
+            const int lo_first = __builtin_amdgcn_readfirstlane(qb + r0 - pfirst[hf]);
+            const int lo_last = __builtin_amdgcn_readfirstlane(qb + rl - plast[hf]);
+            run[hf] = wave_active & (hrows > 0) & (qb + rl >= wk0) & (lo_first <= wk_last);
+            masked[hf] = !((hrows == 32) & (qb + r0 >= wk0 + 31) & (lo_last <= wk0));
         }
 
         f32x16 sp[2];       // P waves: S then P; dS waves: dP
@@ -186,8 +194,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
         // starts from a per-row value stored negated: the P waves from -lse * log2(e), so with
         // Q_rot carrying scale * log2(e) the product ends as the exponent of P; the dS waves from
         // -sigma D, so it ends as sigma (dP - D), the factor that multiplies P in dS.
-        auto scores = [&](int hf) __attribute__((always_inline)) {
-            const char *t = p_role ? cq : cg;
+        auto init_scores = [&](int hf) __attribute__((always_inline)) {
             const float *init = p_role ? sm.lse2[BUF] : sm.dd[BUF];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -196,6 +203,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
 #pragma unroll
                 for (int x = 0; x < 8; ++x) sp[hf][8 * e + x] = iv[x];
             }
+        };
+        auto scores = [&](int hf) __attribute__((always_inline)) {
+            const char *t = p_role ? cq : cg;
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) sp[hf] = mfma32(row_op(t, kk, hf), kvf[kk], sp[hf]);
         };
@@ -255,6 +265,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
         const bool both = run[0] & run[1];
         const bool fast = both & (!p_role | (!masked[0] & !masked[1]));
         if (fast) {
+            // the row values first, in a region of their own, so that the operand reads below
+            // keep their distance ahead of the products
+            init_scores(0);
+            init_scores(1);
+            __builtin_amdgcn_sched_barrier(0);
             scores(0);
             scores(1);
             __builtin_amdgcn_sched_group_barrier(0x100, NKK, 0);       // one half's operands ahead
@@ -273,6 +288,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 if (!run[hf]) continue;
+                init_scores(hf);
                 scores(hf);
                 if constexpr (p_role) softmax(hf, masked[hf]);
             }
