@@ -131,7 +131,10 @@ size_t pk_attn_bwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int3
 
 /* Backward of pk_attn_fwd for the loss sum(out * dout): float32 dq [T,hq,d], dk and dv
  * [T,hkv,d] (dk, dv summed over the query heads of each KV group).  `out` and `lse` are the
- * forward's outputs for the same inputs.  dq, dk and dv are fully overwritten. */
+ * forward's outputs for the same inputs.  dq, dk and dv are fully overwritten.
+ * On packs too small to fill the device, the dQ kernel runs on a library-owned stream of the
+ * same device (default priority, created on first use), forked from and joined back into
+ * `hip_stream` with events, so every result is ordered on `hip_stream` as if it ran there. */
 pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *v,
                       const void *out, const float *lse, const void *dout,
                       int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float rope_base,
