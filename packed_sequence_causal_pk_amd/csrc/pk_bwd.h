@@ -10,11 +10,11 @@
 // its gradients by hand), applied to A = softmax(Q K^T / sqrt(d) + M) V.
 //
 // Two kernels, neither with atomics, so every gradient is written exactly once:
-//   k_attn_bwd_kv  one workgroup per backward work item (128 keys) x KV head.  The 4 waves own
-//                  32 keys each; K_rot and V of those keys are the k operands of S = Q K^T and
-//                  dP = dO V^T (v_mfma_f32_32x32x16_f16), dK^T and dV^T accumulate in registers
-//                  over every query block AND every query head of the GQA group (so the group
-//                  sum is free), and dK, dV are written once.  Query blocks of 64 rows stream
+//   k_attn_bwd_kv  one workgroup per backward work item (128 keys) x KV head, 8 waves split by
+//                  role over four 32-key sub-tiles; K_rot and V of a sub-tile's keys are the k
+//                  operands of S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_f16), dK^T and dV^T
+//                  accumulate in registers over every query block AND every query head of the
+//                  GQA group (so the group sum is free), and dK, dV are written once.  Query blocks of 64 rows stream
 //                  into double-buffered swizzled LDS tiles by asynchronous global->LDS copies;
 //                  the transposed operands of dV^T += dO^T P and dK^T += Q^T dS are read with
 //                  ds_read_b64_tr_b16 from the same row-major tiles.

@@ -19,10 +19,11 @@
 //   * P^T stays in registers and is the k operand of O^T += V^T P^T; key rows of the first
 //     product are fed in row_perm order so each lane's 8 keys of the V^T operand are
 //     consecutive, read with two transposing LDS loads (ds_read_b64_tr_b16);
-//   * K_rot and V tiles of 64 keys (both fp16, written by the prologue pass) stream into
-//     double-buffered swizzled row-major LDS tiles (no padding, no transposed copy) with
-//     asynchronous global->LDS copies, so the next tile loads while the current one is
-//     computed and no registers are spent on staging;
+//   * K_rot and V tiles of 32 keys (both fp16, written by the prologue pass) stream into
+//     double-buffered swizzled row-major LDS tiles (no padding, no transposed copy; 32 KB per
+//     workgroup, so three workgroups share a compute unit) with asynchronous global->LDS
+//     copies, so the next tile loads while the current one is computed and no registers are
+//     spent on staging;
 //   * online softmax in the exp2 domain with scale * log2(e) folded into the scores; the row
 //     sum adds the same fp16-rounded weights that multiply V (v_dot2_f32_f16, two per op);
 //   * LDS operands are issued a few products ahead of the products that take them;
