@@ -19,11 +19,11 @@
 //   * P^T stays in registers and is the k operand of O^T += V^T P^T; key rows of the first
 //     product are fed in row_perm order so each lane's 8 keys of the V^T operand are
 //     consecutive, read with two transposing LDS loads (ds_read_b64_tr_b16);
-//   * K_rot and V tiles of 32 keys (both fp16, written by the prologue pass) stream into
-//     double-buffered swizzled row-major LDS tiles (no padding, no transposed copy; 32 KB per
-//     workgroup, so three workgroups share a compute unit) with asynchronous global->LDS
-//     copies, so the next tile loads while the current one is computed and no registers are
-//     spent on staging;
+//   * K_rot and V tiles of 32 keys (64 on small packs; both fp16, written by the prologue pass)
+//     stream into double-buffered swizzled row-major LDS tiles (no padding, no transposed copy;
+//     32 KB per workgroup, so three workgroups share a compute unit) with asynchronous
+//     global->LDS copies, so the next tile loads while the current one is computed and no
+//     registers are spent on staging;
 //   * online softmax in the exp2 domain with scale * log2(e) folded into the scores; the row
 //     sum adds the same fp16-rounded weights that multiply V (v_dot2_f32_f16, two per op);
 //   * LDS operands are issued a few products ahead of the products that take them;
@@ -65,9 +65,14 @@ __device__ void fwd_zero_tile(const FwdArgs &a, int tile, int h) {
         if (r0 + e < a.T) a.lse[(int64_t)h * a.T + r0 + e] = 0.f;
 }
 
-template <int D>
+// BK keys per LDS tile: 32 (32 KB of tiles per workgroup, three workgroups per compute unit) on
+// packs with many (item, head) workgroups; 64 (64 KB, two per compute unit, half the barriers
+// and tile copies per key) on small packs, whose time goes to latency rather than throughput
+// (measured: 64-key tiles are 4-6% slower on the Qwen3-14B-shaped pack and 6-7% faster on the
+// Llama- and Qwen3-0.6B-shaped ones).
+template <int D, int BK>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
-    constexpr int BK = 32;        // keys per LDS tile
+    static_assert(BK == 32 || BK == 64, "tiles of 32 or 64 keys");
     constexpr int NKK = D / 16;   // k-steps of the score product
     constexpr int NDB = D / 32;   // 32-row blocks of O^T
     constexpr int NMB = BK / 32;  // 32-key blocks per tile
@@ -308,10 +313,18 @@ hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, co
     a.group = sh.hq / sh.hkv;
     a.scale_log2 = sh.scale * pkd::kLog2e;
     const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hq;
-    if (sh.d == 128)
-        k_attn_fwd<128><<<grid, 256, 0, s>>>(a);
-    else
-        k_attn_fwd<64><<<grid, 256, 0, s>>>(a);
+    const bool small = grid <= 2048;   // a few rounds of workgroups on a 256-CU device
+    if (sh.d == 128) {
+        if (small)
+            k_attn_fwd<128, 64><<<grid, 256, 0, s>>>(a);
+        else
+            k_attn_fwd<128, 32><<<grid, 256, 0, s>>>(a);
+    } else {
+        if (small)
+            k_attn_fwd<64, 64><<<grid, 256, 0, s>>>(a);
+        else
+            k_attn_fwd<64, 32><<<grid, 256, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
