@@ -13,11 +13,12 @@
 //
 // Rotated q and k, v, and the scaled dout are written as fp16, the matrix-core operand format of
 // the attention kernels, so those can copy tiles straight into LDS.  The backward prologue first
-// reduces max|dout| (k_bwd_dmax); k_bwd_scale turns it into a power of two sigma with
+// reduces max|dout| per block (k_bwd_pre, whose other blocks write the (cos, sin) table);
+// k_bwd_scale turns the maxima into a power of two sigma with
 // max|dout| * sigma in [1, 2), so the backward's fp16 gradient operands (dout and dS, both scaled
 // by sigma, unscaled exactly at the end) stay inside fp16's range whatever the magnitude of the
-// incoming gradient.  k_rope_table writes the (cos, sin) table and k_bwd_rows then writes the
-// rotated Q and K, V and sigma * dout in fp16, sigma * rowsum(dout * out) and lse * log2(e).
+// incoming gradient.  k_bwd_rows then writes the rotated Q (times scale * log2(e)) and K, V and
+// sigma * dout in fp16, -sigma * rowsum(dout * out) and -lse * log2(e).
 //
 // Thread layout of the two per-token kernels: one thread per (token t, group c of 4 rotation pairs);
 // the thread owns elements d in [4c, 4c+4) and their partners d + D/2 for every head, so each
@@ -114,8 +115,8 @@ __global__ __launch_bounds__(256) void k_fwd_prep(const int32_t *__restrict__ po
 }
 
 // max|dout| per block over the flattened [T * hq * d] tensor, 8 elements per thread step.
-__global__ __launch_bounds__(256) void k_bwd_dmax(const bf16 *__restrict__ dout, int64_t n8,
-                                                  float *__restrict__ blockmax) {
+__device__ __forceinline__ void bwd_dmax_block(const bf16 *__restrict__ dout, int64_t n8,
+                                               float *__restrict__ blockmax, int b, int nb) {
     __shared__ float s_max[4];
     float amax = 0.f;
     auto fold = [&](const uint4 &raw) {
@@ -123,8 +124,8 @@ __global__ __launch_bounds__(256) void k_bwd_dmax(const bf16 *__restrict__ dout,
 #pragma unroll
         for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf((float)b[k]));
     };
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t stride = (int64_t)nb * 256;
+    int64_t c = (int64_t)b * 256 + threadIdx.x;
     // four independent 16-byte loads in flight per thread, then the remainder one at a time
     for (; c + 3 * stride < n8; c += 4 * stride) {
         uint4 raw[4];
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(256) void k_bwd_dmax(const bf16 *__restrict__ dout,
     if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
     __syncthreads();
     if (threadIdx.x == 0)
-        blockmax[blockIdx.x] = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+        blockmax[b] = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
 }
 
 // Store 4 floats as fp16 after scaling.
@@ -150,14 +151,28 @@ __device__ __forceinline__ void store4s(f16 *p, const float x[4], float scale) {
 
 // The (cos, sin) table alone: one thread per (token, group of 4 rotation pairs).
 template <int D>
-__global__ __launch_bounds__(256) void k_rope_table(const int32_t *__restrict__ pos, int64_t T,
-                                                    float base, float2 *__restrict__ table) {
+__device__ __forceinline__ void rope_table_block(const int32_t *__restrict__ pos, int64_t T, float base,
+                                                 float2 *__restrict__ table, int b) {
     constexpr int G = D / 8;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gid = (int64_t)b * 256 + threadIdx.x;
     const int64_t t = gid / G;
     if (t >= T) return;
     float cs[4], sn[4];
     rope_factors<D>(pos, t, (int)(gid % G), base, table, cs, sn);
+}
+
+// First launch of the backward prologue, two independent jobs in one grid (one launch fewer,
+// which small packs feel): blocks [0, nb) reduce max|dout| per block, the rest write the RoPE
+// table (one thread per token and group of 4 rotation pairs).
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_pre(const bf16 *__restrict__ dout, int64_t n8,
+                                                 float *__restrict__ blockmax, int nb,
+                                                 const int32_t *__restrict__ pos, int64_t T,
+                                                 float base, float2 *__restrict__ table) {
+    if ((int)blockIdx.x < nb)
+        bwd_dmax_block(dout, n8, blockmax, (int)blockIdx.x, nb);
+    else
+        rope_table_block<D>(pos, T, base, table, (int)blockIdx.x - nb);
 }
 
 // Rotation factors of pairs [8c, 8c + 8) of token t from the table.
@@ -304,21 +319,24 @@ hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, cons
                            float *lse2, float *blockmax, float *scale, float qscale, hipStream_t s) {
     const int64_t n8 = r.T * r.hq * r.d / 8;
     const unsigned nb = dmax_blocks(r.T, r.hq, r.d);
-    k_bwd_dmax<<<nb, 256, 0, s>>>((const bf16 *)dout, n8, blockmax);
+    const unsigned gt = prep_blocks(r.T, r.d);
+    const unsigned gr = (unsigned)((r.T * (r.hq + r.hkv) * (r.d / 16) + 255) / 256);
+    if (r.d == 128)
+        k_bwd_pre<128><<<nb + gt, 256, 0, s>>>((const bf16 *)dout, n8, blockmax, (int)nb, r.pos, r.T,
+                                               r.rope_base, (float2 *)rope);
+    else
+        k_bwd_pre<64><<<nb + gt, 256, 0, s>>>((const bf16 *)dout, n8, blockmax, (int)nb, r.pos, r.T,
+                                              r.rope_base, (float2 *)rope);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_bwd_scale<<<1, 256, 0, s>>>(blockmax, (int)nb, scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const unsigned gt = prep_blocks(r.T, r.d);
-    const unsigned gr = (unsigned)((r.T * (r.hq + r.hkv) * (r.d / 16) + 255) / 256);
     if (r.d == 128) {
-        k_rope_table<128><<<gt, 256, 0, s>>>(r.pos, r.T, r.rope_base, (float2 *)rope);
         k_bwd_rows<128><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
                                             (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
                                             (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
                                             (f16 *)vh, (f16 *)dout16, dsum, lse2, qscale);
     } else {
-        k_rope_table<64><<<gt, 256, 0, s>>>(r.pos, r.T, r.rope_base, (float2 *)rope);
         k_bwd_rows<64><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
                                            (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
                                            (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
