@@ -60,7 +60,8 @@ pk_status hip_status(hipError_t e) { return e == hipSuccess ? PK_OK : PK_ERR_HIP
 // ------------------------------------------------------------------ side stream of the backward
 // The dK/dV and dQ kernels of one backward call are independent once the prologue has run.  When
 // the dK/dV grid (one workgroup of 512 threads per item and KV head, one per compute unit) is
-// too small to fill the device twice over, the dQ kernel runs on a second stream of the same
+// too small to fill the device twice over (but not so small that the whole backward is a few
+// microseconds, where the fork and join cost more than they save), the dQ kernel runs on a second stream of the same
 // device (default priority), forked from and joined back into the caller's stream with events,
 // and takes the compute units the dK/dV kernel leaves idle (measured: -7% backward time on the
 // Llama-shaped pack, -2% on the Qwen3-0.6B-shaped one; on the Qwen3-14B-shaped pack, whose
@@ -298,7 +299,7 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     SideStream *side = side_stream(meta->device);
     hipStream_t sq = s;   // stream of the dQ kernel
     const int64_t kv_grid = (int64_t)meta->n_items * hkv;
-    if (side && kv_grid <= 2 * (int64_t)side->cus && hipEventRecord(side->fork, s) == hipSuccess &&
+    if (side && kv_grid >= 64 && kv_grid <= 2 * (int64_t)side->cus && hipEventRecord(side->fork, s) == hipSuccess &&
         hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess)
         sq = side->stream;
     {
