@@ -89,8 +89,16 @@ __device__ __forceinline__ void lds_row8(const T *p, T (&out)[8]) {
 //   B0: block data in LDS  ->  S, P (P waves) | dP (dS waves)  ->  B1: P in LDS  ->
 //   dV (P waves) | dS, dK (dS waves)
 // so each SIMD runs one wave's products while the other does its element-wise work.
-template <int D>
+//
+// NS = 2 splits every item over two workgroups of 64 keys each, for packs whose grid of items x
+// KV heads would leave compute units idle: a workgroup's 8 waves are then two 32-key sub-tiles
+// x two roles x the two 32-row halves of each query block, each wave doing one half, and the
+// two halves' partial dK, dV are summed through LDS at the end.  Each block costs a wave half
+// the products, so the longest workgroup (which sets the time of a small pack) takes about half
+// as long.
+template <int D, int NS>
 __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
+    static_assert(NS == 1 || NS == 2, "an item on one or two workgroups");
     using S = KvSmem<D>;
     constexpr int BQ = S::BQ;
     constexpr int NKK = D / 16, NDB = D / 32;
@@ -99,21 +107,28 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets bounds live in SGPRs
-    const int w = wv & 3;                                     // key sub-tile of this wave
+    const int w = wv & 3;              // P hand-off slot; with NS = 1 also the key sub-tile
     const bool p_role = wv < 4;
     const int n32 = lane & 31, hb = lane >> 5;
-    const int r = blockIdx.x / a.hkv, kvh = blockIdx.x % a.hkv;
+    // workgroup -> (item r, key half kh, KV head kvh), heads fastest
+    const int r = blockIdx.x / (a.hkv * NS), kh = (blockIdx.x / a.hkv) % NS, kvh = blockIdx.x % a.hkv;
+    const int sub = NS == 1 ? w : (w & 1);       // 32-key sub-tile of this wave
+    const int hf_own = NS == 1 ? -1 : (w >> 1);  // with NS = 2: the query-block half of this wave
     const int32_t *it = a.items + (int64_t)r * PK_ITEM_FIELDS;
     if (a.hdr[0] != 0) {
-        kv_zero_tile<D>(a, it[7], kvh);
+        if (kh == 0) kv_zero_tile<D>(a, it[7], kvh);
         return;
     }
-    const int kv_start = it[0], kv_end = it[1], q_start = it[2], q_end = it[3];
+    const int kv_start = it[0], kv_end = it[1], q_end = it[3];
+    const int key_base = kv_start + 64 * kh;     // first key of this workgroup
+    if (key_base >= kv_end) return;              // (NS = 2) an item of 64 keys or fewer
+    // Query blocks start at the first key of the workgroup: earlier rows see none of its keys.
+    const int q_start = NS == 1 ? it[2] : it[2] + 64 * kh;
     const float inv_sigma = a.dscale[1];
 
-    const int j = kv_start + 32 * w + n32;  // this lane's key
+    const int j = key_base + 32 * sub + n32;  // this lane's key
     const bool kvalid = j < kv_end;
-    const int wk0 = kv_start + 32 * w;
+    const int wk0 = key_base + 32 * sub;
     const bool wave_active = wk0 < kv_end;
     const int wk_last = min(wk0 + 31, kv_end - 1);
 
@@ -184,7 +199,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
             const int hrows = min(32, nrows - r0);
             const int lo_first = __builtin_amdgcn_readfirstlane(qb + r0 - pfirst[hf]);
             const int lo_last = __builtin_amdgcn_readfirstlane(qb + rl - plast[hf]);
-            run[hf] = wave_active & (hrows > 0) & (qb + rl >= wk0) & (lo_first <= wk_last);
+            run[hf] = wave_active & (hrows > 0) & (qb + rl >= wk0) & (lo_first <= wk_last) &
+                      (NS == 1 || hf == hf_own);
             masked[hf] = !((hrows == 32) & (qb + r0 >= wk0 + 31) & (lo_last <= wk0));
         }
 
@@ -345,6 +361,28 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
     else
         main_loop(std::false_type());
 
+    if constexpr (NS == 2) {
+        // the second-half waves hand their partial sums over in the (now free) block tiles, the
+        // first-half waves add them and write
+        __syncthreads();   // every wave is done with the last block's tiles
+        float *red = reinterpret_cast<float *>(&sm.q[0][0]);   // spans sm.q and sm.dO
+        static_assert(sizeof(sm.q) + sizeof(sm.dO) >= 4 * NDB * 16 * 64 * sizeof(float),
+                      "room for four waves' accumulators");
+        const int slot = (p_role ? 0 : 2) + sub;
+        if (hf_own == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) red[((slot * NDB + db) * 16 + rr) * 64 + lane] = acc[db][rr];
+        }
+        __syncthreads();
+        if (hf_own == 1) return;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) acc[db][rr] += red[((slot * NDB + db) * 16 + rr) * 64 + lane];
+    }
+
     // epilogue: P waves write dV; dS waves write dK = R(-theta) (scale * dK_rot); both
     // unscaled by 1/sigma
     if (kvalid) {
@@ -390,6 +428,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
 
 namespace pk {
 
+// Items x KV heads up to which an item is split over two workgroups (NS = 2).
+constexpr unsigned kSplitGrid = 256;
+
 hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                          const void *krot, const void *v, const void *dout16, const float *lse2,
                          const float *dsum, const float *scale, const void *rope, float *dk,
@@ -398,10 +439,18 @@ hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qr
                                    dk, dv);
     a.items = m.bwd_items;
     const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hkv;
-    if (sh.d == 128)
-        k_attn_bwd_kv<128><<<grid, 512, 0, s>>>(a);
-    else
-        k_attn_bwd_kv<64><<<grid, 512, 0, s>>>(a);
+    const bool split = grid <= kSplitGrid;
+    if (sh.d == 128) {
+        if (split)
+            k_attn_bwd_kv<128, 2><<<2 * grid, 512, 0, s>>>(a);
+        else
+            k_attn_bwd_kv<128, 1><<<grid, 512, 0, s>>>(a);
+    } else {
+        if (split)
+            k_attn_bwd_kv<64, 2><<<2 * grid, 512, 0, s>>>(a);
+        else
+            k_attn_bwd_kv<64, 1><<<grid, 512, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
