@@ -310,24 +310,35 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
             }
         }
         __syncthreads();   // B1: P of both halves is in LDS
-        if (both) {
-            if (!p_role) {
-                dscore(0);
-                dscore(1);
-            } else {
-                pconv(0);
-                pconv(1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            grads(0);
-            grads(1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);         // 4 transposed operands ahead
+        if constexpr (NS == 1) {
+            // One path for every block that runs at all: a half that does not run gets a zero
+            // operand instead of a branch, so the accumulators keep their registers from block
+            // to block (separate whole-block and per-half paths made the register allocator copy
+            // them at every join).
+            if (run[0] | run[1]) {
 #pragma unroll
-            for (int m = 0; m < 4 * NDB - 4; ++m) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                for (int hf = 0; hf < 2; ++hf) {
+                    if (run[hf]) {
+                        if constexpr (!p_role)
+                            dscore(hf);
+                        else
+                            pconv(hf);
+                    } else {
+                        pb[hf][0] = zero_f16x8();
+                        pb[hf][1] = zero_f16x8();
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                grads(0);
+                grads(1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);     // 4 transposed operands ahead
+#pragma unroll
+                for (int m = 0; m < 4 * NDB - 4; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         } else {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
