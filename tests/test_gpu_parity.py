@@ -115,6 +115,43 @@ def test_fwd_bwd_small(case):
     compare("dv", to_np(res["dv"]), dv_ref)
 
 
+LAUNCH_SHAPE_CASES = [
+    # (T, hq, hkv, d): packs on either side of the launch-shape choices.  128-token items x KV
+    # heads <= 256 split each dK/dV item over two workgroups, and (from 64 up to twice the
+    # device's compute units) run the dQ kernel on a side stream; items x query heads <= 2048 give
+    # the forward 64-key tiles.
+    (4096, 8, 8, 64),      # 32 items: split, side stream, 64-key forward tiles
+    (4224, 16, 8, 64),     # 33 items: whole items, side stream, 64-key tiles
+    (4224, 64, 8, 64),     # 2112 forward workgroups: 32-key tiles
+    (8320, 8, 8, 128),     # 65 items x 8 = 520 > 512: one stream
+]
+
+
+@pytest.mark.parametrize("case", range(len(LAUNCH_SHAPE_CASES)))
+def test_launch_shape_boundaries(case):
+    t, hq, hkv, d = LAUNCH_SHAPE_CASES[case]
+    rng = np.random.default_rng(700 + case)
+    lengths = []
+    while sum(lengths) < t:
+        lengths.append(int(rng.integers(1, 600, endpoint=True)))
+    lengths[-1] -= sum(lengths) - t
+    lengths = [x for x in lengths if x > 0]
+    say("launch shapes", case, "T", t, "hq/hkv/d", hq, hkv, d, "n", len(lengths))
+    lens, q, k, v, do = synth.small_problem(700 + case, lengths, hq, hkv, d)
+    scale = 1.0 / math.sqrt(d)
+    res = run_pk(lens, q, k, v, do, scale)
+    kv_heads = [0, hkv - 1]
+    g = hq // hkv
+    heads = [h for kvh in kv_heads for h in range(kvh * g, (kvh + 1) * g)]
+    o_ref, lse_ref = O.attn_fwd(q, k, v, lens, scale, 1e4, heads=heads)
+    dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, scale, 1e4, kv_heads=kv_heads)
+    compare("out", to_np(res["out"]), o_ref)
+    compare("lse", to_np(res["lse"]), lse_ref, max_abs=LSE_MAX_ABS)
+    compare("dq", to_np(res["dq"]), dq_ref)
+    compare("dk", to_np(res["dk"]), dk_ref)
+    compare("dv", to_np(res["dv"]), dv_ref)
+
+
 SCALE_BASE_CASES = [
     # (softmax scale as a function of d, RoPE base, d, power-of-two factor on q and k)
     (lambda d: 1.0 / d, 1e4, 128, 4.0),
