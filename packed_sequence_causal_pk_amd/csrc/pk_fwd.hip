@@ -150,9 +150,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     // K_rot / V tiles stream into double-buffered swizzled LDS tiles with asynchronous
     // global->LDS copies: tile t+1 is in flight while tile t is computed, one barrier per tile.
     // Rows past T are clamped to row T-1 (finite data; the causal mask zeroes their weight).
+    // Whole tiles (every tile but possibly the first, the one holding row T - 1) are addressed
+    // from running pointers that step back one tile per issue, so an issue costs a 64-bit
+    // subtraction instead of a multiply.
+    const int64_t tstride = (int64_t)BK * a.hkv * D;
+    const f16 *kp = a.krot + ((int64_t)kb_hi * a.hkv + kvh) * D;
+    const f16 *vp = a.v + ((int64_t)kb_hi * a.hkv + kvh) * D;
     auto issue_tile = [&](int k0, int buf) {
-        tile_issue<D, BK>(lds_k[buf], a.krot, a.hkv, kvh, k0, T, loff);
-        tile_issue<D, BK>(lds_v[buf], a.v, a.hkv, kvh, k0, T, loff);
+        if (k0 + BK <= T) {
+            tile_copy_async_whole<D, BK, 4>(lds_k[buf], kp, (int64_t)a.hkv * D, loff);
+            tile_copy_async_whole<D, BK, 4>(lds_v[buf], vp, (int64_t)a.hkv * D, loff);
+        } else {
+            tile_issue<D, BK>(lds_k[buf], a.krot, a.hkv, kvh, k0, T, loff);
+            tile_issue<D, BK>(lds_v[buf], a.v, a.hkv, kvh, k0, T, loff);
+        }
+        kp -= tstride;
+        vp -= tstride;
     };
 
     auto tile = [&](auto bufc, int k0) __attribute__((always_inline)) {
