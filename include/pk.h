@@ -111,7 +111,7 @@ pk_status pk_meta_check(pk_meta_t meta, void *hip_stream, int32_t *status_host,
 /* Free the handle (host memory only; the caller's meta buffer is untouched). */
 pk_status pk_meta_destroy(pk_meta_t meta);
 
-/* Workspace bytes pk_attn_fwd needs: the rotated K and the RoPE cos/sin table. */
+/* Workspace bytes pk_attn_fwd needs: the rotated K and V as fp16, and the RoPE cos/sin table. */
 size_t pk_attn_fwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d);
 
 /* Forward ([UN-2023] "手动 Autograd", [N1N-2026] §2):
@@ -125,8 +125,9 @@ pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *
                       int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float rope_base,
                       void *out, float *lse, void *ws, size_t ws_bytes, void *hip_stream);
 
-/* Workspace bytes pk_attn_bwd needs: rotated Q and K, the RoPE table, rowsum(dout * out) and
- * the dout scale. */
+/* Workspace bytes pk_attn_bwd needs: the fp16 operands (rotated Q and K, V, scaled dout), the
+ * RoPE table, per-row values (rowsum(dout * out), lse) and the dout scale with its per-block
+ * maxima. */
 size_t pk_attn_bwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d);
 
 /* Backward of pk_attn_fwd for the loss sum(out * dout): float32 dq [T,hq,d], dk and dv
