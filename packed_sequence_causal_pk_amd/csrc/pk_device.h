@@ -97,6 +97,35 @@ __device__ __forceinline__ int tile_off(int r, int col) {
     return r * D + 8 * ((col >> 3) ^ swz<D>(r)) + (col & 7);
 }
 
+// 8 halves (one 16-byte chunk, col multiple of 8) of row r.
+template <int D>
+__device__ __forceinline__ f16x8 tile_row8(const f16 *tile, int r, int col) {
+    return *reinterpret_cast<const f16x8 *>(tile + tile_off<D>(r, col));
+}
+
+template <int D>
+__device__ __forceinline__ void tile_store8(f16 *tile, int r, int col, f16x8 v) {
+    *reinterpret_cast<f16x8 *>(tile + tile_off<D>(r, col)) = v;
+}
+
+// A operand (32 rows m x 16 k) of mfma32 taken transposed from a swizzled tile X:
+// A[m][k] = X[k0 + k][m0 + m] (k0 multiple of 4, m0 multiple of 32).  Two ds_read_b64_tr_b16:
+// within each 16-lane group, source lane j addresses the 4 halves X[kb + j/4][mb + 4(j%4) ..],
+// and lane i receives element i%4 of the halves read by source lanes i/4 + 4t (t = 0..3),
+// i.e. the 4 consecutive k of its own column m.
+template <int D>
+__device__ __forceinline__ f16x8 tile_a_tr(const f16 *tile, int k0, int m0) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+    const int r = k0 + 8 * (g >> 1) + (j >> 2);
+    const int col = m0 + 16 * (g & 1) + 4 * (j & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + tile_off<D>(r, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + tile_off<D>(r + 4, col)));
+    return __builtin_bit_cast(f16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // One global_load_lds per lane: `BYTES` (4 or 16) bytes from global address g land in LDS at
 // byte lds + BYTES * lane (lds is the wave-uniform LDS offset, passed through M0).  The load is
 // written as inline assembly on purpose: the compiler cannot tell which LDS bytes the builtin form
@@ -193,13 +222,9 @@ __device__ __forceinline__ void tile_issue(f16 *tile, const f16 *x, int H, int h
     }
 }
 
-// Per-lane byte offsets of the two ds_read_b64_tr_b16 that make up the transposed A operand
-// (32 rows m x 16 k) of mfma32 from a swizzled tile X, A[m][k] = X[k][32 db + m], for tile rows
-// [0, 16): within each 16-lane group, source lane j addresses the 4 halves X[8 (g/2) + j/4]
-// [32 db + 16 (g%2) + 4 (j%4) ..] (g the lane's group) and the same 4 rows further down, and lane
-// i receives element i%4 of the halves read by source lanes i/4 + 4t (t = 0..3), i.e. the 4
-// consecutive k of its own column m.  Rows k0 + 16 t add 32 D t bytes, the swizzle being
-// periodic in 16 rows.
+// Per-lane byte offsets of the two ds_read_b64_tr_b16 that make up the transposed operand of
+// columns [32 db, +32) and tile rows [0, 16) (the layout of tile_a_tr with k0 = 0, m0 = 32 db):
+// rows k0 + 16 t add 32 D t bytes, the swizzle being periodic in 16 rows.
 template <int D>
 __device__ __forceinline__ void tile_tr_offsets(uint32_t (&off)[D / 32][2]) {
     const int lane = threadIdx.x & 63, jj = lane & 15, g = lane >> 4;

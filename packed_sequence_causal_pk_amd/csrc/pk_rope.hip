@@ -143,6 +143,12 @@ __device__ __forceinline__ void bwd_dmax_block(const bf16 *__restrict__ dout, in
         blockmax[b] = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
 }
 
+// Store 4 floats as fp16 after scaling.
+__device__ __forceinline__ void store4s(f16 *p, const float x[4], float scale) {
+    const float y[4] = {x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale};
+    store4(p, y);
+}
+
 // The (cos, sin) table alone: one thread per (token, group of 4 rotation pairs).
 template <int D>
 __device__ __forceinline__ void rope_table_block(const int32_t *__restrict__ pos, int64_t T, float base,
