@@ -139,6 +139,25 @@ def layer_tensors(w: Workload, layer: int, seed: int = 0,
     return tuple(normal_bf16(s, [seed, layer, idx], w.input_scale) for idx, s in enumerate(shapes))
 
 
+# MoE routing workloads ([UN-2026] §3 names GPT-OSS's router): a 16384-token batch routed top-4
+# among 32 experts (gpt-oss-20b-shaped) or 128 experts (gpt-oss-120b-shaped).
+MOE_WORKLOADS = {
+    "gptoss20b": (16384, 32, 4),
+    "gptoss120b": (16384, 128, 4),
+}
+
+
+def router_indices(n_tokens: int, n_experts: int, top_k: int, seed: int = 0,
+                   skew: float = 1.0) -> np.ndarray:
+    """Synthetic router output int32 [n_tokens, top_k]: each token's top_k experts (distinct, by
+    descending logit) for logits N(0,1) plus a per-expert offset N(0, skew^2) that makes some
+    experts popular, as trained routers are.  A random draw only: no grouping arithmetic."""
+    rng = np.random.default_rng([seed, 77])
+    bias = rng.standard_normal(n_experts) * skew
+    logits = rng.standard_normal((n_tokens, n_experts)) + bias[None, :]
+    return np.argsort(-logits, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+
+
 def small_problem(seed: int, lengths, hq: int, hkv: int, d: int, scale: float = 1.0):
     """(lengths, q, k, v, dout) for an ad-hoc pack used by tests."""
     lengths = np.asarray(lengths, dtype=np.int32)

@@ -16,6 +16,7 @@ import os
 import numpy as np
 import torch
 
+from oracle import moe_oracle as MO
 from oracle import pk_oracle as O
 from packed_sequence_causal_pk_amd import synth
 
@@ -286,9 +287,80 @@ def pin_permutation_invariance():
         assert np.allclose(a, b, atol=1e-12)
 
 
+# ----------------------------------------------------------------------- materialised mask
+def pin_dense_mask():
+    """The T x T keep pattern: a hand-derived 6-token pack, and a walk over pairs of tokens of
+    random packs (same sequence, key not after the query)."""
+    with open(os.path.join(GOLDEN, "dense_mask_small.json")) as f:
+        g = json.load(f)
+    keep = O.dense_mask(g["lengths"]) == 0.0
+    assert [np.nonzero(r)[0].tolist() for r in keep] == g["visible"]
+    rng = np.random.default_rng(11)
+    for _ in range(10):
+        lens = rng.integers(1, 20, size=int(rng.integers(1, 8)))
+        keep = O.dense_mask(lens) == 0.0
+        owner = []
+        for s, n in enumerate(lens):
+            owner += [s] * int(n)
+        for i in range(len(owner)):
+            for j in range(len(owner)):
+                assert keep[i, j] == (owner[i] == owner[j] and j <= i)
+
+
+# --------------------------------------------------------------------------- MoE grouping
+def pin_moe_golden():
+    """A hand-derived grouping with an expert that receives nothing."""
+    with open(os.path.join(GOLDEN, "moe_group_tiny.json")) as f:
+        g = json.load(f)
+    r = MO.group_by_expert(g["router_indices"], g["n_experts"])
+    assert r["status"] == 0
+    for key in ("counts", "offsets", "perm", "inv"):
+        assert r[key].tolist() == g[key], key
+    top_k = len(g["router_indices"][0])
+    for e, toks in enumerate(g["tokens_per_expert"]):
+        assert MO.tokens_of_expert(r, e, top_k).tolist() == toks
+
+
+def pin_moe_bruteforce():
+    """Walk the assignments token by token, slot by slot, appending each to its expert's list."""
+    rng = np.random.default_rng(12)
+    for _ in range(20):
+        n_tok, top_k, n_exp = int(rng.integers(0, 40)), int(rng.integers(1, 5)), int(rng.integers(1, 9))
+        idx = rng.integers(0, n_exp, size=(n_tok, top_k))
+        r = MO.group_by_expert(idx, n_exp)
+        lists = [[] for _ in range(n_exp)]
+        for t in range(n_tok):
+            for s in range(top_k):
+                lists[idx[t, s]].append(t * top_k + s)
+        assert r["counts"].tolist() == [len(x) for x in lists]
+        assert r["perm"].tolist() == sum(lists, [])
+        start = 0
+        for e in range(n_exp):
+            assert r["offsets"][e] == start
+            start += len(lists[e])
+        assert r["offsets"][n_exp] == n_tok * top_k
+
+
+def pin_moe_sort_and_bincount():
+    """The one-shot recipe through numpy's own routines: a stable argsort of the flattened
+    indices and a bincount give the same grouping; perm and inv are inverse permutations."""
+    for n_exp in (1, 32, 128):
+        idx = synth.router_indices(500, n_exp, min(4, n_exp), seed=3)
+        r = MO.group_by_expert(idx, n_exp)
+        flat = idx.reshape(-1)
+        assert r["perm"].tolist() == np.argsort(flat, kind="stable").tolist()
+        assert r["counts"].tolist() == np.bincount(flat, minlength=n_exp).tolist()
+        assert np.all(r["inv"][r["perm"]] == np.arange(flat.shape[0]))
+        assert np.all(np.diff(flat[r["perm"]]) >= 0)
+    bad = MO.group_by_expert([[0, 5]], 5)
+    assert bad["status"] == MO.STATUS_BAD_EXPERT
+    assert MO.group_by_expert([[-1, 0]], 5)["status"] == MO.STATUS_BAD_EXPERT
+
+
 ALL_PINS = [
     pin_meta_golden, pin_meta_bruteforce, pin_worklist_coverage, pin_rope,
     pin_fwd_dense_equals_per_sequence, pin_fwd_rows_and_closed_forms, pin_fwd_lse_reconstruction,
     pin_torch_sdpa_and_autograd, pin_bwd_finite_differences, pin_bwd_invariants,
-    pin_permutation_invariance,
+    pin_permutation_invariance, pin_dense_mask, pin_moe_golden, pin_moe_bruteforce,
+    pin_moe_sort_and_bincount,
 ]

@@ -4,6 +4,7 @@ A pin set that lets any of these through would not be strong enough to trust the
 import numpy as np
 import pytest
 
+from oracle import moe_oracle as MO
 from oracle import pk_oracle as O
 from tests import oracle_pins as P
 
@@ -51,6 +52,51 @@ def _cost_off_by_one(cu, seq_id, t, r=O.TILE_ROWS):
 
 
 _orig_work_lists = O.work_lists
+_orig_group = MO.group_by_expert
+
+
+def _group_slot_major(idx, n_experts):
+    """Mistake: assignments enumerated slot-major (a transposed operand) inside each group."""
+    idx = np.asarray(idx)
+    r = _orig_group(idx, n_experts)
+    if r["status"] or idx.size == 0:
+        return r
+    n_tok, top_k = idx.shape
+    perm = []
+    for e in range(n_experts):
+        s, t = np.nonzero(idx.T == e)
+        perm += (t * top_k + s).tolist()
+    r["perm"] = np.asarray(perm)
+    r["inv"][r["perm"]] = np.arange(len(perm))
+    return r
+
+
+def _group_inclusive_offsets(idx, n_experts):
+    """Mistake: offsets[e] taken as the end of group e instead of its start."""
+    r = _orig_group(idx, n_experts)
+    if not r["status"]:
+        r["offsets"] = np.concatenate([np.cumsum(r["counts"]), [r["n_assign"]]])
+    return r
+
+
+def _group_descending(idx, n_experts):
+    """Mistake: an unstable (reversed) order inside each group."""
+    r = _orig_group(idx, n_experts)
+    if not r["status"]:
+        o = r["offsets"]
+        r["perm"] = np.concatenate([r["perm"][o[e]:o[e + 1]][::-1] for e in range(n_experts)] or [r["perm"]])
+        r["inv"][r["perm"]] = np.arange(r["perm"].shape[0])
+    return r
+
+
+def _mask_strict(lengths):
+    """Mistake: the mask drops the diagonal."""
+    m = _orig_dense_mask(lengths)
+    np.fill_diagonal(m, -np.inf)
+    return m
+
+
+_orig_dense_mask = O.dense_mask
 
 MUTATIONS = {
     "gqa_interleaved_groups": ("kv_head_of", lambda h, g: h % g),
@@ -69,13 +115,18 @@ MUTATIONS = {
     "dQ_missing_scale": ("query_grad", lambda ds, kr, scale: ds @ kr),
     "dK_transposed_operand": ("key_grad", lambda ds, qr, scale: scale * (ds @ qr)),
     "worklist_short_range": ("work_lists", _cost_off_by_one),
+    "dense_mask_strict": ("dense_mask", _mask_strict),
+    "moe_slot_major": (MO, "group_by_expert", _group_slot_major),
+    "moe_inclusive_offsets": (MO, "group_by_expert", _group_inclusive_offsets),
+    "moe_unstable_order": (MO, "group_by_expert", _group_descending),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_mutation_is_caught(name, monkeypatch):
-    attr, fn = MUTATIONS[name]
-    monkeypatch.setattr(O, attr, fn)
+    spec = MUTATIONS[name]
+    mod, attr, fn = spec if len(spec) == 3 else (O,) + spec
+    monkeypatch.setattr(mod, attr, fn)
     failures = _run_all_pins()
     assert failures, "mutation %s passed every pin" % name
 
