@@ -8,7 +8,7 @@
  *             every layer consumes the same B, so it is built once and used L times, and no
  *             per-layer device-to-host synchronisation is allowed on the path.
  *             §3 (MoE routing): group once with a stable sort + counts instead of one dynamic
- *             query per group -- the pattern the work-list build follows.
+ *             query per group -- the pattern the work-list build follows, and pk_moe_group.
  *   [UN-2023] "Introducing Unsloth：LLM 训练提速 30 倍" (dbyun.net/tutorial/10038),
  *             "手动 Autograd": A(X) = softmax(Q K^T / sqrt(d) + M) V;
  *             "OpenAI Triton kernels": rotate-half RoPE on the two halves of the head dim.
@@ -142,6 +142,53 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
                       float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
                       void *hip_stream);
 
+/* ---- Steps around the attention path, each usable on its own -------------------------- */
+
+#define PK_MASK_MAX_TOKENS 65536  /* largest pack pk_dense_mask accepts (a 4 GiB mask) */
+
+/* Materialised keep pattern of the pack: mask[i * T + j] = 1 when key j is visible to query i
+ * (same packed sequence and j <= i), else 0; T = the meta's token count.  This is the T x T
+ * structure the pages' uncached path rebuilds for every layer ([UN-2026] §1 "快速合理性验证":
+ * the packed SDPA mask rebuild is the dominant repeated cost) -- the attention calls above never
+ * form or read it; it serves as the baseline that caching B removes.  Byte layout = torch.bool.
+ * `mask` is device memory of at least T * T bytes, 16-byte aligned; T <= PK_MASK_MAX_TOKENS
+ * (else PK_ERR_UNSUPPORTED).  A meta whose status word is set yields an all-zero mask. */
+pk_status pk_dense_mask(pk_meta_t meta, uint8_t *mask, size_t mask_bytes, void *hip_stream);
+
+/* Rotate-half RoPE of one bfloat16 tensor x [T, h, d] at each token's position inside its
+ * packed sequence ([UN-2023] "OpenAI Triton kernels": out1 = x1 cos - x2 sin,
+ * out2 = x2 cos + x1 sin over the halves of the head dim; the angle of pair i at position p is
+ * p * rope_base^(-2i/d)).  inverse != 0 applies the transpose rotation (sin -> -sin), the
+ * backward of the forward rotation.  Arithmetic in float32 from double-precision angles, result
+ * rounded to bfloat16 (nearest even).  `out` [T, h, d] bfloat16 may be `x` itself (in place).
+ * d in {64, 128}, 1 <= h <= 1024.  A meta whose status word is set yields zeros. */
+pk_status pk_rope_apply(pk_meta_t meta, const void *x, int32_t h, int32_t d, float rope_base,
+                        int32_t inverse, void *out, void *hip_stream);
+
+#define PK_MOE_MAX_EXPERTS 1024    /* largest expert count pk_moe_group accepts */
+#define PK_MOE_MAX_ASSIGN (1 << 26) /* largest n_tokens * top_k */
+#define PK_MOE_BAD_EXPERT 1        /* status bit: some router index lies outside [0, n_experts) */
+
+/* Workspace bytes of pk_moe_group (per-chunk counts), 0 for unsupported sizes. */
+size_t pk_moe_group_workspace_bytes(int64_t n_assign, int32_t n_experts);
+
+/* Group MoE routing assignments by expert in one pass ([UN-2026] §3: flatten the router's
+ * [n_tokens, top_k] indices, sort them stably by expert, count per expert, offsets from the
+ * counts, split) with no host round trip.  With M = n_tokens * top_k and f = token * top_k + slot:
+ *   counts  [n_experts]     assignments per expert
+ *   offsets [n_experts + 1] start of each expert's group; offsets[n_experts] = M when all valid
+ *   perm    [M]             flat assignment at each grouped position (inside a group: ascending f)
+ *   inv     [M]             grouped position of each flat assignment (-1 for an invalid index)
+ *   status  [1]             0, or PK_MOE_BAD_EXPERT when an index lies outside [0, n_experts);
+ *                           then the other outputs hold the grouping of the valid assignments.
+ * All int32 device buffers written in full (perm and inv may be NULL when M = 0); `ws` holds at
+ * least pk_moe_group_workspace_bytes bytes, 256-byte aligned.  Results are deterministic.
+ * 1 <= n_experts <= PK_MOE_MAX_EXPERTS, top_k >= 1, M <= PK_MOE_MAX_ASSIGN. */
+pk_status pk_moe_group(const int32_t *router_indices, int64_t n_tokens, int32_t top_k,
+                       int32_t n_experts, int32_t *counts, int32_t *offsets, int32_t *perm,
+                       int32_t *inv, int32_t *status, void *ws, size_t ws_bytes,
+                       void *hip_stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *pk_status_str(pk_status status);
 
@@ -159,7 +206,10 @@ typedef enum pk_kernel_kind {
     PK_K_BWD_PREP = 3,    /* backward prologue: RoPE table, rotated Q/K, rowsum(dout*out), dout scale */
     PK_K_BWD = 4,         /* backward attention, key-tile outer: dK, dV */
     PK_K_BWD_DQ = 5,      /* backward attention, query-tile outer: dQ */
-    PK_K_COUNT = 6
+    PK_K_MASK = 6,        /* pk_dense_mask */
+    PK_K_ROPE = 7,        /* pk_rope_apply */
+    PK_K_MOE = 8,         /* all kernels of one pk_moe_group */
+    PK_K_COUNT = 9
 } pk_kernel_kind;
 #define PK_PROF_ALL ((1 << PK_K_COUNT) - 1)
 

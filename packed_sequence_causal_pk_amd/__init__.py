@@ -18,7 +18,7 @@ from ._lib import PkError, lib
 
 __all__ = ["PackedMeta", "build_meta", "attn_fwd", "attn_bwd", "fwd_workspace", "bwd_workspace",
            "PackedCausalAttention", "PkError", "tile_rows", "prof_enable", "prof_reset",
-           "prof_query"]
+           "prof_query", "dense_mask", "rope_apply", "moe_group", "moe_workspace"]
 
 
 def _torch():
@@ -188,6 +188,68 @@ def attn_bwd(meta: PackedMeta, q, k, v, out, lse, dout, softmax_scale: Optional[
                            _ptr(ws), ws.numel(), _stream_ptr(stream))
     _lib.check("pk_attn_bwd", rc)
     return dq, dk, dv
+
+
+def dense_mask(meta: PackedMeta, out=None, stream=None):
+    """The pack's T x T keep pattern as a torch.bool tensor (True: key visible to query), the
+    materialised structure the pages' uncached path rebuilds per layer."""
+    torch = _torch()
+    t = meta.total_tokens
+    out = torch.empty((t, t), dtype=torch.bool, device=meta.device) if out is None else out
+    if out.dtype != torch.bool or tuple(out.shape) != (t, t) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, T] bool tensor")
+    rc = lib().pk_dense_mask(meta.handle, _ptr(out), out.numel(), _stream_ptr(stream))
+    _lib.check("pk_dense_mask", rc)
+    return out
+
+
+def rope_apply(meta: PackedMeta, x, rope_base: float = 10000.0, inverse: bool = False, out=None,
+               stream=None):
+    """Rotate-half RoPE of bf16 x [T, h, d] at positions inside each packed sequence (the
+    transpose rotation when inverse).  out=x rotates in place."""
+    torch = _torch()
+    _check_inputs(meta, x)
+    if x.dtype != torch.bfloat16 or x.dim() != 3 or x.shape[0] != meta.total_tokens:
+        raise ValueError("x must be bf16 [T, h, d] with T the pack's token count")
+    out = torch.empty_like(x) if out is None else out
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must match x")
+    rc = lib().pk_rope_apply(meta.handle, _ptr(x), int(x.shape[1]), int(x.shape[2]),
+                             float(rope_base), 1 if inverse else 0, _ptr(out), _stream_ptr(stream))
+    _lib.check("pk_rope_apply", rc)
+    return out
+
+
+def moe_workspace(n_assign: int, n_experts: int, device):
+    torch = _torch()
+    n = int(lib().pk_moe_group_workspace_bytes(int(n_assign), int(n_experts)))
+    if n == 0:
+        raise PkError("pk_moe_group_workspace_bytes", _lib.PK_ERR_UNSUPPORTED)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_group(router_indices, n_experts: int, workspace=None, stream=None):
+    """Group int32 router indices [n_tokens, top_k] (CUDA) by expert in one pass.  Returns a dict
+    of int32 device tensors: counts [E], offsets [E+1], perm [M] (flat assignment token*top_k+slot
+    at each grouped position, ascending inside a group), inv [M] (grouped position of each flat
+    assignment) and status [1] (PK_MOE_BAD_EXPERT for an index outside [0, E)).  Nothing is
+    read back to the host."""
+    torch = _torch()
+    if router_indices.dtype != torch.int32 or not router_indices.is_cuda or router_indices.dim() != 2:
+        raise ValueError("router_indices must be a 2-D int32 CUDA tensor")
+    idx = router_indices.contiguous()
+    n_tok, top_k = int(idx.shape[0]), int(idx.shape[1])
+    m = n_tok * top_k
+    dev = idx.device
+    mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    res = {"counts": mk(n_experts), "offsets": mk(n_experts + 1), "perm": mk(m), "inv": mk(m),
+           "status": mk(1)}
+    ws = moe_workspace(m, n_experts, dev) if workspace is None else workspace
+    rc = lib().pk_moe_group(_ptr(idx), n_tok, top_k, int(n_experts), _ptr(res["counts"]),
+                            _ptr(res["offsets"]), _ptr(res["perm"]), _ptr(res["inv"]),
+                            _ptr(res["status"]), _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _lib.check("pk_moe_group", rc)
+    return res
 
 
 def prof_enable(on: bool = True, kinds=None) -> None:

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpk.so")
 
-SOURCES = ["pk_api.cpp", "pk_meta.hip", "pk_rope.hip", "pk_fwd.hip", "pk_bwd_kv.hip", "pk_bwd_q.hip"]
+SOURCES = ["pk_api.cpp", "pk_meta.hip", "pk_rope.hip", "pk_fwd.hip", "pk_bwd_kv.hip", "pk_bwd_q.hip",
+           "pk_aux.hip", "pk_moe.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

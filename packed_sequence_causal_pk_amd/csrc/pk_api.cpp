@@ -322,6 +322,61 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     return hip_status(e2);
 }
 
+pk_status pk_dense_mask(pk_meta_t meta, uint8_t *mask, size_t mask_bytes, void *hip_stream) {
+    if (!meta) return PK_ERR_INVALID;
+    const int64_t T = meta->total_tokens;
+    if (T > PK_MASK_MAX_TOKENS) return PK_ERR_UNSUPPORTED;
+    if (T == 0) return PK_OK;
+    if (!mask || (reinterpret_cast<uintptr_t>(mask) & 15)) return PK_ERR_INVALID;
+    if (mask_bytes < (size_t)(T * T)) return PK_ERR_CAPACITY;
+    if (!on_meta_device(meta)) return PK_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ProfScope ps(PK_K_MASK, s);
+    return hip_status(pk::launch_dense_mask(*meta, mask, s));
+}
+
+pk_status pk_rope_apply(pk_meta_t meta, const void *x, int32_t h, int32_t d, float rope_base,
+                        int32_t inverse, void *out, void *hip_stream) {
+    if (!meta) return PK_ERR_INVALID;
+    if ((d != 64 && d != 128) || h < 1 || h > 1024) return PK_ERR_UNSUPPORTED;
+    if (!(rope_base > 0.f)) return PK_ERR_INVALID;
+    if (meta->total_tokens == 0) return PK_OK;
+    if (!x || !out || (reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(out) & 15))
+        return PK_ERR_INVALID;
+    if (!on_meta_device(meta)) return PK_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ProfScope ps(PK_K_ROPE, s);
+    return hip_status(pk::launch_rope_apply(*meta, x, h, d, rope_base, inverse ? 1 : 0, out, s));
+}
+
+size_t pk_moe_group_workspace_bytes(int64_t n_assign, int32_t n_experts) {
+    if (n_assign < 0 || n_assign > PK_MOE_MAX_ASSIGN || n_experts < 1 || n_experts > PK_MOE_MAX_EXPERTS)
+        return 0;
+    const size_t nc = (size_t)pk::moe_chunks(n_assign);
+    return align256(nc * (size_t)n_experts * 4) + align256(nc * 4);
+}
+
+pk_status pk_moe_group(const int32_t *router_indices, int64_t n_tokens, int32_t top_k,
+                       int32_t n_experts, int32_t *counts, int32_t *offsets, int32_t *perm,
+                       int32_t *inv, int32_t *status, void *ws, size_t ws_bytes,
+                       void *hip_stream) {
+    if (n_tokens < 0 || top_k < 1) return PK_ERR_INVALID;
+    if (n_experts < 1 || n_experts > PK_MOE_MAX_EXPERTS) return PK_ERR_UNSUPPORTED;
+    if (n_tokens > PK_MOE_MAX_ASSIGN / top_k) return PK_ERR_UNSUPPORTED;
+    const int64_t M = n_tokens * top_k;
+    if (!counts || !offsets || !status || !ws || !aligned256(ws)) return PK_ERR_INVALID;
+    if (M > 0 && (!router_indices || !perm || !inv)) return PK_ERR_INVALID;
+    if (ws_bytes < pk_moe_group_workspace_bytes(M, n_experts)) return PK_ERR_CAPACITY;
+    const size_t nc = (size_t)pk::moe_chunks(M);
+    char *w = static_cast<char *>(ws);
+    int32_t *chunk_counts = reinterpret_cast<int32_t *>(w);
+    int32_t *chunk_bad = reinterpret_cast<int32_t *>(w + align256(nc * (size_t)n_experts * 4));
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ProfScope ps(PK_K_MOE, s);
+    return hip_status(pk::launch_moe_group(router_indices, M, n_experts, counts, offsets, perm, inv,
+                                           status, chunk_counts, chunk_bad, s));
+}
+
 const char *pk_status_str(pk_status status) {
     switch (status) {
         case PK_OK: return "ok";

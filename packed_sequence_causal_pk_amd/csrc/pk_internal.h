@@ -82,4 +82,15 @@ hipError_t launch_bwd_q(const AttnShape &sh, const pk_meta_s &m, const void *qro
                         const float *dsum, const float *scale, const void *rope, float *dq,
                         hipStream_t s);
 
+// Steps around the attention path (pk_aux.hip, pk_moe.hip).
+hipError_t launch_dense_mask(const pk_meta_s &m, uint8_t *mask, hipStream_t s);
+hipError_t launch_rope_apply(const pk_meta_s &m, const void *x, int H, int d, float base,
+                             int inverse, void *out, hipStream_t s);
+#define PK_MOE_CHUNK 4096   // assignments per workgroup of the grouping kernels
+int moe_chunks(int64_t M);
+// chunk_counts: [n_experts][moe_chunks(M)] int32, chunk_bad: [moe_chunks(M)] int32 (workspace)
+hipError_t launch_moe_group(const int32_t *idx, int64_t M, int E, int32_t *counts,
+                            int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *status,
+                            int32_t *chunk_counts, int32_t *chunk_bad, hipStream_t s);
+
 }  // namespace pk

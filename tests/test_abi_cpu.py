@@ -68,6 +68,40 @@ def test_host_side_rejections(lib):
     assert lib.pk_meta_check(None, None, None, None) == _lib.PK_ERR_INVALID
 
 
+def test_host_side_rejections_aux(lib):
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every case fails before any launch
+    assert lib.pk_dense_mask(None, fake, 1 << 20, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_rope_apply(None, fake, 2, 64, 1e4, 0, fake, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_moe_group_workspace_bytes(0, 1) > 0
+    assert lib.pk_moe_group_workspace_bytes(65536, 128) >= 128 * 16 * 4
+    assert lib.pk_moe_group_workspace_bytes(-1, 8) == 0
+    assert lib.pk_moe_group_workspace_bytes(16, 0) == 0
+    assert lib.pk_moe_group_workspace_bytes(16, _lib.PK_MOE_MAX_EXPERTS + 1) == 0
+    assert lib.pk_moe_group_workspace_bytes(_lib.PK_MOE_MAX_ASSIGN + 1, 8) == 0
+    ws = lib.pk_moe_group_workspace_bytes(64, 8)
+    ok = [fake, 16, 4, 8, fake, fake, fake, fake, fake, fake, ws, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["idx", "n_tok", "top_k", "n_exp", "counts", "offsets", "perm", "inv", "status",
+                 "ws", "ws_bytes", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return lib.pk_moe_group(*a)
+
+    assert call(n_tok=-1) == _lib.PK_ERR_INVALID
+    assert call(top_k=0) == _lib.PK_ERR_INVALID
+    assert call(n_exp=0) == _lib.PK_ERR_UNSUPPORTED
+    assert call(n_exp=_lib.PK_MOE_MAX_EXPERTS + 1) == _lib.PK_ERR_UNSUPPORTED
+    assert call(n_tok=_lib.PK_MOE_MAX_ASSIGN) == _lib.PK_ERR_UNSUPPORTED
+    assert call(idx=None) == _lib.PK_ERR_INVALID
+    assert call(perm=None) == _lib.PK_ERR_INVALID
+    assert call(counts=None) == _lib.PK_ERR_INVALID
+    assert call(status=None) == _lib.PK_ERR_INVALID
+    assert call(ws=ctypes.c_void_p(0x10004)) == _lib.PK_ERR_INVALID
+    assert call(ws_bytes=ws - 1) == _lib.PK_ERR_CAPACITY
+
+
 def test_status_strings_and_profiler_queries(lib):
     for code in (0, -1, -2, -3, -4, -5):
         assert _lib.status_str(code)

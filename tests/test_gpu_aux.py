@@ -1,0 +1,184 @@
+"""The steps around the attention path against the oracle, through the C ABI (needs an MI355X):
+the materialised T x T mask and the MoE grouping bit for bit, the standalone RoPE within the
+bfloat16 rounding bound (and the parity gate)."""
+import numpy as np
+import pytest
+import torch
+
+import packed_sequence_causal_pk_amd as pk
+from oracle import moe_oracle as MO
+from oracle import pk_oracle as O
+from packed_sequence_causal_pk_amd import synth
+from tests.gpu_helpers import compare, dev, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _meta(lengths, t=None):
+    lengths = np.asarray(lengths, np.int32)
+    t = int(lengths.sum()) if t is None else t
+    return pk.build_meta(torch.tensor(lengths, device="cuda"), t)
+
+
+# ------------------------------------------------------------------------- materialised mask
+@pytest.mark.parametrize("lengths", [[5, 1, 7], [1], [16], [3, 29], [37, 100, 5, 114],
+                                     "llama1b", "random"])
+def test_dense_mask_bit_exact(lengths):
+    if lengths == "llama1b":
+        lengths = synth.pack_lengths("llama1b")
+    elif lengths == "random":
+        lengths = synth.random_lengths(np.random.default_rng(5), 40, 1, 60)
+    lengths = np.asarray(lengths, np.int32)
+    t = int(lengths.sum())
+    say("dense mask T", t, "N", len(lengths))
+    meta = _meta(lengths)
+    out = torch.ones((t, t), dtype=torch.bool, device="cuda")
+    pk.dense_mask(meta, out=out)
+    torch.cuda.synchronize()
+    ref = O.dense_mask(lengths) == 0.0
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_dense_mask_sampled_rows_large():
+    # 8192-token pack (a 64 MiB mask): rows checked against the oracle's metadata one by one
+    name = "qwen06b"
+    lengths = synth.pack_lengths(name)
+    t = int(lengths.sum())
+    say("dense mask sampled rows", name, "T", t)
+    ref = O.build_meta(lengths, t)
+    mask = pk.dense_mask(_meta(lengths))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([rng.integers(0, t, 200), ref["cu_seqlens"][:-1],
+                                     ref["cu_seqlens"][1:] - 1, [t - 1]]))
+    got = mask[torch.tensor(rows, device="cuda")].cpu().numpy()
+    for r, row in zip(rows, got):
+        start = int(ref["cu_seqlens"][ref["seq_id"][r]])
+        expect = np.zeros(t, bool)
+        expect[start:r + 1] = True
+        assert np.array_equal(row, expect), r
+    assert int(mask.sum().item()) == O.unmasked_pairs(lengths)
+
+
+def test_dense_mask_invalid_meta_and_empty():
+    meta = _meta([3, 0, 5], 8)
+    out = torch.ones((8, 8), dtype=torch.bool, device="cuda")
+    pk.dense_mask(meta, out=out)
+    torch.cuda.synchronize()
+    assert not out.any().item()
+    empty = pk.dense_mask(_meta([], 0))
+    assert empty.shape == (0, 0)
+
+
+# ------------------------------------------------------------------------------ RoPE alone
+def _rope_bound(got, ref):
+    """bfloat16 rounding (nearest even) of the float32 rotation: |error| <= 2^-8 |ref| + 1e-5."""
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-5
+    bad = err > bound
+    assert not bad.any(), "RoPE outside the bf16 rounding bound at %d entries (worst %.3e)" % (
+        int(bad.sum()), float((err - bound).max()))
+
+
+@pytest.mark.parametrize("case", [("tiny", 2, 64), ("llama1b", 32, 64), ("qwen06b", 16, 128),
+                                  ("qwen14b", 8, 128), ("ragged", 3, 128)])
+@pytest.mark.parametrize("inverse", [False, True])
+def test_rope_apply_vs_oracle(case, inverse):
+    name, h, d = case
+    lengths = (synth.random_lengths(np.random.default_rng(3), 23, 1, 90) if name == "ragged"
+               else synth.pack_lengths(name))
+    t = int(lengths.sum())
+    say("rope", name, "T", t, "h", h, "d", d, "inverse", inverse)
+    x = synth.normal_bf16((t, h, d), [7, h, d])
+    meta = _meta(lengths)
+    got = to_np(pk.rope_apply(meta, dev(x), 10000.0, inverse=inverse))
+    ref_meta = O.build_meta(lengths, t)
+    ref = O.rope_apply(x, ref_meta["pos"], 10000.0, inverse=inverse)
+    compare("rope", got, ref)
+    _rope_bound(got, ref)
+
+
+def test_rope_apply_in_place_roundtrip_and_bases():
+    lengths = synth.pack_lengths("tiny")
+    t = int(lengths.sum())
+    meta = _meta(lengths)
+    pos = O.build_meta(lengths, t)["pos"]
+    x = synth.normal_bf16((t, 4, 128), [8, 1])
+    for base in (10000.0, 500000.0, 1e6):
+        say("rope in place, base", base)
+        tx = dev(x)
+        pk.rope_apply(meta, tx, base, out=tx)
+        fwd = to_np(tx)
+        _rope_bound(fwd, O.rope_apply(x, pos, base))
+        pk.rope_apply(meta, tx, base, inverse=True, out=tx)
+        back = to_np(tx)
+        # the transpose undoes the rotation: two bf16 roundings away from the input
+        compare("roundtrip", back, x.astype(np.float64))
+
+
+def test_rope_apply_invalid_meta_writes_zeros():
+    meta = _meta([4, -1, 5], 8)
+    x = torch.randn(8, 2, 64, device="cuda").bfloat16()
+    out = pk.rope_apply(meta, x)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+
+
+# --------------------------------------------------------------------------- MoE grouping
+def _moe_check(idx, n_experts, ws=None):
+    got = pk.moe_group(torch.tensor(np.ascontiguousarray(idx, np.int32), device="cuda"), n_experts,
+                       workspace=ws)
+    torch.cuda.synchronize()
+    ref = MO.group_by_expert(idx, n_experts)
+    assert int(got["status"].item()) == ref["status"] == 0
+    for key in ("counts", "offsets", "perm", "inv"):
+        assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+    return got
+
+
+@pytest.mark.parametrize("name", sorted(synth.MOE_WORKLOADS))
+def test_moe_group_workloads(name):
+    n_tok, n_exp, top_k = synth.MOE_WORKLOADS[name]
+    say("moe", name, n_tok, n_exp, top_k)
+    _moe_check(synth.router_indices(n_tok, n_exp, top_k), n_exp)
+
+
+@pytest.mark.parametrize("shape", [(0, 4, 8), (1, 1, 1), (5, 2, 1024), (3000, 1, 7),
+                                   (50001, 2, 64), (4096, 1, 2), (2048, 2, 1000), (777, 8, 256)])
+def test_moe_group_edges(shape):
+    n_tok, top_k, n_exp = shape
+    say("moe edge", shape)
+    rng = np.random.default_rng(n_tok + 31 * top_k + n_exp)
+    idx = rng.integers(0, n_exp, size=(n_tok, top_k))
+    _moe_check(idx, n_exp)
+
+
+def test_moe_group_all_to_one_expert_and_workspace_reuse():
+    ws = pk.moe_workspace(40000 * 2, 16, "cuda")
+    for n_tok, e in ((40000, 5), (1234, 15), (40000, 0)):
+        say("moe single expert", n_tok, e)
+        idx = np.full((n_tok, 2), e, np.int64)
+        idx[::7, 1] = (e + 1) % 16
+        _moe_check(idx, 16, ws)
+
+
+def test_moe_group_bad_index_sets_status():
+    idx = np.random.default_rng(4).integers(0, 8, size=(5000, 2))
+    idx[17, 1] = 8
+    idx[4000, 0] = -3
+    got = pk.moe_group(torch.tensor(idx.astype(np.int32), device="cuda"), 8)
+    torch.cuda.synchronize()
+    assert MO.group_by_expert(idx, 8)["status"] == MO.STATUS_BAD_EXPERT
+    assert int(got["status"].item()) == MO.STATUS_BAD_EXPERT
+    inv = got["inv"].cpu().numpy()
+    assert inv[17 * 2 + 1] == -1 and inv[4000 * 2] == -1
+    assert int(got["counts"].sum().item()) == idx.size - 2
+
+
+def test_moe_group_repeatable():
+    idx = torch.tensor(synth.router_indices(16384, 128, 4, seed=1), device="cuda")
+    a = pk.moe_group(idx, 128)
+    b = pk.moe_group(idx, 128)
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
