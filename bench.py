@@ -10,9 +10,13 @@ Prints ONE JSON line.  `value` is algorithmic fwd+bwd TFLOP/s over the timed ste
 (4*hq*d*P + 10*hq*d*P per layer, P = kept query/key pairs), `roofline` reports the dominant
 kernel (the backward) against the chip's dense 16-bit matrix peak, timed per launch with HIP
 events recorded by the library on its stream, and `cpu_baseline` times the float64 CPU oracle on
-a bounded sample of the same workload.  `other_workloads` adds short runs (3 steps) of the other
-seeded packs with their arithmetic intensity and the fraction of the attainable roofline
-min(peak, intensity x HBM bandwidth) they reach.
+a bounded sample of the same workload.  `other_workloads` adds short runs of the other seeded
+packs with their arithmetic intensity and the fraction of the attainable roofline
+min(peak, intensity x HBM bandwidth) they reach; on the 16- and 28-layer packs it also runs the
+step uncached (B rebuilt for every layer call, alone and with the materialised mask and a
+host-visible sync) against the cost model T_saved ~ (n - 1) s.  `steps_around` times the
+materialised mask, the standalone RoPE and the MoE grouping kernels, and the backward layer
+loop with activations reloaded from pinned host memory, single- and double-buffered.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen14b] [--no-cpu-baseline]
                     [--no-sweep]
@@ -41,6 +45,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="qwen14b")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--steps-around-only", action="store_true",
+                   help="time only the mask, RoPE, MoE-grouping and reload steps; print their JSON")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the short runs of the other packs reported under other_workloads")
     p.add_argument("--cpu-target-s", type=float, default=15.0,
@@ -52,16 +58,20 @@ def parse():
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_attn_bwd_kv_qwen14b_hbm_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "packed_sequence_causal_pk_amd", f)
-                  for f in ("csrc/pk_bwd_kv.hip", "csrc/pk_bwd.h", "csrc/pk_device.h", "build.py")]
+KERNEL_SOURCES = [os.path.join(ROOT, "packed_sequence_causal_pk_amd", "csrc", f)
+                  for f in ("pk_bwd_kv.hip", "pk_bwd.h", "pk_device.h")]
 
 
 def kernel_source_digest():
+    """Digest of the dK/dV kernel's sources and of the compiler flags its object is built with."""
     import hashlib
+    from packed_sequence_causal_pk_amd import build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(f, "rb") as fh:
             h.update(fh.read())
+    flags = build.COMMON_FLAGS + build.SOURCE_FLAGS.get("pk_bwd_kv.hip", [])
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
@@ -202,18 +212,39 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
                         w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws_b)
         return meta
 
-    def step_uncached():
+    mask_buf = torch.empty((T, T), dtype=torch.bool, device=dev) if uncached else None
+
+    def rebuild(full):
+        """The per-layer-call work an uncached path repeats: B itself, and with `full` also the
+        materialised T x T mask and a host-visible read of max_seqlen (a device-to-host sync),
+        the two costs the pages name for their unpatched path."""
+        meta = pk.build_meta(lengths_d, T)
+        if full:
+            pk.dense_mask(meta, out=mask_buf)
+            meta.check()
+        return meta
+
+    def step_uncached(full=False):
         # the same step with the metadata rebuilt for every layer call (no reuse across layers)
         metas = []
         for x in layers:
-            metas.append(pk.build_meta(lengths_d, T))
+            metas.append(rebuild(full))
             pk.attn_fwd(metas[-1], x["q"], x["k"], x["v"], w.softmax_scale, w.rope_base,
                         out=x["out"], lse=x["lse"], workspace=ws_f)
         for x in reversed(layers):
-            metas.append(pk.build_meta(lengths_d, T))
+            metas.append(rebuild(full))
             pk.attn_bwd(metas[-1], x["q"], x["k"], x["v"], x["out"], x["lse"], x["do"],
                         w.softmax_scale, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws_b)
         return metas
+
+    def rebuild_cost(full, n=50):
+        """Wall-clock cost s of one rebuild on its own, ms (mean of n, synchronised at the end)."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        metas = [rebuild(full) for _ in range(n)]
+        torch.cuda.synchronize()
+        del metas
+        return (time.perf_counter() - t0) * 1e3 / n
 
     for _ in range(warmup):
         step()
@@ -250,10 +281,15 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
     bd_ms, _, kern = timed(nb, list(KINDS))
     uncached_ms = None
     if uncached:
-        for _ in range(2):
-            step_uncached()
-        uncached_ms, _, _ = timed(steps, (), fn=step_uncached)
-    del layers, dq, dk, dv, ws_f, ws_b
+        uncached_ms = {}
+        for full in (False, True):
+            fn = (lambda: step_uncached(True)) if full else step_uncached
+            for _ in range(2):
+                fn()
+            key = "meta_mask_sync" if full else "meta"
+            uncached_ms[key] = {"step_ms": timed(steps, (), fn=fn)[0],
+                                "rebuild_ms": rebuild_cost(full)}
+    del layers, dq, dk, dv, ws_f, ws_b, mask_buf
     torch.cuda.empty_cache()
     fwd_flops, bwd_flops = attn_flops(lengths, w.hq, w.head_dim)
     layer_ms = step_ms / L
@@ -283,12 +319,192 @@ def summary(m):
         "arithmetic_intensity_flop_per_byte": round(ai, 1),
         "attainable_tflops": round(attainable, 1),
         "frac_of_attainable": round(m["tflops"] / attainable, 4),
-        **({} if m["uncached_step_ms"] is None else {
-            "uncached_ms_per_step": round(m["uncached_step_ms"], 4),
-            "cached_ms_per_step": round(m["step_ms"], 4),
-            "saved_ms_per_step": round(m["uncached_step_ms"] - m["step_ms"], 4),
-            "meta_rebuilds_per_uncached_step": 2 * m["L"]}),
+        **({} if m["uncached_step_ms"] is None else {"uncached": uncached_summary(m)}),
     }
+
+
+def uncached_summary(m):
+    """Cached vs uncached steps against the pages' cost model T_saved ~ (n - 1) s, with n the
+    rebuilds an uncached step makes (one per layer call: 2L here, forward and backward) and s
+    the cost of one rebuild measured on its own."""
+    n = 2 * m["L"]
+    out = {"cached_ms_per_step": round(m["step_ms"], 4), "rebuilds_per_uncached_step": n}
+    what = {"meta": "B rebuilt per layer call (this library's own build, no sync)",
+            "meta_mask_sync": "B + materialised T x T mask + host-visible max_seqlen read per layer call"}
+    for key, u in m["uncached_step_ms"].items():
+        saved = u["step_ms"] - m["step_ms"]
+        out[key] = {"what": what[key], "uncached_ms_per_step": round(u["step_ms"], 4),
+                    "saved_ms_per_step": round(saved, 4), "rebuild_ms": round(u["rebuild_ms"], 4),
+                    "predicted_saved_ms": round((n - 1) * u["rebuild_ms"], 4)}
+    return out
+
+
+def measure_reload(name="qwen06b", reps=3):
+    """The backward layer loop with each layer's q, k, v, out and lse copied back from pinned host
+    memory, single- and double-buffered through the library's reload pipeline, against the model
+    T_single ~ L (c + g) and T_double ~ c + (L - 1) max(c, g) + g, with c the copy of one layer
+    and g one layer's backward, each measured on its own."""
+    import torch
+
+    import packed_sequence_causal_pk_amd as pk
+    from packed_sequence_causal_pk_amd import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[name]
+    lengths = synth.pack_lengths(name)
+    T, L = w.total_tokens, w.layers
+    meta = pk.build_meta(torch.tensor(lengths, dtype=torch.int32, device=dev), T)
+    gen = torch.Generator(device=dev)
+    acts, douts = [], []
+    for l in range(L):
+        gen.manual_seed(2000 + l)
+        mk = lambda *shape: (torch.randn(*shape, generator=gen, device=dev) * w.input_scale).bfloat16()
+        q, k, v = mk(T, w.hq, w.head_dim), mk(T, w.hkv, w.head_dim), mk(T, w.hkv, w.head_dim)
+        out, lse = pk.attn_fwd(meta, q, k, v, w.softmax_scale, w.rope_base)
+        host = []
+        for x in (q, k, v, out, lse):
+            h = torch.empty(x.shape, dtype=x.dtype, pin_memory=True)
+            h.copy_(x)
+            host.append(h)
+        acts.append(host)
+        douts.append(mk(T, w.hq, w.head_dim))
+        del q, k, v, out, lse
+    slots = [[torch.empty(a.shape, dtype=a.dtype, device=dev) for a in acts[0]] for _ in range(2)]
+    dq = torch.empty(T, w.hq, w.head_dim, dtype=torch.float32, device=dev)
+    dk = torch.empty(T, w.hkv, w.head_dim, dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    ws = pk.bwd_workspace(meta, w.hq, w.hkv, w.head_dim)
+    pipe = pk.ReloadPipeline()
+    layer_bytes = sum(a.numel() * a.element_size() for a in acts[0])
+
+    def fetch(slot, l):
+        for dst, src in zip(slots[slot], acts[l]):
+            pipe.fetch(slot, dst, src)
+
+    def bwd(slot, l):
+        q, k, v, out, lse = slots[slot]
+        pk.attn_bwd(meta, q, k, v, out, lse, douts[l], w.softmax_scale, w.rope_base,
+                    dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    def loop(double):
+        order = list(reversed(range(L)))
+        if double:
+            fetch(0, order[0])
+        for i, l in enumerate(order):
+            s = i % 2 if double else 0
+            if not double:
+                fetch(0, l)
+            elif i + 1 < L:
+                fetch(1 - s, order[i + 1])
+            pipe.acquire(s)
+            bwd(s, l)
+            pipe.release(s)
+
+    def wall_ms(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    def copies_only():
+        for l in range(L):
+            fetch(l % 2, l)
+            pipe.acquire(l % 2)
+            pipe.release(l % 2)
+
+    def compute_only():
+        for l in range(L):
+            bwd(0, l)
+
+    c = wall_ms(copies_only, reps) / L
+    g = wall_ms(compute_only, reps) / L
+    single = wall_ms(lambda: loop(False), reps)
+    double = wall_ms(lambda: loop(True), reps)
+    pipe.close()
+    return {
+        "workload": name, "layers": L, "reloaded_per_layer": "q, k, v, out (bf16), lse (fp32)",
+        "bytes_per_layer": layer_bytes, "copy_ms_per_layer_c": round(c, 4),
+        "h2d_GBps": round(layer_bytes / (c * 1e-3) / 1e9, 1), "bwd_ms_per_layer_g": round(g, 4),
+        "single_ms": round(single, 3), "double_ms": round(double, 3),
+        "model_single_ms": round(L * (c + g), 3),
+        "model_double_ms": round(c + (L - 1) * max(c, g) + g, 3),
+        "saved_ms": round(single - double, 3), "model_saved_ms": round((L - 1) * min(c, g), 3),
+    }
+
+
+def measure_steps_around(pk_names=("llama1b", "qwen06b", "qwen14b")):
+    """The steps around the attention path, each timed per launch with the library's HIP event
+    pairs: the materialised mask and the standalone RoPE (HBM streams: GB/s against 8 TB/s), and
+    the MoE grouping (a latency-bound pass), with the per-expert data-dependent query it replaces
+    (one torch.where per expert, each sizing its output on the host) timed beside it."""
+    import torch
+
+    import packed_sequence_causal_pk_amd as pk
+    from packed_sequence_causal_pk_amd import synth
+
+    dev = torch.device("cuda:0")
+
+    def kind_avg_us(kind, fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        pk.prof_reset()
+        pk.prof_enable(True, kinds=[kind])
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        pk.prof_enable(False)
+        ms, cnt = pk.prof_query(kind)
+        return 1000.0 * ms / max(cnt, 1)
+
+    res = {"dense_mask": {}, "rope_apply": {}, "moe_group": {}}
+    for name in pk_names:
+        w = synth.WORKLOADS[name]
+        lengths = synth.pack_lengths(name)
+        T = w.total_tokens
+        meta = pk.build_meta(torch.tensor(lengths, dtype=torch.int32, device=dev), T)
+        mask = torch.empty((T, T), dtype=torch.bool, device=dev)
+        us = kind_avg_us("mask", lambda: pk.dense_mask(meta, out=mask), 20)
+        nbytes = T * T
+        res["dense_mask"][name] = {"T": T, "avg_us": round(us, 2), "bytes_written": nbytes,
+                                   "GBps": round(nbytes / us / 1e3, 1),
+                                   "frac_hbm": round(nbytes / us / 1e3 / HBM_GBS, 4)}
+        del mask
+        x = (torch.randn(T, w.hq, w.head_dim, device=dev) * w.input_scale).bfloat16()
+        y = torch.empty_like(x)
+        us = kind_avg_us("rope", lambda: pk.rope_apply(meta, x, w.rope_base, out=y), 20)
+        nbytes = 2 * x.numel() * 2
+        res["rope_apply"][name] = {"shape": [T, w.hq, w.head_dim], "avg_us": round(us, 2),
+                                   "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                                   "frac_hbm": round(nbytes / us / 1e3 / HBM_GBS, 4)}
+        del x, y
+    for name, (n_tok, n_exp, top_k) in sorted(synth.MOE_WORKLOADS.items()):
+        idx = torch.tensor(synth.router_indices(n_tok, n_exp, top_k), device=dev)
+        M = n_tok * top_k
+        ws = pk.moe_workspace(M, n_exp, dev)
+        us = kind_avg_us("moe", lambda: pk.moe_group(idx, n_exp, workspace=ws), 50)
+
+        def per_expert_where():
+            return [torch.where(idx == e)[0] for e in range(n_exp)]
+        for _ in range(2):
+            per_expert_where()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            per_expert_where()
+        torch.cuda.synchronize()
+        naive_us = (time.perf_counter() - t0) * 1e6 / 5
+        res["moe_group"][name] = {
+            "n_tokens": n_tok, "n_experts": n_exp, "top_k": top_k, "avg_us": round(us, 2),
+            "assignments_per_s": round(M / (us * 1e-6), 1),
+            "algorithmic_bytes": 12 * M + 8 * n_exp + 8, "bound": "latency (3 launches)",
+            "per_expert_where_us": round(naive_us, 1),
+            "speedup_vs_per_expert_where": round(naive_us / us, 1)}
+    res["reload"] = measure_reload()
+    return res
 
 
 def main():
@@ -298,6 +514,9 @@ def main():
               "for how it would shard); --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    if args.steps_around_only:
+        print(json.dumps({"steps_around": measure_steps_around()}), flush=True)
+        return
     # the dK/dV kernel dominates the step on every pack measured here: its launches are timed
     # inside the timed region for the roofline
     m = measure(args.workload, args.steps, args.warmup, args.calibrate_copy_mib, timed_kinds=("bwd",))
@@ -365,6 +584,7 @@ def main():
             other[name] = summary(measure(name, 20 if small else 5, 3,
                                           uncached=name in ("llama1b", "qwen06b")))
         result["other_workloads"] = other
+        result["steps_around"] = measure_steps_around()
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, lengths, args.cpu_target_s)

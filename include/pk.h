@@ -15,6 +15,8 @@
  *   [N1N-2026] "利用 Unsloth 和 NVIDIA 硬件加速 LLM 训练：技术深度解析" (explore.n1n.ai),
  *             §2 "FlashAttention-2 的深度集成": tiles kept on chip, softmax fused with the
  *             products, no N x N matrix stored.
+ *             §2 (checkpoint reload): two device buffers so that copying activations back from
+ *             pinned host memory overlaps the backward -- pk_reload_*.
  *   [MV] "UnSloth极速微调：底层CUDA优化带来的变革" (maplevalley.com.cn), RoPE paragraph:
  *             positions' rotation factors served from a precomputed table.
  *
@@ -188,6 +190,39 @@ pk_status pk_moe_group(const int32_t *router_indices, int64_t n_tokens, int32_t 
                        int32_t n_experts, int32_t *counts, int32_t *offsets, int32_t *perm,
                        int32_t *inv, int32_t *status, void *ws, size_t ws_bytes,
                        void *hip_stream);
+
+/* ---- Double-buffered reload of activations from pinned host memory --------------------
+ * [UN-2026] §2 "用双缓冲检查点重载隐藏延迟": activations offloaded to pinned host memory are
+ * copied back for the backward; with one device buffer the copy and the backward that consumes it
+ * alternate (T ~ L (c + g)), with two the copy of the next layer overlaps the current layer's
+ * compute (T ~ c + (L - 1) max(c, g) + g).  A pipeline owns a copy stream (default priority) and
+ * two slots; the caller owns the device buffers of each slot and the pinned host memory (allocate
+ * it pinned, e.g. hipHostMalloc; pageable memory works but is not overlapped).  Ordering is by
+ * events only -- no call blocks the host except pk_reload_destroy, which waits for pending
+ * copies.  Typical loop over layers l = L-1 .. 0 with slot s = (L-1-l) % 2:
+ *     fetch(s0, layer L-1); for each l: fetch(1-s, layer l-1); acquire(s, stream);
+ *     backward(l) on stream; release(s, stream).
+ * One pipeline is used from one device; calls on it are serialised internally. */
+typedef struct pk_reload_s *pk_reload_t;
+
+/* Create a pipeline on the current device.  *out receives the handle. */
+pk_status pk_reload_create(pk_reload_t *out /* host */);
+
+/* Enqueue on the pipeline's copy stream a copy of `bytes` from host memory `src_host` to device
+ * memory `dst` (a buffer of slot `slot`, 0 or 1), after the compute work that the last
+ * pk_reload_release(slot) marked.  Several fetches may fill one slot. */
+pk_status pk_reload_fetch(pk_reload_t r, int32_t slot, void *dst, const void *src_host,
+                          size_t bytes);
+
+/* Make `hip_stream` wait until every fetch issued so far into `slot` has landed. */
+pk_status pk_reload_acquire(pk_reload_t r, int32_t slot, void *hip_stream);
+
+/* Mark the work enqueued so far on `hip_stream` as the last use of `slot`'s buffers: the next
+ * fetch into the slot waits for it. */
+pk_status pk_reload_release(pk_reload_t r, int32_t slot, void *hip_stream);
+
+/* Wait for pending copies, then free the stream and events. */
+pk_status pk_reload_destroy(pk_reload_t r);
 
 /* Human-readable name of a status code (static storage). */
 const char *pk_status_str(pk_status status);

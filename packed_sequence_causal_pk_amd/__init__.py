@@ -18,7 +18,8 @@ from ._lib import PkError, lib
 
 __all__ = ["PackedMeta", "build_meta", "attn_fwd", "attn_bwd", "fwd_workspace", "bwd_workspace",
            "PackedCausalAttention", "PkError", "tile_rows", "prof_enable", "prof_reset",
-           "prof_query", "dense_mask", "rope_apply", "moe_group", "moe_workspace"]
+           "prof_query", "dense_mask", "rope_apply", "moe_group", "moe_workspace",
+           "ReloadPipeline"]
 
 
 def _torch():
@@ -250,6 +251,43 @@ def moe_group(router_indices, n_experts: int, workspace=None, stream=None):
                             _ptr(res["status"]), _ptr(ws), ws.numel(), _stream_ptr(stream))
     _lib.check("pk_moe_group", rc)
     return res
+
+
+class ReloadPipeline:
+    """Two-slot reload of tensors from pinned host memory on a library-owned copy stream
+    (pk_reload_*): fetch(slot, dst, src) copies host -> device after the slot's last release;
+    acquire(slot) makes the current stream wait for the slot's copies; release(slot) marks the
+    current stream's work so far as the slot's last use."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _lib.check("pk_reload_create", lib().pk_reload_create(ctypes.byref(h)))
+        self._h = h
+
+    def fetch(self, slot: int, dst, src) -> None:
+        if not dst.is_cuda or src.is_cuda or not dst.is_contiguous() or not src.is_contiguous():
+            raise ValueError("dst must be a contiguous CUDA tensor and src a contiguous host tensor")
+        n = dst.numel() * dst.element_size()
+        if src.numel() * src.element_size() != n:
+            raise ValueError("size mismatch")
+        _lib.check("pk_reload_fetch", lib().pk_reload_fetch(self._h, int(slot), _ptr(dst), _ptr(src), n))
+
+    def acquire(self, slot: int, stream=None) -> None:
+        _lib.check("pk_reload_acquire", lib().pk_reload_acquire(self._h, int(slot), _stream_ptr(stream)))
+
+    def release(self, slot: int, stream=None) -> None:
+        _lib.check("pk_reload_release", lib().pk_reload_release(self._h, int(slot), _stream_ptr(stream)))
+
+    def close(self) -> None:
+        if self._h is not None:
+            lib().pk_reload_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def prof_enable(on: bool = True, kinds=None) -> None:

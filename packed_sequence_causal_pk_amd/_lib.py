@@ -61,6 +61,11 @@ SIGNATURES = {
     "pk_rope_apply": (_i32, [_vp, _vp, _i32, _i32, _f32, _i32, _vp, _vp]),
     "pk_moe_group_workspace_bytes": (_sz, [_i64, _i32]),
     "pk_moe_group": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pk_reload_create": (_i32, [ctypes.POINTER(_vp)]),
+    "pk_reload_fetch": (_i32, [_vp, _i32, _vp, _vp, _sz]),
+    "pk_reload_acquire": (_i32, [_vp, _i32, _vp]),
+    "pk_reload_release": (_i32, [_vp, _i32, _vp]),
+    "pk_reload_destroy": (_i32, [_vp]),
     "pk_status_str": (ctypes.c_char_p, [_i32]),
     "pk_prof_enable": (_i32, [_i32]),
     "pk_prof_reset": (_i32, []),

@@ -182,3 +182,51 @@ def test_moe_group_repeatable():
     torch.cuda.synchronize()
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+# ------------------------------------------------------------------ double-buffered reload
+@pytest.mark.parametrize("double", [False, True])
+def test_reload_pipeline_matches_resident(double):
+    """Backward of several layers whose q, k, v, out, lse come back from pinned host memory
+    through the two-slot pipeline: bit-identical to the backward on resident tensors (the
+    kernels are deterministic), so no layer ever read a slot before its copy landed or after the
+    next copy overwrote it."""
+    w = synth.WORKLOADS["llama1b"]
+    lengths = synth.pack_lengths("llama1b")
+    t, n_layers = w.total_tokens, 6
+    say("reload pipeline, double =", double)
+    meta = _meta(lengths)
+    acts, douts, ref = [], [], []
+    for l in range(n_layers):
+        q, k, v, do = (dev(a) for a in synth.layer_tensors(w, l))
+        out, lse = pk.attn_fwd(meta, q, k, v)
+        acts.append([x.cpu().pin_memory() for x in (q, k, v, out, lse)])
+        douts.append(do)
+        ref.append(pk.attn_bwd(meta, q, k, v, out, lse, do))
+    torch.cuda.synchronize()
+    slots = [[torch.empty_like(a, device="cuda") for a in acts[0]] for _ in range(2)]
+    pipe = pk.ReloadPipeline()
+    got = [None] * n_layers
+    order = list(reversed(range(n_layers)))
+
+    def fetch(slot, l):
+        for dst, src in zip(slots[slot], acts[l]):
+            pipe.fetch(slot, dst, src)
+
+    if double:
+        fetch(0, order[0])
+    for i, l in enumerate(order):
+        s = i % 2 if double else 0
+        if not double:
+            fetch(0, l)
+        elif i + 1 < n_layers:
+            fetch(1 - s, order[i + 1])
+        pipe.acquire(s)
+        q, k, v, out, lse = slots[s]
+        got[l] = pk.attn_bwd(meta, q, k, v, out, lse, douts[l])
+        pipe.release(s)
+    torch.cuda.synchronize()
+    pipe.close()
+    for l in range(n_layers):
+        for a, b in zip(got[l], ref[l]):
+            assert torch.equal(a, b), "layer %d" % l
