@@ -47,9 +47,6 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--steps-around-only", action="store_true",
                    help="time only the mask, RoPE, MoE-grouping and reload steps; print their JSON")
-    p.add_argument("--plain", action="store_true",
-                   help="time the plain pk_attn_fwd / pk_attn_bwd pair instead of the saving "
-                        "forward and saved-operand backward")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the short runs of the other packs reported under other_workloads")
     p.add_argument("--cpu-target-s", type=float, default=15.0,
@@ -158,13 +155,10 @@ def min_bytes(w, T):
 KINDS = ("meta", "fwd_prep", "fwd", "bwd_prep", "bwd", "bwd_dq")
 
 
-def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False, saved=True,
-            breakdown=True):
+def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False):
     """Time `steps` steps (after `warmup`) of one workload, timing the kernel kinds
     `timed_kinds` inside that region; a second, shorter pass times every kind for the
-    per-kernel breakdown.  With `saved` each layer's forward keeps the backward's fp16 operands
-    (pk_attn_fwd_save) and the backward runs on them (pk_attn_bwd_saved); otherwise the plain
-    pk_attn_fwd / pk_attn_bwd pair.  Returns the timings and shapes."""
+    per-kernel breakdown.  Returns the timings and shapes."""
     import torch
 
     import packed_sequence_causal_pk_amd as pk
@@ -194,26 +188,7 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
     meta0 = pk.build_meta(lengths_d, T)
     ws_f = pk.fwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
     ws_b = pk.bwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
-    if saved:
-        for x in layers:
-            x["saved"] = pk.saved_buffer(meta0, w.hq, w.hkv, w.head_dim)
     meta0.close()
-
-    def fwd(meta, x):
-        if saved:
-            pk.attn_fwd_save(meta, x["q"], x["k"], x["v"], w.softmax_scale, w.rope_base,
-                             out=x["out"], lse=x["lse"], saved=x["saved"], workspace=ws_f)
-        else:
-            pk.attn_fwd(meta, x["q"], x["k"], x["v"], w.softmax_scale, w.rope_base,
-                        out=x["out"], lse=x["lse"], workspace=ws_f)
-
-    def bwd(meta, x):
-        if saved:
-            pk.attn_bwd_saved(meta, x["saved"], x["out"], x["lse"], x["do"], w.hkv,
-                              w.softmax_scale, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws_b)
-        else:
-            pk.attn_bwd(meta, x["q"], x["k"], x["v"], x["out"], x["lse"], x["do"], w.softmax_scale,
-                        w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws_b)
     if calibrate_mib > 0:
         nbytes = calibrate_mib << 20
         src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
@@ -230,9 +205,11 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
     def step():
         meta = pk.build_meta(lengths_d, T)  # once per pack; every layer reuses it
         for x in layers:
-            fwd(meta, x)
+            pk.attn_fwd(meta, x["q"], x["k"], x["v"], w.softmax_scale, w.rope_base,
+                        out=x["out"], lse=x["lse"], workspace=ws_f)
         for x in reversed(layers):
-            bwd(meta, x)
+            pk.attn_bwd(meta, x["q"], x["k"], x["v"], x["out"], x["lse"], x["do"], w.softmax_scale,
+                        w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws_b)
         return meta
 
     mask_buf = torch.empty((T, T), dtype=torch.bool, device=dev) if uncached else None
@@ -252,10 +229,12 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
         metas = []
         for x in layers:
             metas.append(rebuild(full))
-            fwd(metas[-1], x)
+            pk.attn_fwd(metas[-1], x["q"], x["k"], x["v"], w.softmax_scale, w.rope_base,
+                        out=x["out"], lse=x["lse"], workspace=ws_f)
         for x in reversed(layers):
             metas.append(rebuild(full))
-            bwd(metas[-1], x)
+            pk.attn_bwd(metas[-1], x["q"], x["k"], x["v"], x["out"], x["lse"], x["do"],
+                        w.softmax_scale, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws_b)
         return metas
 
     def rebuild_cost(full, n=50):
@@ -299,7 +278,7 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
           file=sys.stderr, flush=True)
     # a second pass times every kernel kind (for the per-kernel breakdown only)
     nb = max(2, steps // 2)
-    kern = timed(nb, list(KINDS))[2] if breakdown else None
+    bd_ms, _, kern = timed(nb, list(KINDS))
     uncached_ms = None
     if uncached:
         uncached_ms = {}
@@ -540,8 +519,7 @@ def main():
         return
     # the dK/dV kernel dominates the step on every pack measured here: its launches are timed
     # inside the timed region for the roofline
-    m = measure(args.workload, args.steps, args.warmup, args.calibrate_copy_mib, timed_kinds=("bwd",),
-                saved=not args.plain)
+    m = measure(args.workload, args.steps, args.warmup, args.calibrate_copy_mib, timed_kinds=("bwd",))
     w, lengths, T, L, kern = m["w"], m["lengths"], m["T"], m["L"], m["kern"]
     s = summary(m)
 
@@ -571,9 +549,7 @@ def main():
         "config": {
             "workload": args.workload, "description": w.description, "total_tokens": T,
             "n_seqs": int(len(lengths)), "hq": w.hq, "hkv": w.hkv, "head_dim": w.head_dim,
-            "layers": L, "step": "build meta once + %d layer forwards + %d layer backwards" % (L, L)
-            + ("" if args.plain else " (each forward keeps its layer's fp16 backward operands: "
-               "pk_attn_fwd_save / pk_attn_bwd_saved)"),
+            "layers": L, "step": "build meta once + %d layer forwards + %d layer backwards" % (L, L),
             "io_dtypes": "q/k/v/out/dout bf16, lse/dq/dk/dv fp32",
         },
         "tokens_per_s_per_layer": s["tokens_per_s_per_layer"],
@@ -597,11 +573,6 @@ def main():
         },
     }
     if not args.no_sweep:
-        # the same workload through the other API pair, a few steps (context for the choice)
-        alt = measure(args.workload, 3, 1, saved=args.plain, breakdown=False)
-        result["other_api_pair"] = {
-            "api": "pk_attn_fwd_save / pk_attn_bwd_saved" if args.plain else "pk_attn_fwd / pk_attn_bwd",
-            "ms_per_step": round(alt["step_ms"], 4), "tflops": round(alt["tflops"], 2)}
         # the other packs, a few steps each (their own figures; `value` is the workload above)
         other = {}
         for name in ("tiny", "llama1b", "qwen06b", "qwen14b", "skewed"):

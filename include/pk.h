@@ -144,33 +144,6 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
                       float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
                       void *hip_stream);
 
-/* ---- Saving forward and saved-operand backward ----------------------------------------
- * The backward's matrix operands are the rotated Q (times scale * log2(e)), the rotated K and V in
- * fp16 -- values the forward forms anyway (Q rotated in its registers, K and V in its prologue).
- * A training step keeps each layer's q, k, v until its backward in any case; a caller that keeps
- * this fp16 form instead (pk_attn_saved_bytes per layer: [T,hq,d] + 2 x [T,hkv,d] halves) lets
- * the backward skip reading and converting q, k, v again.  Results equal pk_attn_fwd /
- * pk_attn_bwd up to fp32 rounding order of the rotation. */
-
-/* Bytes of the saved buffer of one layer (0 for unsupported shapes). */
-size_t pk_attn_saved_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d);
-
-/* pk_attn_fwd that also fills `saved` (device, >= pk_attn_saved_bytes bytes, 256-byte aligned)
- * with the backward's fp16 operands; the workspace is pk_attn_fwd's. */
-pk_status pk_attn_fwd_save(pk_meta_t meta, const void *q, const void *k, const void *v,
-                           int32_t hq, int32_t hkv, int32_t d, float softmax_scale,
-                           float rope_base, void *out, float *lse, void *saved,
-                           size_t saved_bytes, void *ws, size_t ws_bytes, void *hip_stream);
-
-/* pk_attn_bwd on the operands a pk_attn_fwd_save of the same layer stored in `saved` (q, k, v
- * are not read).  softmax_scale and rope_base must be the ones that forward was given (the saved
- * Q carries the scale).  The workspace is pk_attn_bwd's. */
-pk_status pk_attn_bwd_saved(pk_meta_t meta, const void *saved, size_t saved_bytes,
-                            const void *out, const float *lse, const void *dout, int32_t hq,
-                            int32_t hkv, int32_t d, float softmax_scale, float rope_base,
-                            float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
-                            void *hip_stream);
-
 /* ---- Steps around the attention path, each usable on its own -------------------------- */
 
 #define PK_MASK_MAX_TOKENS 65536  /* largest pack pk_dense_mask accepts (a 4 GiB mask) */

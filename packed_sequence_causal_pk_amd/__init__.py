@@ -19,7 +19,7 @@ from ._lib import PkError, lib
 __all__ = ["PackedMeta", "build_meta", "attn_fwd", "attn_bwd", "fwd_workspace", "bwd_workspace",
            "PackedCausalAttention", "PkError", "tile_rows", "prof_enable", "prof_reset",
            "prof_query", "dense_mask", "rope_apply", "moe_group", "moe_workspace",
-           "ReloadPipeline", "saved_buffer", "attn_fwd_save", "attn_bwd_saved"]
+           "ReloadPipeline"]
 
 
 def _torch():
@@ -288,59 +288,6 @@ class ReloadPipeline:
             self.close()
         except Exception:
             pass
-
-
-def saved_buffer(meta: PackedMeta, hq: int, hkv: int, d: int):
-    """Device buffer for one layer's saved backward operands (pk_attn_saved_bytes)."""
-    torch = _torch()
-    n = int(lib().pk_attn_saved_bytes(meta.handle, hq, hkv, d))
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=meta.device)
-
-
-def attn_fwd_save(meta: PackedMeta, q, k, v, softmax_scale: Optional[float] = None,
-                  rope_base: float = 10000.0, out=None, lse=None, saved=None, workspace=None,
-                  stream=None):
-    """attn_fwd that also stores the backward's fp16 operands; returns (out, lse, saved)."""
-    torch = _torch()
-    t, hq, hkv, d = _dims(q, k)
-    _check_inputs(meta, q, k, v)
-    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
-        raise ValueError("q, k, v must be bfloat16")
-    if t != meta.total_tokens or k.shape != v.shape or k.shape[0] != t or k.shape[2] != d:
-        raise ValueError("shape mismatch with the pack")
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((hq, t), dtype=torch.float32, device=q.device) if lse is None else lse
-    saved = saved_buffer(meta, hq, hkv, d) if saved is None else saved
-    ws = fwd_workspace(meta, hq, hkv, d) if workspace is None else workspace
-    rc = lib().pk_attn_fwd_save(meta.handle, _ptr(q), _ptr(k), _ptr(v), hq, hkv, d, scale,
-                                float(rope_base), _ptr(out), _ptr(lse), _ptr(saved), saved.numel(),
-                                _ptr(ws), ws.numel(), _stream_ptr(stream))
-    _lib.check("pk_attn_fwd_save", rc)
-    return out, lse, saved
-
-
-def attn_bwd_saved(meta: PackedMeta, saved, out, lse, dout, hkv: int,
-                   softmax_scale: Optional[float] = None, rope_base: float = 10000.0, dq=None,
-                   dk=None, dv=None, workspace=None, stream=None):
-    """attn_bwd on the operands attn_fwd_save stored (q, k, v not needed): (dq, dk, dv) fp32."""
-    torch = _torch()
-    t, hq, d = (int(x) for x in out.shape)
-    _check_inputs(meta, saved, out, lse, dout)
-    if t != meta.total_tokens or dout.shape != out.shape:
-        raise ValueError("shape mismatch with the pack")
-    if dout.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or lse.dtype != torch.float32:
-        raise ValueError("out/dout must be bfloat16 and lse float32")
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    dq = torch.empty((t, hq, d), dtype=torch.float32, device=out.device) if dq is None else dq
-    dk = torch.empty((t, hkv, d), dtype=torch.float32, device=out.device) if dk is None else dk
-    dv = torch.empty((t, hkv, d), dtype=torch.float32, device=out.device) if dv is None else dv
-    ws = bwd_workspace(meta, hq, hkv, d) if workspace is None else workspace
-    rc = lib().pk_attn_bwd_saved(meta.handle, _ptr(saved), saved.numel(), _ptr(out), _ptr(lse),
-                                 _ptr(dout), hq, hkv, d, scale, float(rope_base), _ptr(dq), _ptr(dk),
-                                 _ptr(dv), _ptr(ws), ws.numel(), _stream_ptr(stream))
-    _lib.check("pk_attn_bwd_saved", rc)
-    return dq, dk, dv
 
 
 def prof_enable(on: bool = True, kinds=None) -> None:

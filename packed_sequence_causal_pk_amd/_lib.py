@@ -57,11 +57,6 @@ SIGNATURES = {
     "pk_attn_bwd_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
     "pk_attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32,
                            _vp, _vp, _vp, _vp, _sz, _vp]),
-    "pk_attn_saved_bytes": (_sz, [_vp, _i32, _i32, _i32]),
-    "pk_attn_fwd_save": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp, _sz,
-                                _vp, _sz, _vp]),
-    "pk_attn_bwd_saved": (_i32, [_vp, _vp, _sz, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32,
-                                 _vp, _vp, _vp, _vp, _sz, _vp]),
     "pk_dense_mask": (_i32, [_vp, _vp, _sz, _vp]),
     "pk_rope_apply": (_i32, [_vp, _vp, _i32, _i32, _f32, _i32, _vp, _vp]),
     "pk_moe_group_workspace_bytes": (_sz, [_i64, _i32]),

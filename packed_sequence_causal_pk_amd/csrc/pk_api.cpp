@@ -136,123 +136,7 @@ BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d) {
     return w;
 }
 
-SavedLayout saved_layout(int64_t T, int hq, int hkv, int d) {
-    SavedLayout w;
-    size_t off = 0;
-    w.qrot = off; off += align256((size_t)T * hq * d * 2);
-    w.krot = off; off += align256((size_t)T * hkv * d * 2);
-    w.vh = off; off += align256((size_t)T * hkv * d * 2);
-    w.total = off;
-    return w;
-}
-
 }  // namespace pk
-
-namespace {
-
-// Forward of one layer; with `saved` the fp16 operands of the backward (rotated K, V, and
-// rotated Q times scale * log2(e)) go there, else rotated K and V go to the workspace.
-pk_status fwd_impl(pk_meta_t meta, const void *q, const void *k, const void *v, int32_t hq,
-                   int32_t hkv, int32_t d, float softmax_scale, float rope_base, void *out,
-                   float *lse, void *saved, size_t saved_bytes, void *ws, size_t ws_bytes,
-                   void *hip_stream) {
-    if (!meta) return PK_ERR_INVALID;
-    if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
-    if (!(softmax_scale > 0.f) || !(rope_base > 0.f)) return PK_ERR_INVALID;
-    const int64_t T = meta->total_tokens;
-    if (T == 0) return PK_OK;
-    if (!q || !k || !v || !out || !lse || !ws || !aligned256(ws)) return PK_ERR_INVALID;
-    const pk::FwdWorkspace W = pk::fwd_workspace(T, hq, hkv, d);
-    if (ws_bytes < W.total) return PK_ERR_CAPACITY;
-    const pk::SavedLayout S = pk::saved_layout(T, hq, hkv, d);
-    if (saved && !aligned256(saved)) return PK_ERR_INVALID;
-    if (saved && saved_bytes < S.total) return PK_ERR_CAPACITY;
-    if (!on_meta_device(meta)) return PK_ERR_INVALID;
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    char *w = static_cast<char *>(ws);
-    char *sv = static_cast<char *>(saved);
-    void *krot = saved ? sv + S.krot : w + W.krot;
-    void *vh = saved ? sv + S.vh : w + W.vh;
-    pk::RopeArgs ra{meta->pos, T, hq, hkv, d, rope_base};
-    hipError_t e;
-    {
-        ProfScope ps(PK_K_FWD_PREP, s);
-        e = pk::launch_fwd_prep(ra, k, v, krot, vh, w + W.rope, s);
-    }
-    if (e != hipSuccess) return PK_ERR_HIP;
-    pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
-    {
-        ProfScope ps(PK_K_FWD, s);
-        e = pk::launch_fwd(sh, *meta, q, krot, vh, w + W.rope, out, lse, saved ? sv + S.qrot : nullptr, s);
-    }
-    return hip_status(e);
-}
-
-// Backward of one layer.  With q == nullptr the fp16 operands come from `saved` (a saving
-// forward's buffer); otherwise the prologue writes them into the workspace.
-pk_status bwd_impl(pk_meta_t meta, const void *q, const void *k, const void *v,
-                   const void *saved, const void *out, const float *lse, const void *dout,
-                   int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float rope_base,
-                   float *dq, float *dk, float *dv, void *ws, size_t ws_bytes, void *hip_stream) {
-    if (!meta) return PK_ERR_INVALID;
-    if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
-    if (!(softmax_scale > 0.f) || !(rope_base > 0.f)) return PK_ERR_INVALID;
-    const int64_t T = meta->total_tokens;
-    if (T == 0) return PK_OK;
-    if (!out || !lse || !dout || !dq || !dk || !dv || !ws || !aligned256(ws)) return PK_ERR_INVALID;
-    if (saved ? !aligned256(saved) : (!q || !k || !v)) return PK_ERR_INVALID;
-    const pk::BwdWorkspace W = pk::bwd_workspace(T, hq, hkv, d);
-    if (ws_bytes < W.total) return PK_ERR_CAPACITY;
-    if (!on_meta_device(meta)) return PK_ERR_INVALID;
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    char *w = static_cast<char *>(ws);
-    const pk::SavedLayout S = pk::saved_layout(T, hq, hkv, d);
-    const char *sv = static_cast<const char *>(saved);
-    void *qrot = saved ? (void *)(sv + S.qrot) : w + W.qrot;
-    void *krot = saved ? (void *)(sv + S.krot) : w + W.krot;
-    void *vh = saved ? (void *)(sv + S.vh) : w + W.vh;
-    float *dsum = reinterpret_cast<float *>(w + W.dsum);
-    float *lse2 = reinterpret_cast<float *>(w + W.lse2);
-    float *blockmax = reinterpret_cast<float *>(w + W.blockmax);
-    float *scale = reinterpret_cast<float *>(w + W.scale);
-    pk::RopeArgs ra{meta->pos, T, hq, hkv, d, rope_base};
-    hipError_t e;
-    {
-        ProfScope ps(PK_K_BWD_PREP, s);
-        e = pk::launch_bwd_prep(ra, saved ? nullptr : q, k, v, out, dout, lse, qrot, krot, vh,
-                                w + W.dout16, w + W.rope, dsum, lse2, blockmax, scale,
-                                softmax_scale * 1.4426950408889634f, s);
-    }
-    if (e != hipSuccess) return PK_ERR_HIP;
-    pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream *side = side_stream(meta->device);
-    hipStream_t sq = s;   // stream of the dQ kernel
-    const int64_t kv_grid = (int64_t)meta->n_items * hkv;
-    if (side && kv_grid >= 64 && kv_grid <= 2 * (int64_t)side->cus && hipEventRecord(side->fork, s) == hipSuccess &&
-        hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess)
-        sq = side->stream;
-    {
-        ProfScope ps(PK_K_BWD_DQ, sq);
-        e = pk::launch_bwd_q(sh, *meta, qrot, krot, vh, w + W.dout16, lse2, dsum, scale, w + W.rope,
-                             dq, sq);
-    }
-    hipError_t e2;
-    {
-        ProfScope ps(PK_K_BWD, s);
-        e2 = pk::launch_bwd_kv(sh, *meta, qrot, krot, vh, w + W.dout16, lse2, dsum, scale, w + W.rope,
-                               dk, dv, s);
-    }
-    if (sq != s) {
-        // join: the caller's stream continues only after the dQ kernel
-        if (hipEventRecord(side->join, sq) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
-            return PK_ERR_HIP;
-    }
-    if (e != hipSuccess) return PK_ERR_HIP;
-    return hip_status(e2);
-}
-
-}  // namespace
 
 extern "C" {
 
@@ -355,44 +239,87 @@ size_t pk_attn_bwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int3
 pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *v, int32_t hq,
                       int32_t hkv, int32_t d, float softmax_scale, float rope_base, void *out,
                       float *lse, void *ws, size_t ws_bytes, void *hip_stream) {
-    return fwd_impl(meta, q, k, v, hq, hkv, d, softmax_scale, rope_base, out, lse, nullptr, 0, ws,
-                    ws_bytes, hip_stream);
+    if (!meta) return PK_ERR_INVALID;
+    if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.f) || !(rope_base > 0.f)) return PK_ERR_INVALID;
+    const int64_t T = meta->total_tokens;
+    if (T == 0) return PK_OK;
+    if (!q || !k || !v || !out || !lse || !ws || !aligned256(ws)) return PK_ERR_INVALID;
+    const pk::FwdWorkspace W = pk::fwd_workspace(T, hq, hkv, d);
+    if (ws_bytes < W.total) return PK_ERR_CAPACITY;
+    if (!on_meta_device(meta)) return PK_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    char *w = static_cast<char *>(ws);
+    pk::RopeArgs ra{meta->pos, T, hq, hkv, d, rope_base};
+    hipError_t e;
+    {
+        ProfScope ps(PK_K_FWD_PREP, s);
+        e = pk::launch_fwd_prep(ra, k, v, w + W.krot, w + W.vh, w + W.rope, s);
+    }
+    if (e != hipSuccess) return PK_ERR_HIP;
+    pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
+    {
+        ProfScope ps(PK_K_FWD, s);
+        e = pk::launch_fwd(sh, *meta, q, w + W.krot, w + W.vh, w + W.rope, out, lse, s);
+    }
+    return hip_status(e);
 }
 
 pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *v,
                       const void *out, const float *lse, const void *dout, int32_t hq,
                       int32_t hkv, int32_t d, float softmax_scale, float rope_base, float *dq,
                       float *dk, float *dv, void *ws, size_t ws_bytes, void *hip_stream) {
-    return bwd_impl(meta, q, k, v, nullptr, out, lse, dout, hq, hkv, d, softmax_scale, rope_base,
-                    dq, dk, dv, ws, ws_bytes, hip_stream);
-}
-
-size_t pk_attn_saved_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d) {
-    if (!meta || !shape_supported(hq, hkv, d)) return 0;
-    return pk::saved_layout(meta->total_tokens, hq, hkv, d).total;
-}
-
-pk_status pk_attn_fwd_save(pk_meta_t meta, const void *q, const void *k, const void *v,
-                           int32_t hq, int32_t hkv, int32_t d, float softmax_scale,
-                           float rope_base, void *out, float *lse, void *saved,
-                           size_t saved_bytes, void *ws, size_t ws_bytes, void *hip_stream) {
-    if (!saved && meta && meta->total_tokens > 0) return PK_ERR_INVALID;
-    return fwd_impl(meta, q, k, v, hq, hkv, d, softmax_scale, rope_base, out, lse, saved,
-                    saved_bytes, ws, ws_bytes, hip_stream);
-}
-
-pk_status pk_attn_bwd_saved(pk_meta_t meta, const void *saved, size_t saved_bytes,
-                            const void *out, const float *lse, const void *dout, int32_t hq,
-                            int32_t hkv, int32_t d, float softmax_scale, float rope_base,
-                            float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
-                            void *hip_stream) {
     if (!meta) return PK_ERR_INVALID;
     if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
-    if (meta->total_tokens == 0) return PK_OK;
-    if (!saved) return PK_ERR_INVALID;
-    if (saved_bytes < pk::saved_layout(meta->total_tokens, hq, hkv, d).total) return PK_ERR_CAPACITY;
-    return bwd_impl(meta, nullptr, nullptr, nullptr, saved, out, lse, dout, hq, hkv, d,
-                    softmax_scale, rope_base, dq, dk, dv, ws, ws_bytes, hip_stream);
+    if (!(softmax_scale > 0.f) || !(rope_base > 0.f)) return PK_ERR_INVALID;
+    const int64_t T = meta->total_tokens;
+    if (T == 0) return PK_OK;
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !ws || !aligned256(ws))
+        return PK_ERR_INVALID;
+    const pk::BwdWorkspace W = pk::bwd_workspace(T, hq, hkv, d);
+    if (ws_bytes < W.total) return PK_ERR_CAPACITY;
+    if (!on_meta_device(meta)) return PK_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    char *w = static_cast<char *>(ws);
+    float *dsum = reinterpret_cast<float *>(w + W.dsum);
+    float *lse2 = reinterpret_cast<float *>(w + W.lse2);
+    float *blockmax = reinterpret_cast<float *>(w + W.blockmax);
+    float *scale = reinterpret_cast<float *>(w + W.scale);
+    pk::RopeArgs ra{meta->pos, T, hq, hkv, d, rope_base};
+    hipError_t e;
+    {
+        ProfScope ps(PK_K_BWD_PREP, s);
+        e = pk::launch_bwd_prep(ra, q, k, v, out, dout, lse, w + W.qrot, w + W.krot, w + W.vh,
+                                w + W.dout16, w + W.rope, dsum, lse2, blockmax, scale,
+                                softmax_scale * 1.4426950408889634f, s);
+    }
+    if (e != hipSuccess) return PK_ERR_HIP;
+    pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream *side = side_stream(meta->device);
+    hipStream_t sq = s;   // stream of the dQ kernel
+    const int64_t kv_grid = (int64_t)meta->n_items * hkv;
+    if (side && kv_grid >= 64 && kv_grid <= 2 * (int64_t)side->cus && hipEventRecord(side->fork, s) == hipSuccess &&
+        hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess)
+        sq = side->stream;
+    {
+        ProfScope ps(PK_K_BWD_DQ, sq);
+        e = pk::launch_bwd_q(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
+                             scale, w + W.rope, dq, sq);
+    }
+    hipError_t e2;
+    {
+        ProfScope ps(PK_K_BWD, s);
+        e2 = pk::launch_bwd_kv(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
+                               scale, w + W.rope, dk, dv, s);
+    }
+    if (sq != s) {
+        // join: the caller's stream continues only after the dQ kernel
+        if (hipEventRecord(side->join, sq) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
+            return PK_ERR_HIP;
+    }
+    if (e != hipSuccess) return PK_ERR_HIP;
+    return hip_status(e2);
 }
 
 pk_status pk_dense_mask(pk_meta_t meta, uint8_t *mask, size_t mask_bytes, void *hip_stream) {

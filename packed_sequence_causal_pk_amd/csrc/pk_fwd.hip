@@ -49,8 +49,6 @@ struct FwdArgs {
     const int32_t *hdr;   // status, max_seqlen
     bf16 *out;            // [T, hq, D]
     float *lse;           // [hq, T]
-    f16 *qsave;           // optional [T, hq, D]: R(q) * scale * log2(e) in fp16, for the backward
-                          // (rounded from the fp16 R(q), so two roundings: |error| <= 2^-10 rel.)
     int64_t T;
     int hq, hkv, group;
     float scale_log2;     // softmax scale * log2(e)
@@ -303,20 +301,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
             }
         }
         if (hb == 0) a.lse[(int64_t)h * T + i] = (mref + log2f(l_tot)) * kLn2;
-        // the backward's Q operand, R(q) * scale * log2(e) in fp16, from the fp16 fragments
-        // (stored here rather than in the prologue: a store there would be drained by the first
-        // tile's copy wait and stall every workgroup's start)
-        if (a.qsave) {
-            f16 *srow = a.qsave + ((int64_t)i * a.hq + h) * D;
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const int d = 16 * (kk % (NKK / 2)) + 8 * hb + (kk >= NKK / 2 ? D / 2 : 0);
-                f16x8 z;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) z[e] = (f16)((float)qf[kk][e] * a.scale_log2);
-                store_f16x8(srow + d, z);
-            }
-        }
     }
 }
 
@@ -325,10 +309,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
 namespace pk {
 
 hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, const void *krot,
-                      const void *v, const void *rope, void *out, float *lse, void *qsave,
-                      hipStream_t s) {
+                      const void *v, const void *rope, void *out, float *lse, hipStream_t s) {
     FwdArgs a;
-    a.qsave = (f16 *)qsave;
     a.q = (const bf16 *)q;
     a.krot = (const f16 *)krot;
     a.v = (const f16 *)v;

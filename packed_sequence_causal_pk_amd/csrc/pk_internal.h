@@ -38,11 +38,6 @@ struct FwdWorkspace {
 struct BwdWorkspace {
     size_t qrot, krot, vh, dout16, rope, dsum, lse2, blockmax, scale, total;
 };
-// Byte layout of the buffer a saving forward fills for the backward.
-struct SavedLayout {
-    size_t qrot, krot, vh, total;
-};
-SavedLayout saved_layout(int64_t T, int hq, int hkv, int d);
 FwdWorkspace fwd_workspace(int64_t T, int hq, int hkv, int d);
 BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d);
 
@@ -63,8 +58,6 @@ hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, const void *v, void
 unsigned prep_blocks(int64_t T, int d);
 // Blocks of the max|dout| reduction (at most 1024).
 unsigned dmax_blocks(int64_t T, int hq, int d);
-// With q == nullptr the fp16 operands (qrot, krot, vh) are taken as already written (by a
-// saving forward) and only dout16, dsum, lse2, the table and the dout scale are produced.
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *v,
                            const void *out, const void *dout, const float *lse, void *qrot,
                            void *krot, void *vh, void *dout16, void *rope, float *dsum,
@@ -75,10 +68,8 @@ struct AttnShape {
     int hq, hkv, d, n_items;
     float scale;
 };
-// qsave (nullable): [T, hq, d] fp16 receiving R(q) * scale * log2(e) for the backward.
 hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, const void *krot,
-                      const void *v, const void *rope, void *out, float *lse, void *qsave,
-                      hipStream_t s);
+                      const void *v, const void *rope, void *out, float *lse, hipStream_t s);
 // qrot = R(q) * softmax_scale * log2(e) (fp16), dout16 = sigma * dout (fp16),
 // dsum = -sigma * rowsum(dout * out), lse2 = -lse * log2(e).
 // launch_bwd_kv writes dk and dv, launch_bwd_q writes dq.

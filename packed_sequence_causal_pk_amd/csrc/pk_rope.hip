@@ -197,9 +197,7 @@ __device__ __forceinline__ void table8(const float2 *__restrict__ table, int64_t
 // scale times log2(e), so that the backward's score products come out in the exp2 domain),
 // sigma * dout, and the row values -sigma * sum(dout * out) and -lse * log2(e), stored negated
 // because the backward's products start from them.
-// ROTATE = false: the fp16 operands were saved by the forward; only the query-head rows'
-// sigma * dout, -sigma * D and -lse * log2(e) are written (rows [0, T * hq)).
-template <int D, bool ROTATE>
+template <int D>
 __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
                                                   const float2 *__restrict__ table,
                                                   const bf16 *__restrict__ q,
@@ -219,7 +217,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int c = (int)(gid % G);
     int64_t row = gid / G;
-    const int64_t nkv = ROTATE ? T * hkv : 0;
+    const int64_t nkv = T * hkv;
     float cs[8], sn[8];
     auto rotate = [&](const bf16 *src, f16 *dst, float mult) {
         const bf16x8 x1 = pkd::load_bf16x8(src + 8 * c), x2 = pkd::load_bf16x8(src + D / 2 + 8 * c);
@@ -233,7 +231,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
         pkd::store_f16x8(dst + 8 * c, y1);
         pkd::store_f16x8(dst + D / 2 + 8 * c, y2);
     };
-    if (ROTATE && row < nkv) {
+    if (row < nkv) {
         table8<D>(table, row / hkv, c, cs, sn);
         const int64_t off = row * D;
         rotate(k + off, krot + off, 1.0f);
@@ -248,11 +246,9 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
     if (row >= T * hq) return;
     const int64_t t = row / hq;
     const int h = (int)(row % hq);
+    table8<D>(table, t, c, cs, sn);
     const int64_t off = row * D;
-    if (ROTATE) {
-        table8<D>(table, t, c, cs, sn);
-        rotate(q + off, qrot + off, qscale);
-    }
+    rotate(q + off, qrot + off, qscale);
     const float sigma = dscale[0];
     const bf16x8 o1 = pkd::load_bf16x8(out + off + 8 * c), o2 = pkd::load_bf16x8(out + off + D / 2 + 8 * c);
     const bf16x8 g1 = pkd::load_bf16x8(dout + off + 8 * c), g2 = pkd::load_bf16x8(dout + off + D / 2 + 8 * c);
@@ -324,8 +320,7 @@ hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, cons
     const int64_t n8 = r.T * r.hq * r.d / 8;
     const unsigned nb = dmax_blocks(r.T, r.hq, r.d);
     const unsigned gt = prep_blocks(r.T, r.d);
-    const bool rotate = q != nullptr;
-    const unsigned gr = (unsigned)((r.T * (r.hq + (rotate ? r.hkv : 0)) * (r.d / 16) + 255) / 256);
+    const unsigned gr = (unsigned)((r.T * (r.hq + r.hkv) * (r.d / 16) + 255) / 256);
     if (r.d == 128)
         k_bwd_pre<128><<<nb + gt, 256, 0, s>>>((const bf16 *)dout, n8, blockmax, (int)nb, r.pos, r.T,
                                                r.rope_base, (float2 *)rope);
@@ -336,16 +331,17 @@ hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, cons
     if (e != hipSuccess) return e;
     k_bwd_scale<<<1, 256, 0, s>>>(blockmax, (int)nb, scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    auto rows = [&](auto kernel) {
-        kernel<<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
-                                  (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
-                                  (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
-                                  (f16 *)vh, (f16 *)dout16, dsum, lse2, qscale);
-    };
-    if (r.d == 128)
-        rotate ? rows(k_bwd_rows<128, true>) : rows(k_bwd_rows<128, false>);
-    else
-        rotate ? rows(k_bwd_rows<64, true>) : rows(k_bwd_rows<64, false>);
+    if (r.d == 128) {
+        k_bwd_rows<128><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
+                                            (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
+                                            (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
+                                            (f16 *)vh, (f16 *)dout16, dsum, lse2, qscale);
+    } else {
+        k_bwd_rows<64><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
+                                           (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
+                                           (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
+                                           (f16 *)vh, (f16 *)dout16, dsum, lse2, qscale);
+    }
     return hipGetLastError();
 }
 

@@ -23,25 +23,17 @@ def dev(x, dtype=torch.bfloat16):
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype).contiguous()
 
 
-def run_pk(lengths, q, k, v, dout, scale, base=10000.0, meta=None, bwd=True, saved=False):
-    """Build the meta (unless given) and run fwd (+ bwd) through libpk.  With saved=True the
-    forward stores the backward's operands (pk_attn_fwd_save) and the backward runs on them
-    (pk_attn_bwd_saved)."""
+def run_pk(lengths, q, k, v, dout, scale, base=10000.0, meta=None, bwd=True):
+    """Build the meta (unless given) and run fwd (+ bwd) through libpk; numpy float64 outputs."""
     t = q.shape[0]
     if meta is None:
         meta = pk.build_meta(torch.tensor(np.asarray(lengths, np.int32), device="cuda"), t)
     tq, tk, tv = dev(q), dev(k), dev(v)
-    if saved:
-        out, lse, buf = pk.attn_fwd_save(meta, tq, tk, tv, scale, base)
-    else:
-        out, lse = pk.attn_fwd(meta, tq, tk, tv, scale, base)
+    out, lse = pk.attn_fwd(meta, tq, tk, tv, scale, base)
     res = {"meta": meta, "out": out, "lse": lse}
     if bwd:
         tdo = dev(dout)
-        if saved:
-            dq, dk, dv = pk.attn_bwd_saved(meta, buf, out, lse, tdo, tk.shape[1], scale, base)
-        else:
-            dq, dk, dv = pk.attn_bwd(meta, tq, tk, tv, out, lse, tdo, scale, base)
+        dq, dk, dv = pk.attn_bwd(meta, tq, tk, tv, out, lse, tdo, scale, base)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return res

@@ -79,11 +79,8 @@ def test_empty_pack():
     k = torch.zeros(0, 1, 64, device="cuda", dtype=torch.bfloat16)
     out, lse = pk.attn_fwd(meta, q, k, k)
     dq, dk, dv = pk.attn_bwd(meta, q, k, k, out, lse, q)
-    out2, lse2, sv = pk.attn_fwd_save(meta, q, k, k)
-    dq2, _, _ = pk.attn_bwd_saved(meta, sv, out2, lse2, q, 1)
     torch.cuda.synchronize()
     assert out.shape == (0, 2, 64) and dq.shape == (0, 2, 64)
-    assert out2.shape == (0, 2, 64) and dq2.shape == (0, 2, 64)
 
 
 SMALL_CASES = [
@@ -100,16 +97,15 @@ SMALL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("saved", [False, True], ids=["plain", "saved"])
 @pytest.mark.parametrize("case", range(len(SMALL_CASES)))
-def test_fwd_bwd_small(case, saved):
+def test_fwd_bwd_small(case):
     lengths, hq, hkv, d = SMALL_CASES[case]
     if lengths == "short":
         lengths = synth.random_lengths(np.random.default_rng(5), 120, 1, 16)
-    say("small case", case, "T", int(np.sum(lengths)), "hq/hkv/d", hq, hkv, d, "saved", saved)
+    say("small case", case, "T", int(np.sum(lengths)), "hq/hkv/d", hq, hkv, d)
     lens, q, k, v, do = synth.small_problem(100 + case, lengths, hq, hkv, d)
     scale = 1.0 / math.sqrt(d)
-    res = run_pk(lens, q, k, v, do, scale, saved=saved)
+    res = run_pk(lens, q, k, v, do, scale)
     o_ref, lse_ref = O.attn_fwd(q, k, v, lens, scale, 1e4)
     dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, scale, 1e4)
     compare("out", to_np(res["out"]), o_ref)
@@ -131,9 +127,8 @@ LAUNCH_SHAPE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("saved", [False, True], ids=["plain", "saved"])
 @pytest.mark.parametrize("case", range(len(LAUNCH_SHAPE_CASES)))
-def test_launch_shape_boundaries(case, saved):
+def test_launch_shape_boundaries(case):
     t, hq, hkv, d = LAUNCH_SHAPE_CASES[case]
     rng = np.random.default_rng(700 + case)
     lengths = []
@@ -141,10 +136,10 @@ def test_launch_shape_boundaries(case, saved):
         lengths.append(int(rng.integers(1, 600, endpoint=True)))
     lengths[-1] -= sum(lengths) - t
     lengths = [x for x in lengths if x > 0]
-    say("launch shapes", case, "T", t, "hq/hkv/d", hq, hkv, d, "n", len(lengths), "saved", saved)
+    say("launch shapes", case, "T", t, "hq/hkv/d", hq, hkv, d, "n", len(lengths))
     lens, q, k, v, do = synth.small_problem(700 + case, lengths, hq, hkv, d)
     scale = 1.0 / math.sqrt(d)
-    res = run_pk(lens, q, k, v, do, scale, saved=saved)
+    res = run_pk(lens, q, k, v, do, scale)
     kv_heads = [0, hkv - 1]
     g = hq // hkv
     heads = [h for kvh in kv_heads for h in range(kvh * g, (kvh + 1) * g)]
@@ -165,19 +160,18 @@ SCALE_BASE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("saved", [False, True], ids=["plain", "saved"])
 @pytest.mark.parametrize("case", range(len(SCALE_BASE_CASES)))
-def test_softmax_scale_and_rope_base(case, saved):
+def test_softmax_scale_and_rope_base(case):
     """Softmax scales and RoPE bases other than the workloads' (the kernels fold the scale into
     their fp16 operands and exponents and read the table built for the base).  The max-abs gate
     is absolute and was set for scores of unit spread, so q and k are multiplied by a power of
     two (exact in bf16) that keeps scale * <q, k> near that spread."""
     scale_of, base, d, f = SCALE_BASE_CASES[case]
     scale = scale_of(d)
-    say("scale %.6g base %g d %d qk factor %g saved %s" % (scale, base, d, f, saved))
+    say("scale %.6g base %g d %d qk factor %g" % (scale, base, d, f))
     lens, q, k, v, do = synth.small_problem(400 + case, [300, 1, 170, 45], 4, 2, d)
     q, k = (q * f).astype(np.float32), (k * f).astype(np.float32)
-    res = run_pk(lens, q, k, v, do, scale, base, saved=saved)
+    res = run_pk(lens, q, k, v, do, scale, base)
     o_ref, lse_ref = O.attn_fwd(q, k, v, lens, scale, base)
     dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, scale, base)
     compare("out", to_np(res["out"]), o_ref)
@@ -187,15 +181,14 @@ def test_softmax_scale_and_rope_base(case, saved):
     compare("dv", to_np(res["dv"]), dv_ref)
 
 
-@pytest.mark.parametrize("saved", [False, True], ids=["plain", "saved"])
 @pytest.mark.parametrize("log2_scale", [-24, -12, 10])
-def test_gradient_scale_invariance(log2_scale, saved):
+def test_gradient_scale_invariance(log2_scale):
     """dout scaled by 2^e (exact in bf16) gives gradients scaled by 2^e: the backward's fp16
     operands follow the gradient's magnitude instead of under- or overflowing."""
-    say("dout scaled by 2^%d, saved %s" % (log2_scale, saved))
+    say("dout scaled by 2^%d" % log2_scale)
     lens, q, k, v, do = synth.small_problem(300, [90, 200, 3], 4, 2, 128)
     f = 2.0 ** log2_scale
-    res = run_pk(lens, q, k, v, (do * f).astype(np.float32), 1.0 / math.sqrt(128), saved=saved)
+    res = run_pk(lens, q, k, v, (do * f).astype(np.float32), 1.0 / math.sqrt(128))
     dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, 1.0 / math.sqrt(128), 1e4)
     compare("dq", to_np(res["dq"]) / f, dq_ref)
     compare("dk", to_np(res["dk"]) / f, dk_ref)
@@ -208,13 +201,13 @@ def _sub_pack(lengths, seqs):
     return [int(lengths[s]) for s in seqs], idx
 
 
-def _check_workload(name, layer, seqs=None, kv_heads=None, saved=False):
+def _check_workload(name, layer, seqs=None, kv_heads=None):
     w = synth.WORKLOADS[name]
     lengths = synth.pack_lengths(name)
     q, k, v, do = synth.layer_tensors(w, layer)
     say("workload", name, "layer", layer, "seqs", "all" if seqs is None else len(seqs),
-        "kv heads", "all" if kv_heads is None else list(kv_heads), "saved", saved)
-    res = run_pk(lengths, q, k, v, do, w.softmax_scale, w.rope_base, saved=saved)
+        "kv heads", "all" if kv_heads is None else list(kv_heads))
+    res = run_pk(lengths, q, k, v, do, w.softmax_scale, w.rope_base)
     if seqs is None:
         seqs = list(range(len(lengths)))
     sub_len, idx = _sub_pack(lengths, seqs)
@@ -246,36 +239,9 @@ def test_workload_qwen06b(layer):
     _check_workload("qwen06b", layer)
 
 
-@pytest.mark.parametrize("saved", [False, True], ids=["plain", "saved"])
-def test_workload_qwen14b_sampled(saved):
+def test_workload_qwen14b_sampled():
     # the longest, the shortest and the last sequence; the first and last KV-head groups
-    _check_workload("qwen14b", 39 if saved else 0, seqs=[0, 7, 9], kv_heads=[0, 7], saved=saved)
-
-
-@pytest.mark.parametrize("name,layer", [("llama1b", 15), ("qwen06b", 27)])
-def test_workload_saved_operands(name, layer):
-    _check_workload(name, layer, saved=True)
-
-
-def test_saved_forward_matches_plain_forward():
-    """The saving forward runs the same kernels with one more store: out and lse are
-    bit-identical to pk_attn_fwd's; an invalid pack gives zeros on the saved path too."""
-    w = synth.WORKLOADS["qwen06b"]
-    lengths = synth.pack_lengths("qwen06b")
-    q, k, v, do = (dev(x) for x in synth.layer_tensors(w, 3))
-    meta = pk.build_meta(torch.tensor(lengths, device="cuda"), w.total_tokens)
-    say("saved forward vs plain forward, qwen06b layer 3")
-    o1, l1 = pk.attn_fwd(meta, q, k, v, w.softmax_scale)
-    o2, l2, buf = pk.attn_fwd_save(meta, q, k, v, w.softmax_scale)
-    torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    bad = pk.build_meta(torch.tensor([3, 0, 5], dtype=torch.int32, device="cuda"), 8)
-    q8, k8 = q[:8, :2].contiguous(), k[:8, :1].contiguous()
-    out, lse, sv = pk.attn_fwd_save(bad, q8, k8, k8)
-    dq, dk, dv = pk.attn_bwd_saved(bad, sv, out, lse, q8, 1)
-    torch.cuda.synchronize()
-    for x in (out, lse, dq, dk, dv):
-        assert torch.count_nonzero(x).item() == 0
+    _check_workload("qwen14b", 0, seqs=[0, 7, 9], kv_heads=[0, 7])
 
 
 def test_workload_skewed_sampled():

@@ -39,3 +39,16 @@ def test_layer_tensors_shapes_and_seeding():
     assert abs(float(q.std()) - 1.0) < 0.05
     w14 = synth.WORKLOADS["qwen14b"]
     assert abs(float(synth.layer_tensors(w14, 0, total_tokens=512)[2].std()) - 0.5) < 0.03
+
+
+def test_router_indices_shape_distinct_and_seeded():
+    """The synthetic router gives each token top_k distinct experts in range, is reproducible for a
+    seed, and spreads load unevenly (the per-expert offset) without leaving most experts idle."""
+    for (n_tok, n_exp, top_k) in synth.MOE_WORKLOADS.values():
+        idx = synth.router_indices(n_tok, n_exp, top_k)
+        assert idx.shape == (n_tok, top_k) and idx.dtype == np.int32
+        assert idx.min() >= 0 and idx.max() < n_exp
+        assert all(len(set(row)) == top_k for row in idx[:2000].tolist())
+        assert np.array_equal(idx, synth.router_indices(n_tok, n_exp, top_k))
+        counts = np.bincount(idx.ravel(), minlength=n_exp)
+        assert counts.max() > 2 * counts.mean() and (counts > 0).sum() > n_exp // 2
