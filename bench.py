@@ -34,7 +34,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "packed causal attn fwd+bwd TFLOP/s + tokens/s per layer; % bf16 MFMA peak"
 PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 matrix peak (256 CUs x 4096 flop/clk x 2.4 GHz)
-MEASURED_MFMA_TFLOPS = 2440.5   # v_mfma_f32_32x32x16_f16 microbenchmark on the same part (8 waves/CU)
+# v_mfma_f32_32x32x16_f16 rate, measured by pk_peak_mfma at the start of each run (the value
+# here is only a placeholder until then)
+MEASURED_MFMA_TFLOPS = 2200.0
 HBM_GBS = 8000.0
 
 
@@ -517,6 +519,16 @@ def main():
     if args.steps_around_only:
         print(json.dumps({"steps_around": measure_steps_around()}), flush=True)
         return
+    # the measured roofline of this device: matrix-core rate and HBM bandwidths
+    import packed_sequence_causal_pk_amd as pk
+    import torch
+    torch.cuda.set_device(0)
+    global MEASURED_MFMA_TFLOPS
+    burst_mfma = pk.peak_mfma_tflops(iters=2000)   # about 0.3 ms per launch
+    MEASURED_MFMA_TFLOPS = pk.peak_mfma_tflops()   # about 3 ms per launch: the sustained clock
+    measured_hbm = pk.peak_hbm_gbps()
+    print("bench: measured MFMA %.1f TFLOP/s, HBM %s GB/s" % (MEASURED_MFMA_TFLOPS, measured_hbm),
+          file=sys.stderr, flush=True)
     # the dK/dV kernel dominates the step on every pack measured here: its launches are timed
     # inside the timed region for the roofline
     m = measure(args.workload, args.steps, args.warmup, args.calibrate_copy_mib, timed_kinds=("bwd",))
@@ -555,6 +567,12 @@ def main():
         "tokens_per_s_per_layer": s["tokens_per_s_per_layer"],
         "pct_bf16_peak": s["pct_bf16_peak"],
         "pct_measured_mfma_peak": s["pct_measured_mfma_peak"],
+        "measured_roofline": {"mfma_fp16_tflops": round(MEASURED_MFMA_TFLOPS, 1),
+                              "mfma_fp16_tflops_short_launch": round(burst_mfma, 1),
+                              "hbm_gbps": measured_hbm,
+                              "how": "pk_peak_mfma (8 workgroups of 4 waves per CU, 4 chains of "
+                                     "v_mfma_f32_32x32x16_f16 per wave; 20000 iterations, 2000 for the "
+                                     "short launch) and pk_peak_hbm (2 GiB read / write / copy), best of 3"},
         "ms_per_layer_fwd_bwd": s["ms_per_layer_fwd_bwd"],
         "ms_per_layer_fwd": s["ms_per_layer_fwd"],
         "fwd_tflops": s["fwd_tflops"],

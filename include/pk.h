@@ -224,6 +224,17 @@ pk_status pk_reload_release(pk_reload_t r, int32_t slot, void *hip_stream);
 /* Wait for pending copies, then free the stream and events. */
 pk_status pk_reload_destroy(pk_reload_t r);
 
+/* ---- Measured roofline (measurement aids; nothing on the attention path calls them) -----
+ * pk_peak_mfma: `workgroups` workgroups of 4 waves, each wave running 4 independent chains of
+ * `iters` v_mfma_f32_32x32x16_f16 on register operands (32 * 32 * 16 * 2 flops each), so
+ * flops = workgroups * 4 * 4 * iters * 32768; `sink` (device, >= 4 * workgroups floats) receives
+ * one value per wave.  pk_peak_hbm: mode 0 reads `bytes` of `src` (sink: device, >= 1 float),
+ * mode 1 writes `bytes` to `dst`, mode 2 copies; 16-byte aligned buffers, bytes % 16 == 0.
+ * Both only enqueue on `hip_stream`; time them with events on that stream. */
+pk_status pk_peak_mfma(float *sink, int32_t workgroups, int32_t iters, void *hip_stream);
+pk_status pk_peak_hbm(int32_t mode, const void *src, void *dst, size_t bytes, float *sink,
+                      void *hip_stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *pk_status_str(pk_status status);
 

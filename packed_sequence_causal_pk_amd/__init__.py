@@ -19,7 +19,7 @@ from ._lib import PkError, lib
 __all__ = ["PackedMeta", "build_meta", "attn_fwd", "attn_bwd", "fwd_workspace", "bwd_workspace",
            "PackedCausalAttention", "PkError", "tile_rows", "prof_enable", "prof_reset",
            "prof_query", "dense_mask", "rope_apply", "moe_group", "moe_workspace",
-           "ReloadPipeline"]
+           "ReloadPipeline", "peak_mfma_tflops", "peak_hbm_gbps"]
 
 
 def _torch():
@@ -288,6 +288,49 @@ class ReloadPipeline:
             self.close()
         except Exception:
             pass
+
+
+def peak_mfma_tflops(workgroups: Optional[int] = None, iters: int = 20000, reps: int = 3) -> float:
+    """Measured dense fp16 matrix-core rate (TFLOP/s): best of `reps` timed launches of
+    pk_peak_mfma, by default with eight workgroups (32 waves) per compute unit (the highest of
+    2, 3, 4 and 8 per compute unit when measured on the part)."""
+    torch = _torch()
+    if workgroups is None:
+        workgroups = 8 * torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    sink = torch.empty(4 * workgroups, dtype=torch.float32, device="cuda")
+    flops = workgroups * 4 * 4 * iters * 32 * 32 * 16 * 2
+    best = 0.0
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _lib.check("pk_peak_mfma", lib().pk_peak_mfma(_ptr(sink), workgroups, iters, _stream_ptr(None)))
+        e1.record()
+        e1.synchronize()
+        if r:   # the first launch warms up
+            best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
+
+
+def peak_hbm_gbps(nbytes: int = 2 << 30, reps: int = 3) -> dict:
+    """Measured HBM bandwidth (GB/s) of a plain read, write and copy of `nbytes` (best of reps)."""
+    torch = _torch()
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    out = {}
+    for mode, name, moved in ((0, "read", nbytes), (1, "write", nbytes), (2, "copy", 2 * nbytes)):
+        best = 0.0
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            _lib.check("pk_peak_hbm", lib().pk_peak_hbm(mode, _ptr(src), _ptr(dst), nbytes, _ptr(sink),
+                                                        _stream_ptr(None)))
+            e1.record()
+            e1.synchronize()
+            if r:
+                best = max(best, moved / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        out[name] = round(best, 1)
+    return out
 
 
 def prof_enable(on: bool = True, kinds=None) -> None:

@@ -66,6 +66,8 @@ SIGNATURES = {
     "pk_reload_acquire": (_i32, [_vp, _i32, _vp]),
     "pk_reload_release": (_i32, [_vp, _i32, _vp]),
     "pk_reload_destroy": (_i32, [_vp]),
+    "pk_peak_mfma": (_i32, [_vp, _i32, _i32, _vp]),
+    "pk_peak_hbm": (_i32, [_i32, _vp, _vp, _sz, _vp, _vp]),
     "pk_status_str": (ctypes.c_char_p, [_i32]),
     "pk_prof_enable": (_i32, [_i32]),
     "pk_prof_reset": (_i32, []),

@@ -102,6 +102,23 @@ def test_host_side_rejections_aux(lib):
     assert call(ws_bytes=ws - 1) == _lib.PK_ERR_CAPACITY
 
 
+def test_host_side_rejections_peak_and_reload(lib):
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every case fails before any launch
+    assert lib.pk_peak_mfma(None, 512, 100, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_peak_mfma(fake, 0, 100, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_peak_mfma(fake, 512, 0, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_peak_hbm(3, fake, fake, 1 << 20, fake, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_peak_hbm(0, fake, fake, 1000, fake, None) == _lib.PK_ERR_INVALID     # not a multiple of 16
+    assert lib.pk_peak_hbm(0, None, fake, 1 << 20, fake, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_peak_hbm(1, fake, None, 1 << 20, fake, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_peak_hbm(0, ctypes.c_void_p(0x10008), fake, 1 << 20, fake, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_reload_create(None) == _lib.PK_ERR_INVALID
+    assert lib.pk_reload_fetch(None, 0, fake, fake, 16) == _lib.PK_ERR_INVALID
+    assert lib.pk_reload_acquire(None, 0, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_reload_release(None, 1, None) == _lib.PK_ERR_INVALID
+    assert lib.pk_reload_destroy(None) == _lib.PK_ERR_INVALID
+
+
 def test_status_strings_and_profiler_queries(lib):
     for code in (0, -1, -2, -3, -4, -5):
         assert _lib.status_str(code)

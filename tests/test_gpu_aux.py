@@ -230,3 +230,15 @@ def test_reload_pipeline_matches_resident(double):
     for l in range(n_layers):
         for a, b in zip(got[l], ref[l]):
             assert torch.equal(a, b), "layer %d" % l
+
+
+# ------------------------------------------------------------------- measured roofline aids
+def test_peak_microbenchmarks_run_and_are_plausible():
+    """The matrix-core and HBM microbenchmarks run and land in a plausible range for the part
+    (their figures are reported, not asserted tightly)."""
+    say("peak microbenchmarks")
+    tf = pk.peak_mfma_tflops(iters=2000, reps=1)
+    bw = pk.peak_hbm_gbps(nbytes=256 << 20, reps=1)
+    say("  mfma %.1f TFLOP/s, hbm %s GB/s" % (tf, bw))
+    assert 200.0 < tf < 3000.0
+    assert all(500.0 < v < 10000.0 for v in bw.values())
