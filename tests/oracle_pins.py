@@ -16,6 +16,7 @@ import os
 import numpy as np
 import torch
 
+from oracle import lora_oracle as LO
 from oracle import moe_oracle as MO
 from oracle import pk_oracle as O
 from packed_sequence_causal_pk_amd import synth
@@ -357,10 +358,46 @@ def pin_moe_sort_and_bincount():
     assert MO.group_by_expert([[-1, 0]], 5)["status"] == MO.STATUS_BAD_EXPERT
 
 
+# ------------------------------------------------------------------- LoRA QKV projection
+def pin_lora_scalar_loops():
+    """Y[t, n] = sum_k x[t, k] (W[k, n] + s sum_j A[k, j] B[j, n]), summed element by element."""
+    rng = np.random.default_rng(21)
+    t, k, n, r, s = 3, 5, 4, 2, 0.75
+    x, w = rng.standard_normal((t, k)), rng.standard_normal((k, n))
+    a, b = rng.standard_normal((k, r)), rng.standard_normal((r, n))
+    y = LO.lora_qkv(x, w, a, b, s)
+    for i in range(t):
+        for c in range(n):
+            acc = 0.0
+            for kk in range(k):
+                adapted = w[kk, c]
+                for j in range(r):
+                    adapted += s * a[kk, j] * b[j, c]
+                acc += x[i, kk] * adapted
+            assert abs(y[i, c] - acc) <= 1e-12 * max(1.0, abs(acc))
+
+
+def pin_lora_unmerged_and_zero_scale():
+    """The merged weight equals the two-step adapter path x W + s (x A) B (what a LoRA layer
+    computes without merging); with s = 0 the projection is torch's own float64 matmul of x and W;
+    the q/k/v split takes columns in q, k, v order."""
+    rng = np.random.default_rng(22)
+    x, w = rng.standard_normal((17, 48)), rng.standard_normal((48, 40))
+    a, b = rng.standard_normal((48, 8)), rng.standard_normal((8, 40))
+    y = LO.lora_qkv(x, w, a, b, 0.5)
+    two_step = x @ w + 0.5 * ((x @ a) @ b)
+    assert np.allclose(y, two_step, rtol=1e-12, atol=1e-10)
+    plain = torch.matmul(torch.from_numpy(x), torch.from_numpy(w)).numpy()
+    assert np.allclose(LO.lora_qkv(x, w, a, b, 0.0), plain, rtol=1e-12, atol=1e-10)
+    q, k, v = LO.split_qkv(np.arange(2 * 40).reshape(2, 40), 3, 1, 8)   # (3 + 2) heads x 8 = 40
+    assert q.shape == (2, 3, 8) and k.shape == (2, 1, 8) and v.shape == (2, 1, 8)
+    assert q[1, 2, 7] == 40 + 23 and k[0, 0, 0] == 24 and v[1, 0, 3] == 40 + 35
+
+
 ALL_PINS = [
     pin_meta_golden, pin_meta_bruteforce, pin_worklist_coverage, pin_rope,
     pin_fwd_dense_equals_per_sequence, pin_fwd_rows_and_closed_forms, pin_fwd_lse_reconstruction,
     pin_torch_sdpa_and_autograd, pin_bwd_finite_differences, pin_bwd_invariants,
     pin_permutation_invariance, pin_dense_mask, pin_moe_golden, pin_moe_bruteforce,
-    pin_moe_sort_and_bincount,
+    pin_moe_sort_and_bincount, pin_lora_scalar_loops, pin_lora_unmerged_and_zero_scale,
 ]

@@ -4,6 +4,7 @@ A pin set that lets any of these through would not be strong enough to trust the
 import numpy as np
 import pytest
 
+from oracle import lora_oracle as LO
 from oracle import moe_oracle as MO
 from oracle import pk_oracle as O
 from tests import oracle_pins as P
@@ -97,6 +98,17 @@ def _mask_strict(lengths):
 
 
 _orig_dense_mask = O.dense_mask
+_orig_lora = LO.lora_qkv
+
+
+def _lora_adapter_omitted(x, w, a, b, scale=1.0):
+    """Mistake: the frozen weight alone (the adapter never added)."""
+    return np.asarray(x, np.float64) @ np.asarray(w, np.float64)
+
+
+def _lora_scale_dropped(x, w, a, b, scale=1.0):
+    """Mistake: the adapter scale ignored."""
+    return _orig_lora(x, w, a, b, 1.0)
 
 MUTATIONS = {
     "gqa_interleaved_groups": ("kv_head_of", lambda h, g: h % g),
@@ -119,6 +131,8 @@ MUTATIONS = {
     "moe_slot_major": (MO, "group_by_expert", _group_slot_major),
     "moe_inclusive_offsets": (MO, "group_by_expert", _group_inclusive_offsets),
     "moe_unstable_order": (MO, "group_by_expert", _group_descending),
+    "lora_adapter_omitted": (LO, "lora_qkv", _lora_adapter_omitted),
+    "lora_scale_dropped": (LO, "lora_qkv", _lora_scale_dropped),
 }
 
 
