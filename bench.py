@@ -505,6 +505,22 @@ def measure_steps_around(pk_names=("llama1b", "qwen06b", "qwen14b")):
             "algorithmic_bytes": 12 * M + 8 * n_exp + 8, "bound": "latency (3 launches)",
             "per_expert_where_us": round(naive_us, 1),
             "speedup_vs_per_expert_where": round(naive_us / us, 1)}
+    res["lora_qkv"] = {}
+    for name in pk_names:
+        w = synth.WORKLOADS[name]
+        T, K, N, r = w.total_tokens, synth.PROJ_HIDDEN[name], (w.hq + 2 * w.hkv) * w.head_dim, 16
+        x = torch.randn(T, K, device=dev).bfloat16()
+        wt = (torch.randn(N, K, device=dev) / K ** 0.5).bfloat16()
+        at = (torch.randn(r, K, device=dev) / K ** 0.5).bfloat16()
+        bt = (torch.randn(N, r, device=dev) * (0.25 / r ** 0.5)).bfloat16()
+        y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+        ws = pk.lora_workspace(T, K, N, r, dev)
+        us = kind_avg_us("lora", lambda: pk.lora_qkv(x, wt, at, bt, 2.0, out=y, workspace=ws), 10)
+        flops = 2 * T * K * N + 2 * T * K * r + 2 * T * r * N
+        tf = flops / (us * 1e-6) / 1e12
+        res["lora_qkv"][name] = {"T": T, "K": K, "N": N, "rank": r, "avg_us": round(us, 2),
+                                 "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_TFLOPS, 4)}
+        del x, wt, at, bt, y, ws
     res["reload"] = measure_reload()
     return res
 

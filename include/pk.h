@@ -191,6 +191,24 @@ pk_status pk_moe_group(const int32_t *router_indices, int64_t n_tokens, int32_t 
                        int32_t *inv, int32_t *status, void *ws, size_t ws_bytes,
                        void *hip_stream);
 
+/* ---- LoRA-adapted QKV projection (the producer of q, k, v) ----------------------------
+ * "Introducing Unsloth：LLM 训练提速 30 倍", "手动 Autograd": Q = X (W_q + A_q B_q), likewise K
+ * and V.  With the three projections stacked along the output dimension (N = (hq + 2 hkv) d;
+ * columns [0, hq d) are q, then k, then v, so y viewed as [T, N] splits into the [T, h, d]
+ * tensors pk_attn_fwd takes):
+ *     y [T, N] = x [T, K] (W + scale A B),   W [K, N], A [K, r], B [r, N],
+ * computed as x W + (scale x A) B without forming W + scale A B.  Storage is the weight layout
+ * of a linear layer (out x in): wt = W^T [N, K], at = A^T [r, K], bt = B^T [N, r]; x, y
+ * row-major.  All bfloat16, fp32 accumulation; scale x A is rounded to bf16 before it meets B.
+ * K % 64 == 0 (64..65536), N % 128 == 0 (128..65536), 1 <= r <= PK_LORA_MAX_RANK,
+ * T <= PK_MAX_TOKENS; device pointers 16-byte aligned, `ws` (>= pk_lora_qkv_workspace_bytes,
+ * 256-byte aligned) holds scale x A and zero-padded copies of the adapter. */
+#define PK_LORA_MAX_RANK 64
+size_t pk_lora_qkv_workspace_bytes(int64_t T, int32_t K, int32_t N, int32_t r);
+pk_status pk_lora_qkv(const void *x, const void *wt, const void *at, const void *bt, int64_t T,
+                      int32_t K, int32_t N, int32_t r, float scale, void *y, void *ws,
+                      size_t ws_bytes, void *hip_stream);
+
 /* ---- Double-buffered reload of activations from pinned host memory --------------------
  * [UN-2026] §2 "用双缓冲检查点重载隐藏延迟": activations offloaded to pinned host memory are
  * copied back for the backward; with one device buffer the copy and the backward that consumes it
@@ -255,7 +273,8 @@ typedef enum pk_kernel_kind {
     PK_K_MASK = 6,        /* pk_dense_mask */
     PK_K_ROPE = 7,        /* pk_rope_apply */
     PK_K_MOE = 8,         /* all kernels of one pk_moe_group */
-    PK_K_COUNT = 9
+    PK_K_LORA = 9,        /* all kernels of one pk_lora_qkv */
+    PK_K_COUNT = 10
 } pk_kernel_kind;
 #define PK_PROF_ALL ((1 << PK_K_COUNT) - 1)
 

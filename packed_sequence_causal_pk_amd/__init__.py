@@ -19,7 +19,7 @@ from ._lib import PkError, lib
 __all__ = ["PackedMeta", "build_meta", "attn_fwd", "attn_bwd", "fwd_workspace", "bwd_workspace",
            "PackedCausalAttention", "PkError", "tile_rows", "prof_enable", "prof_reset",
            "prof_query", "dense_mask", "rope_apply", "moe_group", "moe_workspace",
-           "ReloadPipeline", "peak_mfma_tflops", "peak_hbm_gbps"]
+           "ReloadPipeline", "peak_mfma_tflops", "peak_hbm_gbps", "lora_qkv", "lora_workspace"]
 
 
 def _torch():
@@ -330,6 +330,33 @@ def peak_hbm_gbps(nbytes: int = 2 << 30, reps: int = 3) -> dict:
             if r:
                 best = max(best, moved / (e0.elapsed_time(e1) * 1e-3) / 1e9)
         out[name] = round(best, 1)
+    return out
+
+
+def lora_workspace(t: int, k: int, n: int, r: int, device):
+    torch = _torch()
+    nb = int(lib().pk_lora_qkv_workspace_bytes(int(t), int(k), int(n), int(r)))
+    if nb == 0:
+        raise PkError("pk_lora_qkv_workspace_bytes", _lib.PK_ERR_UNSUPPORTED)
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def lora_qkv(x, wt, at, bt, scale: float = 1.0, out=None, workspace=None, stream=None):
+    """y = x (W + scale A B) for bf16 x [T, K], wt = W^T [N, K], at = A^T [r, K], bt = B^T [N, r]
+    (a linear layer's weight layout); returns y bf16 [T, N]."""
+    torch = _torch()
+    for z in (x, wt, at, bt):
+        if not z.is_cuda or not z.is_contiguous() or z.dtype != torch.bfloat16 or z.dim() != 2:
+            raise ValueError("x, wt, at, bt must be contiguous 2-D bf16 CUDA tensors")
+    t, k = int(x.shape[0]), int(x.shape[1])
+    n, r = int(wt.shape[0]), int(at.shape[0])
+    if wt.shape[1] != k or at.shape[1] != k or tuple(bt.shape) != (n, r):
+        raise ValueError("shape mismatch")
+    out = torch.empty((t, n), dtype=torch.bfloat16, device=x.device) if out is None else out
+    ws = lora_workspace(t, k, n, r, x.device) if workspace is None else workspace
+    rc = lib().pk_lora_qkv(_ptr(x), _ptr(wt), _ptr(at), _ptr(bt), t, k, n, r, float(scale), _ptr(out),
+                           _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _lib.check("pk_lora_qkv", rc)
     return out
 
 

@@ -18,15 +18,16 @@ PK_META_BAD_LENGTH = 1
 PK_META_BAD_TOTAL = 2
 
 PK_K_META, PK_K_FWD_PREP, PK_K_FWD, PK_K_BWD_PREP, PK_K_BWD, PK_K_BWD_DQ = range(6)
-PK_K_MASK, PK_K_ROPE, PK_K_MOE = 6, 7, 8
+PK_K_MASK, PK_K_ROPE, PK_K_MOE, PK_K_LORA = 6, 7, 8, 9
 KERNEL_KINDS = {"meta": PK_K_META, "fwd_prep": PK_K_FWD_PREP, "fwd": PK_K_FWD,
                 "bwd_prep": PK_K_BWD_PREP, "bwd": PK_K_BWD, "bwd_dq": PK_K_BWD_DQ,
-                "mask": PK_K_MASK, "rope": PK_K_ROPE, "moe": PK_K_MOE}
+                "mask": PK_K_MASK, "rope": PK_K_ROPE, "moe": PK_K_MOE, "lora": PK_K_LORA}
 
 PK_MASK_MAX_TOKENS = 65536
 PK_MOE_MAX_EXPERTS = 1024
 PK_MOE_MAX_ASSIGN = 1 << 26
 PK_MOE_BAD_EXPERT = 1
+PK_LORA_MAX_RANK = 64
 PK_PROF_ALL = (1 << len(KERNEL_KINDS)) - 1
 
 # every function pk.h declares, with (restype, argtypes)
@@ -61,6 +62,8 @@ SIGNATURES = {
     "pk_rope_apply": (_i32, [_vp, _vp, _i32, _i32, _f32, _i32, _vp, _vp]),
     "pk_moe_group_workspace_bytes": (_sz, [_i64, _i32]),
     "pk_moe_group": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pk_lora_qkv_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
+    "pk_lora_qkv": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     "pk_reload_create": (_i32, [ctypes.POINTER(_vp)]),
     "pk_reload_fetch": (_i32, [_vp, _i32, _vp, _vp, _sz]),
     "pk_reload_acquire": (_i32, [_vp, _i32, _vp]),

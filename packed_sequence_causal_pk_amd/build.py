@@ -16,7 +16,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpk.so")
 
 SOURCES = ["pk_api.cpp", "pk_meta.hip", "pk_rope.hip", "pk_fwd.hip", "pk_bwd_kv.hip", "pk_bwd_q.hip",
-           "pk_aux.hip", "pk_moe.hip", "pk_reload.cpp", "pk_peak.hip"]
+           "pk_aux.hip", "pk_moe.hip", "pk_reload.cpp", "pk_peak.hip", "pk_lora.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -377,6 +377,33 @@ pk_status pk_moe_group(const int32_t *router_indices, int64_t n_tokens, int32_t 
                                            status, chunk_counts, chunk_bad, s));
 }
 
+static bool lora_shape_ok(int64_t T, int32_t K, int32_t N, int32_t r) {
+    return T >= 0 && T <= PK_MAX_TOKENS && K >= 64 && K % 64 == 0 && K <= 65536 && N >= 128 &&
+           N % 128 == 0 && N <= 65536 && r >= 1 && r <= PK_LORA_MAX_RANK;
+}
+
+size_t pk_lora_qkv_workspace_bytes(int64_t T, int32_t K, int32_t N, int32_t r) {
+    if (!lora_shape_ok(T, K, N, r)) return 0;
+    return pk::lora_workspace(T, K, N).total;
+}
+
+pk_status pk_lora_qkv(const void *x, const void *wt, const void *at, const void *bt, int64_t T,
+                      int32_t K, int32_t N, int32_t r, float scale, void *y, void *ws,
+                      size_t ws_bytes, void *hip_stream) {
+    if (!lora_shape_ok(T, K, N, r)) return PK_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return PK_ERR_INVALID;
+    if (!wt || !at || !bt || !ws || !aligned256(ws)) return PK_ERR_INVALID;
+    if (T > 0 && (!x || !y)) return PK_ERR_INVALID;
+    const uintptr_t align = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(wt) |
+                            reinterpret_cast<uintptr_t>(at) | reinterpret_cast<uintptr_t>(bt) |
+                            reinterpret_cast<uintptr_t>(y);
+    if (align & 15) return PK_ERR_INVALID;
+    if (ws_bytes < pk::lora_workspace(T, K, N).total) return PK_ERR_CAPACITY;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ProfScope ps(PK_K_LORA, s);
+    return hip_status(pk::launch_lora_qkv(x, wt, at, bt, T, K, N, r, scale, y, ws, s));
+}
+
 const char *pk_status_str(pk_status status) {
     switch (status) {
         case PK_OK: return "ok";

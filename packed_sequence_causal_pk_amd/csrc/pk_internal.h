@@ -93,4 +93,13 @@ hipError_t launch_moe_group(const int32_t *idx, int64_t M, int E, int32_t *count
                             int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *status,
                             int32_t *chunk_counts, int32_t *chunk_bad, hipStream_t s);
 
+// LoRA-adapted QKV projection (pk_lora.hip).
+struct LoraWorkspace {
+    size_t u, apad, bpad, total;
+};
+LoraWorkspace lora_workspace(int64_t T, int K, int N);
+hipError_t launch_lora_qkv(const void *x, const void *wt, const void *at, const void *bt,
+                           int64_t T, int K, int N, int r, float scale, void *y, void *ws,
+                           hipStream_t s);
+
 }  // namespace pk

@@ -139,6 +139,12 @@ def layer_tensors(w: Workload, layer: int, seed: int = 0,
     return tuple(normal_bf16(s, [seed, layer, idx], w.input_scale) for idx, s in enumerate(shapes))
 
 
+# Hidden size of each pack's model (the K of the projection that produces its q, k, v):
+# Llama-3.2-1B 2048, Qwen3-0.6B 1024, Qwen3-14B 5120; the tiny and skewed packs are not tied to a
+# model and use hq x d.
+PROJ_HIDDEN = {"tiny": 128, "llama1b": 2048, "qwen06b": 1024, "qwen14b": 5120, "skewed": 4096}
+
+
 # MoE routing workloads ([UN-2026] §3 names GPT-OSS's router): a 16384-token batch routed top-4
 # among 32 experts (gpt-oss-20b-shaped) or 128 experts (gpt-oss-120b-shaped).
 MOE_WORKLOADS = {

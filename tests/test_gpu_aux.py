@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import packed_sequence_causal_pk_amd as pk
+from oracle import lora_oracle as LO
 from oracle import moe_oracle as MO
 from oracle import pk_oracle as O
 from packed_sequence_causal_pk_amd import synth
@@ -242,3 +243,80 @@ def test_peak_microbenchmarks_run_and_are_plausible():
     say("  mfma %.1f TFLOP/s, hbm %s GB/s" % (tf, bw))
     assert 200.0 < tf < 3000.0
     assert all(500.0 < v < 10000.0 for v in bw.values())
+
+
+# ------------------------------------------------------------------ LoRA-adapted QKV projection
+def _lora_inputs(t, k, n, r, seed):
+    """bf16-exact inputs: x ~ N(0,1), W, A ~ N(0, 1/K), B ~ N(0, 1/(16 r)): x W has unit spread
+    and the adapter term s x A B a spread of s / 4 (an adapter is a small correction to the frozen
+    weight), so the outputs stay in the range the absolute 2e-2 gate was set for (bf16 rounding
+    of |y| >= 8 alone is 2^-5)."""
+    x = synth.normal_bf16((t, k), [seed, 1])
+    w = synth.normal_bf16((k, n), [seed, 2], 1.0 / np.sqrt(k))
+    a = synth.normal_bf16((k, r), [seed, 3], 1.0 / np.sqrt(k))
+    b = synth.normal_bf16((r, n), [seed, 4], 0.25 / np.sqrt(r))
+    return x, w, a, b
+
+
+def _lora_run(x, w, a, b, scale):
+    tx = dev(x)
+    twt, tat, tbt = dev(w.T.copy()), dev(a.T.copy()), dev(b.T.copy())
+    y = pk.lora_qkv(tx, twt, tat, tbt, scale)
+    torch.cuda.synchronize()
+    return to_np(y)
+
+
+def _lora_bound(got, ref, x, w, a, b, scale):
+    """The error the kernel's roundings allow, element by element: the bf16 output (half an ulp,
+    <= 2^-8 |y|), the bf16 rounding of scale * x A (each entry within 2^-8 of itself, so
+    2^-8 (|scale x A| |B|)), and fp32 accumulation over K (2^-20 (|x| |W|), generous)."""
+    x64, w64 = np.asarray(x, np.float64), np.asarray(w, np.float64)
+    u = np.abs(float(scale) * (x64 @ np.asarray(a, np.float64)))
+    bound = (2.0 ** -8 * np.abs(ref) + 2.0 ** -8 * (u @ np.abs(np.asarray(b, np.float64)))
+             + 2.0 ** -20 * (np.abs(x64) @ np.abs(w64)) + 1e-6)
+    err = np.abs(got - ref)
+    bad = err > bound
+    assert not bad.any(), "LoRA QKV outside the rounding bound at %d entries (worst excess %.3e)" % (
+        int(bad.sum()), float((err - bound).max()))
+
+
+@pytest.mark.parametrize("shape", [(300, 256, 384, 16, 0.5), (1, 64, 128, 1, 1.0),
+                                   (129, 128, 256, 64, 2.0), (1000, 640, 640, 8, 0.25),
+                                   (64, 1024, 128, 16, 0.0)])
+def test_lora_qkv_vs_oracle(shape):
+    t, k, n, r, scale = shape
+    say("lora qkv T K N r s", shape)
+    x, w, a, b = _lora_inputs(t, k, n, r, t + k + n + r)
+    got = _lora_run(x, w, a, b, scale)
+    ref = LO.lora_qkv(x, w, a, b, scale)
+    compare("y", got, ref)
+    _lora_bound(got, ref, x, w, a, b, scale)
+
+
+@pytest.mark.parametrize("name", ["llama1b", "qwen06b", "qwen14b"])
+def test_lora_qkv_model_shapes_sampled(name):
+    """The projections that produce each pack's q, k, v (the model's hidden size K,
+    N = (hq + 2 hkv) d, rank 16); rows sampled, each checked against the oracle on its own."""
+    wl = synth.WORKLOADS[name]
+    t, k, n, r = wl.total_tokens, synth.PROJ_HIDDEN[name], (wl.hq + 2 * wl.hkv) * wl.head_dim, 16
+    say("lora qkv", name, "T K N r", t, k, n, r)
+    x, w, a, b = _lora_inputs(t, k, n, r, 5)
+    got = _lora_run(x, w, a, b, 2.0)
+    rows = np.unique(np.concatenate([np.random.default_rng(6).integers(0, t, 48), [0, t - 1]]))
+    ref = LO.lora_qkv(x[rows], w, a, b, 2.0)
+    compare("y", got[rows], ref)
+    _lora_bound(got[rows], ref, x[rows], w, a, b, 2.0)
+    q, kk, v = LO.split_qkv(got, wl.hq, wl.hkv, wl.head_dim)
+    assert q.shape == (t, wl.hq, wl.head_dim) and v.shape == (t, wl.hkv, wl.head_dim)
+
+
+def test_lora_qkv_empty_and_repeatable():
+    x, w, a, b = _lora_inputs(0, 64, 128, 4, 9)
+    y = pk.lora_qkv(dev(x), dev(w.T.copy()), dev(a.T.copy()), dev(b.T.copy()))
+    torch.cuda.synchronize()
+    assert y.shape == (0, 128)
+    x, w, a, b = _lora_inputs(500, 256, 256, 16, 10)
+    args = (dev(x), dev(w.T.copy()), dev(a.T.copy()), dev(b.T.copy()), 1.5)
+    y1, y2 = pk.lora_qkv(*args), pk.lora_qkv(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
