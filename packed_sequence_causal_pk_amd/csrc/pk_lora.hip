@@ -11,18 +11,19 @@
 // Three launches:
 //   k_lora_pad   A^T and B^T copied into rank-64 zero-padded buffers (so the adapter term is one
 //                more full 64-wide step of the same product);
-//   k_gemm_nt<64>   U = s X A (T x 64, columns >= r are zero), bf16;
-//   k_gemm_nt<128>  Y = X W + U B: one product over K + 64 reduction steps, the last 64 from
-//                (U, B), so the adapter costs one extra step instead of a pass over Y.
+//   k_gemm_nt (64 columns)   U = s X A (T x 64, columns >= r are zero), bf16;
+//   k_gemm_nt (128 columns)  Y = X W + U B: one product over K + 64 reduction steps, the last
+//                64 from (U, B), so the adapter costs one extra step instead of a pass over Y.
 //
 // k_gemm_nt computes C [M, N] = alpha (A1 B1^T + A2 B2^T) for row-major A* [M, K*] and B* [N, K*]
-// (K* multiples of 64; the second pair optional).  Workgroup: 128 rows of C x BN columns, 4
+// (K* multiples of 64; the second pair optional).  Workgroup: BM rows of C x BN columns, 4
 // waves; 64-wide K slices of both operands stream through double-buffered swizzled LDS tiles by
 // asynchronous global->LDS copies (the attention kernels' tile format, 64 halves per row).  The
 // product is taken transposed, C^T = B A^T, so each lane's accumulator holds 4 consecutive output
 // columns of one row and the epilogue stores 8 bytes at a time.
 #include "pk_internal.h"
 #include "pk_device.h"
+
 
 namespace {
 
@@ -35,7 +36,6 @@ __device__ __forceinline__ f32x16 mfma32_bf16(f16x8 a, f16x8 b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-constexpr int kBM = 128;   // rows of C per workgroup
 constexpr int kBK = 64;    // K slice per LDS tile (64 halves per tile row)
 constexpr int kRank = 64;  // padded adapter rank
 
@@ -48,10 +48,13 @@ struct GemmArgs {
     float alpha;
 };
 
-// Waves: BN = 128 -> 2 x 2 waves of 64 (C columns) x 64 (C rows); BN = 64 -> 1 x 4 waves of 64 x 32.
-template <int BN>
-__global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs g) {
-    constexpr int WN = BN == 128 ? 2 : 1, WM = 4 / WN;
+// 4 waves as WN x WM over a BM x BN tile of C; each wave computes (BM / WM) rows x (BN / WN)
+// columns.  The larger the wave's tile, the fewer LDS bytes per product (each operand chunk read
+// from LDS feeds MBW or NBW products).
+template <int BM, int BN, int WN, int MINWG>
+__global__ __launch_bounds__(256, MINWG) void k_gemm_nt(GemmArgs g) {
+    constexpr int kBM = BM;
+    constexpr int WM = 4 / WN;
     constexpr int NBW = BN / WN / 32;          // 32-column blocks per wave
     constexpr int MBW = kBM / WM / 32;         // 32-row blocks per wave
     __shared__ __attribute__((aligned(16))) f16 lds_a[2][kBM * kBK];
@@ -206,12 +209,14 @@ hipError_t launch_lora_qkv(const void *x, const void *wt, const void *at, const 
                                                               apad, bpad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || T == 0) return e;
-    const unsigned mtiles = (unsigned)((T + kBM - 1) / kBM);
     GemmArgs g1{(const f16 *)x, apad, nullptr, nullptr, u, T, kRank, K, 0, scale};
-    k_gemm_nt<64><<<mtiles, 256, 0, s>>>(g1);
+    k_gemm_nt<128, 64, 1, 2><<<(unsigned)((T + 127) / 128), 256, 0, s>>>(g1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     GemmArgs g2{(const f16 *)x, (const f16 *)wt, u, bpad, (f16 *)y, T, N, K, kRank, 1.0f};
-    k_gemm_nt<128><<<mtiles * (unsigned)(N / 128), 256, 0, s>>>(g2);
+    // 128 x 128 tiles, 64 KB of LDS, two workgroups per compute unit (measured on the
+    // Qwen3-14B-shaped projection: 879 TFLOP/s; 256 x 128 tiles, whose 96 KB leave one workgroup
+    // per compute unit, 683 TFLOP/s)
+    k_gemm_nt<128, 128, 2, 2><<<(unsigned)((T + 127) / 128) * (unsigned)(N / 128), 256, 0, s>>>(g2);
     return hipGetLastError();
 }
 
