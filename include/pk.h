@@ -144,6 +144,20 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
                       float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
                       void *hip_stream);
 
+/* pk_attn_bwd in two halves, for callers that overlap one layer's prologue with another
+ * layer's attention kernels (the prologue streams HBM while the attention kernels keep the
+ * matrix cores busy).  pk_attn_bwd_prep reads q, k, v, out, lse, dout and writes the backward's
+ * operands into `ws`; pk_attn_bwd_main reads only `ws` (same size as pk_attn_bwd's) and writes
+ * dq, dk, dv.  pk_attn_bwd = prep then main on one stream.  Between the two halves the caller
+ * orders the streams (e.g. with events); two layers in flight need two workspaces. */
+pk_status pk_attn_bwd_prep(pk_meta_t meta, const void *q, const void *k, const void *v,
+                           const void *out, const float *lse, const void *dout, int32_t hq,
+                           int32_t hkv, int32_t d, float softmax_scale, float rope_base, void *ws,
+                           size_t ws_bytes, void *hip_stream);
+pk_status pk_attn_bwd_main(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d,
+                           float softmax_scale, float *dq, float *dk, float *dv, void *ws,
+                           size_t ws_bytes, void *hip_stream);
+
 /* ---- Steps around the attention path, each usable on its own -------------------------- */
 
 #define PK_MASK_MAX_TOKENS 65536  /* largest pack pk_dense_mask accepts (a 4 GiB mask) */

@@ -19,7 +19,8 @@ from ._lib import PkError, lib
 __all__ = ["PackedMeta", "build_meta", "attn_fwd", "attn_bwd", "fwd_workspace", "bwd_workspace",
            "PackedCausalAttention", "PkError", "tile_rows", "prof_enable", "prof_reset",
            "prof_query", "dense_mask", "rope_apply", "moe_group", "moe_workspace",
-           "ReloadPipeline", "peak_mfma_tflops", "peak_hbm_gbps", "lora_qkv", "lora_workspace"]
+           "ReloadPipeline", "peak_mfma_tflops", "peak_hbm_gbps", "lora_qkv", "lora_workspace",
+           "attn_bwd_prep", "attn_bwd_main"]
 
 
 def _torch():
@@ -358,6 +359,34 @@ def lora_qkv(x, wt, at, bt, scale: float = 1.0, out=None, workspace=None, stream
                            _ptr(ws), ws.numel(), _stream_ptr(stream))
     _lib.check("pk_lora_qkv", rc)
     return out
+
+
+def attn_bwd_prep(meta: PackedMeta, q, k, v, out, lse, dout, workspace,
+                  softmax_scale: Optional[float] = None, rope_base: float = 10000.0, stream=None):
+    """First half of attn_bwd: the backward's operands into `workspace` (pk_attn_bwd_prep)."""
+    torch = _torch()
+    t, hq, hkv, d = _dims(q, k)
+    _check_inputs(meta, q, k, v, out, lse, dout, workspace)
+    if t != meta.total_tokens or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch with the pack")
+    if dout.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or lse.dtype != torch.float32:
+        raise ValueError("out/dout must be bfloat16 and lse float32")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    rc = lib().pk_attn_bwd_prep(meta.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                hq, hkv, d, scale, float(rope_base), _ptr(workspace), workspace.numel(),
+                                _stream_ptr(stream))
+    _lib.check("pk_attn_bwd_prep", rc)
+
+
+def attn_bwd_main(meta: PackedMeta, hq: int, hkv: int, d: int, workspace, dq, dk, dv,
+                  softmax_scale: Optional[float] = None, stream=None):
+    """Second half of attn_bwd: dq, dk, dv from the operands attn_bwd_prep left in `workspace`."""
+    _check_inputs(meta, workspace, dq, dk, dv)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    rc = lib().pk_attn_bwd_main(meta.handle, int(hq), int(hkv), int(d), scale, _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+    _lib.check("pk_attn_bwd_main", rc)
+    return dq, dk, dv
 
 
 def prof_enable(on: bool = True, kinds=None) -> None:

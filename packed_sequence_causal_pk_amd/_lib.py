@@ -71,6 +71,9 @@ SIGNATURES = {
     "pk_reload_destroy": (_i32, [_vp]),
     "pk_peak_mfma": (_i32, [_vp, _i32, _i32, _vp]),
     "pk_peak_hbm": (_i32, [_i32, _vp, _vp, _sz, _vp, _vp]),
+    "pk_attn_bwd_prep": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32,
+                                _vp, _sz, _vp]),
+    "pk_attn_bwd_main": (_i32, [_vp, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pk_status_str": (ctypes.c_char_p, [_i32]),
     "pk_prof_enable": (_i32, [_i32]),
     "pk_prof_reset": (_i32, []),

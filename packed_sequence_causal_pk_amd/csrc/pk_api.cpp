@@ -265,35 +265,47 @@ pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *
     return hip_status(e);
 }
 
-pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *v,
-                      const void *out, const float *lse, const void *dout, int32_t hq,
-                      int32_t hkv, int32_t d, float softmax_scale, float rope_base, float *dq,
-                      float *dk, float *dv, void *ws, size_t ws_bytes, void *hip_stream) {
+pk_status pk_attn_bwd_prep(pk_meta_t meta, const void *q, const void *k, const void *v,
+                           const void *out, const float *lse, const void *dout, int32_t hq,
+                           int32_t hkv, int32_t d, float softmax_scale, float rope_base, void *ws,
+                           size_t ws_bytes, void *hip_stream) {
     if (!meta) return PK_ERR_INVALID;
     if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
     if (!(softmax_scale > 0.f) || !(rope_base > 0.f)) return PK_ERR_INVALID;
     const int64_t T = meta->total_tokens;
     if (T == 0) return PK_OK;
-    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !ws || !aligned256(ws))
-        return PK_ERR_INVALID;
+    if (!q || !k || !v || !out || !lse || !dout || !ws || !aligned256(ws)) return PK_ERR_INVALID;
     const pk::BwdWorkspace W = pk::bwd_workspace(T, hq, hkv, d);
     if (ws_bytes < W.total) return PK_ERR_CAPACITY;
     if (!on_meta_device(meta)) return PK_ERR_INVALID;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     char *w = static_cast<char *>(ws);
-    float *dsum = reinterpret_cast<float *>(w + W.dsum);
-    float *lse2 = reinterpret_cast<float *>(w + W.lse2);
-    float *blockmax = reinterpret_cast<float *>(w + W.blockmax);
-    float *scale = reinterpret_cast<float *>(w + W.scale);
     pk::RopeArgs ra{meta->pos, T, hq, hkv, d, rope_base};
-    hipError_t e;
-    {
-        ProfScope ps(PK_K_BWD_PREP, s);
-        e = pk::launch_bwd_prep(ra, q, k, v, out, dout, lse, w + W.qrot, w + W.krot, w + W.vh,
-                                w + W.dout16, w + W.rope, dsum, lse2, blockmax, scale,
-                                softmax_scale * 1.4426950408889634f, s);
-    }
-    if (e != hipSuccess) return PK_ERR_HIP;
+    ProfScope ps(PK_K_BWD_PREP, s);
+    return hip_status(pk::launch_bwd_prep(
+        ra, q, k, v, out, dout, lse, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, w + W.rope,
+        reinterpret_cast<float *>(w + W.dsum), reinterpret_cast<float *>(w + W.lse2),
+        reinterpret_cast<float *>(w + W.blockmax), reinterpret_cast<float *>(w + W.scale),
+        softmax_scale * 1.4426950408889634f, s));
+}
+
+pk_status pk_attn_bwd_main(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d,
+                           float softmax_scale, float *dq, float *dk, float *dv, void *ws,
+                           size_t ws_bytes, void *hip_stream) {
+    if (!meta) return PK_ERR_INVALID;
+    if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.f)) return PK_ERR_INVALID;
+    const int64_t T = meta->total_tokens;
+    if (T == 0) return PK_OK;
+    if (!dq || !dk || !dv || !ws || !aligned256(ws)) return PK_ERR_INVALID;
+    const pk::BwdWorkspace W = pk::bwd_workspace(T, hq, hkv, d);
+    if (ws_bytes < W.total) return PK_ERR_CAPACITY;
+    if (!on_meta_device(meta)) return PK_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    char *w = static_cast<char *>(ws);
+    const float *dsum = reinterpret_cast<const float *>(w + W.dsum);
+    const float *lse2 = reinterpret_cast<const float *>(w + W.lse2);
+    const float *scale = reinterpret_cast<const float *>(w + W.scale);
     pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream *side = side_stream(meta->device);
@@ -302,6 +314,7 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     if (side && kv_grid >= 64 && kv_grid <= 2 * (int64_t)side->cus && hipEventRecord(side->fork, s) == hipSuccess &&
         hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess)
         sq = side->stream;
+    hipError_t e;
     {
         ProfScope ps(PK_K_BWD_DQ, sq);
         e = pk::launch_bwd_q(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
@@ -320,6 +333,17 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     return hip_status(e2);
+}
+
+pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *v,
+                      const void *out, const float *lse, const void *dout, int32_t hq,
+                      int32_t hkv, int32_t d, float softmax_scale, float rope_base, float *dq,
+                      float *dk, float *dv, void *ws, size_t ws_bytes, void *hip_stream) {
+    if (meta && meta->total_tokens > 0 && (!dq || !dk || !dv)) return PK_ERR_INVALID;
+    const pk_status st = pk_attn_bwd_prep(meta, q, k, v, out, lse, dout, hq, hkv, d, softmax_scale,
+                                          rope_base, ws, ws_bytes, hip_stream);
+    if (st != PK_OK) return st;
+    return pk_attn_bwd_main(meta, hq, hkv, d, softmax_scale, dq, dk, dv, ws, ws_bytes, hip_stream);
 }
 
 pk_status pk_dense_mask(pk_meta_t meta, uint8_t *mask, size_t mask_bytes, void *hip_stream) {

@@ -61,6 +61,9 @@ def test_host_side_rejections(lib):
     assert lib.pk_attn_fwd(*args_fwd) == _lib.PK_ERR_INVALID
     args_bwd = [None, fake, fake, fake, fake, fake, fake, 2, 1, 64, 0.125, 1e4, fake, fake, fake, fake, 1 << 20, None]
     assert lib.pk_attn_bwd(*args_bwd) == _lib.PK_ERR_INVALID
+    args_prep = [None, fake, fake, fake, fake, fake, fake, 2, 1, 64, 0.125, 1e4, fake, 1 << 20, None]
+    assert lib.pk_attn_bwd_prep(*args_prep) == _lib.PK_ERR_INVALID
+    assert lib.pk_attn_bwd_main(None, 2, 1, 64, 0.125, fake, fake, fake, fake, 1 << 20, None) == _lib.PK_ERR_INVALID
     assert lib.pk_attn_fwd_workspace_bytes(None, 2, 1, 64) == 0
     assert lib.pk_attn_bwd_workspace_bytes(None, 2, 1, 64) == 0
     assert lib.pk_meta_destroy(None) == _lib.PK_ERR_INVALID

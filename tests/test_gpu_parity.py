@@ -356,3 +356,53 @@ def test_max_tokens_sampled(d):
                 v.index_select(0, ones)[:, gmap].float().cpu().numpy())
         compare("dq1", dq.index_select(0, ones).cpu().numpy(), np.zeros((len(ones), hq, d)))
         compare("dk1", dk.index_select(0, ones).cpu().numpy(), np.zeros((len(ones), hkv, d)))
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b", "qwen06b"])
+def test_split_backward_overlapped_matches_fused(name):
+    """pk_attn_bwd_prep on a side stream and pk_attn_bwd_main on the current one, the prologue of
+    each next layer overlapping the current layer's attention kernels through two workspaces (the
+    benchmark's backward loop), give every layer the same dq, dk, dv as pk_attn_bwd."""
+    w = synth.WORKLOADS[name]
+    lengths = synth.pack_lengths(name)
+    n_layers = 4
+    say("split backward, overlapped", name, "layers", n_layers)
+    meta = pk.build_meta(torch.tensor(lengths, device="cuda"), w.total_tokens)
+    layers, ref = [], []
+    for l in range(n_layers):
+        q, k, v, do = (dev(x) for x in synth.layer_tensors(w, l))
+        out, lse = pk.attn_fwd(meta, q, k, v, w.softmax_scale)
+        layers.append((q, k, v, out, lse, do))
+        ref.append(pk.attn_bwd(meta, q, k, v, out, lse, do, w.softmax_scale))
+    torch.cuda.synchronize()
+    cur, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    wss = [pk.bwd_workspace(meta, w.hq, w.hkv, w.head_dim) for _ in range(2)]
+    ready, free, start = [torch.cuda.Event(), torch.cuda.Event()], [torch.cuda.Event(), torch.cuda.Event()], torch.cuda.Event()
+    start.record(cur)
+    side.wait_event(start)
+    order = list(reversed(range(n_layers)))
+    got = {}
+    for i, l in enumerate(order):
+        slot = i % 2
+        if i == 0:
+            q, k, v, out, lse, do = layers[l]
+            pk.attn_bwd_prep(meta, q, k, v, out, lse, do, wss[0], w.softmax_scale, stream=side)
+            ready[0].record(side)
+        if i + 1 < n_layers:
+            q, k, v, out, lse, do = layers[order[i + 1]]
+            side.wait_event(free[1 - slot])
+            pk.attn_bwd_prep(meta, q, k, v, out, lse, do, wss[1 - slot], w.softmax_scale, stream=side)
+            ready[1 - slot].record(side)
+        cur.wait_event(ready[slot])
+        q = layers[l][0]
+        dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        dk = torch.empty((q.shape[0], w.hkv, w.head_dim), dtype=torch.float32, device="cuda")
+        dv = torch.empty_like(dk)
+        got[l] = pk.attn_bwd_main(meta, w.hq, w.hkv, w.head_dim, wss[slot], dq, dk, dv, w.softmax_scale)
+        free[slot].record(cur)
+    torch.cuda.synchronize()
+    for l in range(n_layers):
+        dq_a, dk_a, dv_a = got[l]
+        dq_b, dk_b, dv_b = ref[l]
+        assert torch.equal(dk_a, dk_b) and torch.equal(dv_a, dv_b), l
+        assert torch.allclose(dq_a, dq_b, atol=1e-5, rtol=0), l
