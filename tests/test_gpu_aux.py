@@ -320,3 +320,80 @@ def test_lora_qkv_empty_and_repeatable():
     y1, y2 = pk.lora_qkv(*args), pk.lora_qkv(*args)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+# ------------------------------------------------------------------------------ maximum sizes
+def test_moe_group_max_size_properties():
+    """PK_MOE_MAX_ASSIGN assignments (2^24 tokens x top-4) among PK_MOE_MAX_EXPERTS experts: too
+    large for the per-expert oracle, so the properties that define the grouping are checked on the
+    device: counts are the per-expert tallies, offsets their exclusive scan, perm a permutation
+    whose experts never decrease and whose flat indices ascend inside each group, inv its inverse.
+    A sampled block of tokens is also checked against the oracle on its own routing."""
+    from packed_sequence_causal_pk_amd import _lib
+    n_tok, top_k, n_exp = _lib.PK_MOE_MAX_ASSIGN // 4, 4, _lib.PK_MOE_MAX_EXPERTS
+    say("moe max size", n_tok, top_k, n_exp)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    idx = torch.randint(0, n_exp, (n_tok, top_k), generator=g, device="cuda", dtype=torch.int32)
+    r = pk.moe_group(idx, n_exp)
+    torch.cuda.synchronize()
+    flat = idx.reshape(-1).long()
+    m = flat.numel()
+    assert int(r["status"].item()) == 0
+    counts = torch.bincount(flat, minlength=n_exp)
+    assert torch.equal(r["counts"].long(), counts)
+    assert int(r["offsets"][0].item()) == 0 and int(r["offsets"][-1].item()) == m
+    assert torch.equal(r["offsets"][1:].long(), torch.cumsum(counts, 0))
+    perm = r["perm"].long()
+    experts = flat[perm]
+    assert bool((experts[1:] >= experts[:-1]).all().item())
+    same = experts[1:] == experts[:-1]
+    assert bool((perm[1:][same] > perm[:-1][same]).all().item())
+    assert torch.equal(r["inv"].long()[perm], torch.arange(m, device="cuda"))
+    del perm, experts, same, counts
+
+
+def test_dense_mask_max_tokens_sampled():
+    """The largest mask (PK_MASK_MAX_TOKENS = 65536 tokens, 4 GiB) of the skewed pack: sampled
+    rows against the oracle's metadata, and the total of kept pairs in closed form."""
+    name = "skewed"
+    lengths = synth.pack_lengths(name)
+    t = int(lengths.sum())
+    say("dense mask max size T", t)
+    ref = O.build_meta(lengths, t)
+    mask = pk.dense_mask(_meta(lengths))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(12).integers(0, t, 64),
+                                     ref["cu_seqlens"][:4], [8191, 8192, t - 1]]))
+    got = mask[torch.tensor(rows, device="cuda")].cpu().numpy()
+    for r, row in zip(rows, got):
+        start = int(ref["cu_seqlens"][ref["seq_id"][r]])
+        assert row[start:r + 1].all() and not row[:start].any() and not row[r + 1:].any(), r
+    assert int(mask.sum(dtype=torch.int64).item()) == O.unmasked_pairs(lengths)
+
+
+def test_rope_apply_max_tokens_sampled():
+    """RoPE over the largest pack (2^20 tokens, positions up to 2047) and 8 heads: sampled tokens
+    against the oracle, within the bf16 rounding bound."""
+    t = 1 << 20
+    rng = np.random.default_rng(13)
+    lengths, acc = [], 0
+    while acc < t:
+        x = int(rng.integers(1, 2048, endpoint=True))
+        lengths.append(x)
+        acc += x
+    lengths[-1] -= acc - t
+    lengths = np.asarray(lengths, np.int32)
+    say("rope max size T", t)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    x = torch.randn(t, 8, 128, generator=g, device="cuda").bfloat16()
+    y = pk.rope_apply(_meta(lengths), x)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([rng.integers(0, t, 256), [0, t - 1]]))
+    tr = torch.tensor(rows, device="cuda")
+    xs = x.index_select(0, tr).float().cpu().numpy()
+    pos = O.build_meta(lengths, t)["pos"][rows]
+    ref = O.rope_apply(xs, pos, 10000.0)
+    got = y.index_select(0, tr).float().cpu().numpy().astype(np.float64)
+    _rope_bound(got, ref)
