@@ -86,7 +86,7 @@ hipError_t launch_bwd_q(const AttnShape &sh, const pk_meta_s &m, const void *qro
 hipError_t launch_dense_mask(const pk_meta_s &m, uint8_t *mask, hipStream_t s);
 hipError_t launch_rope_apply(const pk_meta_s &m, const void *x, int H, int d, float base,
                              int inverse, void *out, hipStream_t s);
-#define PK_MOE_CHUNK 4096   // assignments per workgroup of the grouping kernels
+#define PK_MOE_CHUNK 1024   // assignments per workgroup of the grouping kernels
 int moe_chunks(int64_t M);
 // chunk_counts: [n_experts][moe_chunks(M)] int32, chunk_bad: [moe_chunks(M)] int32 (workspace)
 hipError_t launch_moe_group(const int32_t *idx, int64_t M, int E, int32_t *counts,

@@ -6,7 +6,7 @@
 //
 // The stable sort is a counting sort, which is what "stable sort by expert + bincount" amounts
 // to when the keys are small integers:
-//   k_moe_hist    one workgroup per chunk of 4096 assignments: per-expert counts of the chunk
+//   k_moe_hist    one workgroup per chunk of 1024 assignments: per-expert counts of the chunk
 //                 (LDS atomics), written expert-major [E][n_chunks]; ids outside [0, E) are
 //                 counted per chunk as bad.
 //   k_moe_scan    one workgroup per expert: exclusive scan of that expert's chunk counts, in
@@ -136,11 +136,14 @@ __global__ __launch_bounds__(kThreads) void k_moe_scatter(const int32_t *__restr
         }
         run += c[k];
     }
-    if (b == 0 && threadIdx.x == 0) {
-        offsets[E] = total;
+    if (b == 0) {   // uniform over the workgroup
         int bad = 0;
-        for (int i = 0; i < n_chunks; ++i) bad |= chunk_bad[i];
-        status[0] = bad ? PK_MOE_BAD_EXPERT : 0;
+        for (int i = threadIdx.x; i < n_chunks; i += kThreads) bad |= chunk_bad[i];
+        bad = __syncthreads_or(bad);
+        if (threadIdx.x == 0) {
+            offsets[E] = total;
+            status[0] = bad ? PK_MOE_BAD_EXPERT : 0;
+        }
     }
     __syncthreads();
 
