@@ -157,7 +157,7 @@ def min_bytes(w, T):
 KINDS = ("meta", "fwd_prep", "fwd", "bwd_prep", "bwd", "bwd_dq")
 
 
-def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False):
+def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False, graph=False):
     """Time `steps` steps (after `warmup`) of one workload, timing the kernel kinds
     `timed_kinds` inside that region; a second, shorter pass times every kind for the
     per-kernel breakdown.  Returns the timings and shapes."""
@@ -281,6 +281,22 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
     # a second pass times every kernel kind (for the per-kernel breakdown only)
     nb = max(2, steps // 2)
     bd_ms, _, kern = timed(nb, list(KINDS))
+    graph_ms = None
+    if graph:
+        # the whole step captured once into a HIP graph and replayed (launch-bound small packs)
+        cap = torch.cuda.Stream(device=dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            step()
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(2):
+            g.replay()
+        graph_ms = timed(steps, (), fn=g.replay)[0]
+        del g
     uncached_ms = None
     if uncached:
         uncached_ms = {}
@@ -296,7 +312,7 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
     fwd_flops, bwd_flops = attn_flops(lengths, w.hq, w.head_dim)
     layer_ms = step_ms / L
     return {"w": w, "lengths": lengths, "T": T, "L": L, "steps": nb, "step_ms": step_ms,
-            "main_kern": main_kern, "uncached_step_ms": uncached_ms,
+            "main_kern": main_kern, "uncached_step_ms": uncached_ms, "graph_step_ms": graph_ms,
             "layer_ms": layer_ms, "kern": kern, "fwd_flops": fwd_flops, "bwd_flops": bwd_flops,
             "tflops": (fwd_flops + bwd_flops) * L / (step_ms * 1e-3) / 1e12}
 
@@ -322,6 +338,10 @@ def summary(m):
         "attainable_tflops": round(attainable, 1),
         "frac_of_attainable": round(m["tflops"] / attainable, 4),
         **({} if m["uncached_step_ms"] is None else {"uncached": uncached_summary(m)}),
+        **({} if m.get("graph_step_ms") is None else {
+            "graph_ms_per_step": round(m["graph_step_ms"], 4),
+            "graph_tflops": round((m["fwd_flops"] + m["bwd_flops"]) * m["L"] / (m["graph_step_ms"] * 1e-3) / 1e12, 2),
+            "graph_note": "the same step captured once into a HIP graph and replayed"}),
     }
 
 
@@ -616,7 +636,7 @@ def main():
             # packs also run with the metadata rebuilt per layer call (the uncached mode)
             small = name in ("tiny", "llama1b", "qwen06b")
             other[name] = summary(measure(name, 20 if small else 5, 3,
-                                          uncached=name in ("llama1b", "qwen06b")))
+                                          uncached=name in ("llama1b", "qwen06b"), graph=small))
         result["other_workloads"] = other
         result["steps_around"] = measure_steps_around()
     if not args.no_cpu_baseline:

@@ -472,3 +472,56 @@ def test_work_list_order_does_not_change_results(name):
             assert torch.allclose(x, y, atol=1e-5, rtol=0)
         else:
             assert torch.equal(x, y), name_
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b"])
+def test_layer_loop_in_a_hip_graph(name):
+    """The whole step (B built once, then every layer's forward and backward, including the dQ
+    kernel's side stream on small packs) captured into one HIP graph: every replay, with eager
+    work and synchronisations between replays, gives the eager results."""
+    w = synth.WORKLOADS[name]
+    lengths_d = torch.tensor(synth.pack_lengths(name), device="cuda")
+    t, n_layers = w.total_tokens, min(w.layers, 3)
+    layers = []
+    for l in range(n_layers):
+        q, k, v, do = (dev(x) for x in synth.layer_tensors(w, l))
+        layers.append({"q": q, "k": k, "v": v, "do": do,
+                       "out": torch.empty_like(q), "lse": torch.empty(w.hq, t, device="cuda"),
+                       "dq": torch.empty(q.shape, device="cuda"),
+                       "dk": torch.empty(k.shape, device="cuda"), "dv": torch.empty(k.shape, device="cuda")})
+    meta0 = pk.build_meta(lengths_d, t)
+    ws_f = pk.fwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
+    ws_b = pk.bwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
+
+    def step():
+        meta = pk.build_meta(lengths_d, t)
+        for x in layers:
+            pk.attn_fwd(meta, x["q"], x["k"], x["v"], w.softmax_scale, out=x["out"], lse=x["lse"], workspace=ws_f)
+        for x in reversed(layers):
+            pk.attn_bwd(meta, x["q"], x["k"], x["v"], x["out"], x["lse"], x["do"], w.softmax_scale,
+                        dq=x["dq"], dk=x["dk"], dv=x["dv"], workspace=ws_b)
+        return meta
+
+    say("layer loop in a HIP graph", name, "layers", n_layers)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        keep = step()   # warm up on the capture stream's pool
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [{k_: x[k_].clone() for k_ in ("out", "lse", "dq", "dk", "dv")} for x in layers]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured = step()
+    for rep in range(3):
+        for x in layers:   # eager work between replays: clobber every output
+            for k_ in ("out", "lse", "dq", "dk", "dv"):
+                x[k_].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, r in zip(layers, ref):
+            for k_ in ("out", "lse", "dk", "dv"):
+                assert torch.equal(x[k_], r[k_]), (rep, k_)
+            assert torch.allclose(x["dq"], r["dq"], atol=1e-5, rtol=0), rep
+    del keep, captured
