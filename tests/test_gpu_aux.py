@@ -397,3 +397,24 @@ def test_rope_apply_max_tokens_sampled():
     ref = O.rope_apply(xs, pos, 10000.0)
     got = y.index_select(0, tr).float().cpu().numpy().astype(np.float64)
     _rope_bound(got, ref)
+
+
+def test_dense_mask_flat_path_near_max():
+    """A pack whose token count is not a multiple of 16 (the flattened-byte form of the kernel,
+    runs crossing rows) at 65519 tokens, the largest such size below the limit: sampled rows
+    against the oracle's metadata and the kept-pair total."""
+    lengths = np.concatenate([synth.pack_lengths("skewed")[:-1], [0]]).astype(np.int32)
+    lengths = lengths[lengths > 0]
+    lengths[-1] -= int(lengths.sum()) - 65519
+    t = int(lengths.sum())
+    assert t == 65519 and lengths.min() >= 1
+    say("dense mask flat path T", t)
+    ref = O.build_meta(lengths, t)
+    mask = pk.dense_mask(_meta(lengths))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(14).integers(0, t, 64), [0, 1, t - 2, t - 1]]))
+    got = mask[torch.tensor(rows, device="cuda")].cpu().numpy()
+    for r, row in zip(rows, got):
+        start = int(ref["cu_seqlens"][ref["seq_id"][r]])
+        assert row[start:r + 1].all() and not row[:start].any() and not row[r + 1:].any(), r
+    assert int(mask.sum(dtype=torch.int64).item()) == O.unmasked_pairs(lengths)
