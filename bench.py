@@ -128,13 +128,29 @@ def cpu_baseline(w, lengths, target_s):
             break
     cores = len(os.sched_getaffinity(0))
     groups = sorted(set(c[0] for c in chosen))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rate = done_flops / done_s
+    fl, bl = attn_flops(lengths, w.hq, w.head_dim)
     return {
-        "value": done_flops / done_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "value": rate / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
         "sample": "layer 0, KV heads %s each with its %d query heads, %d (KV head, sequence) "
                   "pairs of the pack (whole sequences, shortest first), fwd+bwd float64 numpy, "
                   "%.1f s; TFLOP/s counts the same algorithmic FLOPs as the GPU value"
                   % (groups, w.group, len(chosen), done_s),
         "seconds": round(done_s, 2),
+        "cpu_model": model,
+        "extrapolated_s_per_layer": round((fl + bl) / rate, 3),
+        "extrapolated_s_per_step": round((fl + bl) * w.layers / rate, 3),
+        "extrapolation": "the sample's FLOP rate applied to a whole layer and to the %d-layer step"
+                         % w.layers,
     }
 
 
