@@ -1,5 +1,5 @@
 // Measured roofline of the device: the dense fp16 matrix-core rate and the HBM read, write and
-// copy bandwidths the attention kernels are judged against.  Measurement aids only; nothing on
+// copy bandwidths the attention kernels are measured against.  Measurement aids only; nothing on
 // the attention path calls them.
 //
 //   k_peak_mfma  every wave runs 4 independent chains of v_mfma_f32_32x32x16_f16 (the product
