@@ -276,7 +276,9 @@ const char *pk_status_str(pk_status status);
  * records a pair of HIP events around it on its stream (no synchronisation; each record costs
  * a few microseconds of GPU time, so enable only the kinds to be timed).  pk_prof_query
  * synchronises on the recorded events and returns the total milliseconds and launch count of
- * one kernel kind since the last reset. */
+ * one kernel kind since the last reset.  The records are process-wide and guarded by a lock, so
+ * several host threads may launch while timing is on.  The events belong to the device that was
+ * current at the first pk_prof_enable; launches on other devices are not recorded. */
 typedef enum pk_kernel_kind {
     PK_K_META = 0,        /* all metadata-build kernels of one pk_build_meta */
     PK_K_FWD_PREP = 1,    /* forward prologue: RoPE table + rotated K */

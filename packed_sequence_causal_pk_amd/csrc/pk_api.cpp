@@ -23,6 +23,9 @@ bool shape_supported(int hq, int hkv, int d) {
 }
 
 // ------------------------------------------------------------------ kernel timing (optional)
+// The records live in one process-wide table guarded by g_prof_mu, so calls from several host
+// threads may record at once.  A scope keeps its own copy of its stop event (the pool is never
+// freed), so a reset while a launch is being recorded leaves nothing dangling.
 struct ProfRecord {
     int kind;
     hipEvent_t start, stop;
@@ -34,12 +37,14 @@ struct Prof {
     size_t used = 0;
 };
 Prof g_prof;
+std::mutex g_prof_mu;
 constexpr size_t kProfCapacity = 16384;  // event pairs
 
 struct ProfScope {
-    ProfRecord *rec = nullptr;
+    hipEvent_t stop = nullptr;
     hipStream_t stream;
     ProfScope(int kind, hipStream_t s) : stream(s) {
+        std::lock_guard<std::mutex> lock(g_prof_mu);
         if (!((g_prof.mask >> kind) & 1u) || g_prof.used >= kProfCapacity) return;
         ProfRecord r;
         r.kind = kind;
@@ -47,11 +52,11 @@ struct ProfScope {
         r.stop = g_prof.pool[2 * g_prof.used + 1];
         if (hipEventRecord(r.start, s) != hipSuccess) return;
         g_prof.recs.push_back(r);
-        rec = &g_prof.recs.back();
+        stop = r.stop;
         ++g_prof.used;
     }
     ~ProfScope() {
-        if (rec) (void)hipEventRecord(rec->stop, stream);
+        if (stop) (void)hipEventRecord(stop, stream);
     }
 };
 
@@ -442,13 +447,15 @@ const char *pk_status_str(pk_status status) {
 
 pk_status pk_prof_enable(int32_t kinds) {
     if (kinds < 0 || kinds > PK_PROF_ALL) return PK_ERR_INVALID;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
     if (kinds && g_prof.pool.empty()) {
-        g_prof.pool.resize(2 * kProfCapacity);
-        for (auto &ev : g_prof.pool)
-            if (hipEventCreate(&ev) != hipSuccess) {
-                g_prof.pool.clear();
+        std::vector<hipEvent_t> pool(2 * kProfCapacity, nullptr);
+        for (size_t e = 0; e < pool.size(); ++e)
+            if (hipEventCreate(&pool[e]) != hipSuccess) {
+                for (size_t x = 0; x < e; ++x) (void)hipEventDestroy(pool[x]);
                 return PK_ERR_HIP;
             }
+        g_prof.pool.swap(pool);
         g_prof.recs.reserve(kProfCapacity);
     }
     g_prof.mask = (uint32_t)kinds;
@@ -456,6 +463,7 @@ pk_status pk_prof_enable(int32_t kinds) {
 }
 
 pk_status pk_prof_reset(void) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
     g_prof.recs.clear();
     g_prof.used = 0;
     return PK_OK;
@@ -463,18 +471,21 @@ pk_status pk_prof_reset(void) {
 
 pk_status pk_prof_query(int32_t kind, double *total_ms, int64_t *launches) {
     if (!total_ms || !launches || kind < 0 || kind >= PK_K_COUNT) return PK_ERR_INVALID;
+    std::vector<ProfRecord> recs;
+    {
+        std::lock_guard<std::mutex> lock(g_prof_mu);
+        for (const ProfRecord &r : g_prof.recs)
+            if (r.kind == kind) recs.push_back(r);
+    }
     double sum = 0.0;
-    int64_t n = 0;
-    for (const ProfRecord &r : g_prof.recs) {
-        if (r.kind != kind) continue;
+    for (const ProfRecord &r : recs) {
         if (hipEventSynchronize(r.stop) != hipSuccess) return PK_ERR_HIP;
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return PK_ERR_HIP;
         sum += ms;
-        ++n;
     }
     *total_ms = sum;
-    *launches = n;
+    *launches = (int64_t)recs.size();
     return PK_OK;
 }
 
