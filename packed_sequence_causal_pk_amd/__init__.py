@@ -149,6 +149,22 @@ def _check_inputs(meta, *tensors):
             raise ValueError("tensor on %s, meta on %s" % (t.device, meta.device))
 
 
+def _check_out(name, t, shape, dtype, device):
+    """A caller-supplied output: exactly the shape, dtype and device the call writes, contiguous
+    (the library writes through the raw pointer, so nothing else may be passed)."""
+    if (t.dtype != dtype or tuple(t.shape) != tuple(int(x) for x in shape) or not t.is_contiguous()
+            or t.device != device):
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on %s"
+                         % (name, dtype, tuple(shape), device))
+
+
+def _ws_bytes(ws, device) -> int:
+    """Byte size of a caller-supplied workspace (any dtype; contiguous, on the call's device)."""
+    if not ws.is_cuda or not ws.is_contiguous() or ws.device != device:
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
+    return int(ws.numel()) * int(ws.element_size())
+
+
 def attn_fwd(meta: PackedMeta, q, k, v, softmax_scale: Optional[float] = None,
              rope_base: float = 10000.0, out=None, lse=None, workspace=None, stream=None):
     """(out bf16 [T,hq,d], lse float32 [hq,T]) for bf16 q [T,hq,d], k, v [T,hkv,d]."""
@@ -162,12 +178,31 @@ def attn_fwd(meta: PackedMeta, q, k, v, softmax_scale: Optional[float] = None,
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((hq, t), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_out("out", out, q.shape, torch.bfloat16, q.device)
+    _check_out("lse", lse, (hq, t), torch.float32, q.device)
     ws = fwd_workspace(meta, hq, hkv, d) if workspace is None else workspace
     rc = lib().pk_attn_fwd(meta.handle, _ptr(q), _ptr(k), _ptr(v), hq, hkv, d, scale,
-                           float(rope_base), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                           float(rope_base), _ptr(out), _ptr(lse), _ptr(ws), _ws_bytes(ws, q.device),
                            _stream_ptr(stream))
     _lib.check("pk_attn_fwd", rc)
     return out, lse
+
+
+def _check_bwd_inputs(q, k, v, out, lse, dout, t, hq, d):
+    torch = _torch()
+    for name, x in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if x.dtype != torch.bfloat16:
+            raise ValueError("%s must be bfloat16" % name)
+    if k.shape != v.shape or k.dim() != 3 or k.shape[0] != t or k.shape[2] != d:
+        raise ValueError("k and v must be [T, hkv, d] like each other")
+    _check_out("lse", lse, (hq, t), torch.float32, q.device)
+
+
+def _check_grads(dq, dk, dv, q, k):
+    torch = _torch()
+    _check_out("dq", dq, q.shape, torch.float32, q.device)
+    _check_out("dk", dk, k.shape, torch.float32, q.device)
+    _check_out("dv", dv, k.shape, torch.float32, q.device)
 
 
 def attn_bwd(meta: PackedMeta, q, k, v, out, lse, dout, softmax_scale: Optional[float] = None,
@@ -178,16 +213,16 @@ def attn_bwd(meta: PackedMeta, q, k, v, out, lse, dout, softmax_scale: Optional[
     _check_inputs(meta, q, k, v, out, lse, dout)
     if t != meta.total_tokens or out.shape != q.shape or dout.shape != q.shape:
         raise ValueError("shape mismatch with the pack")
-    if dout.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or lse.dtype != torch.float32:
-        raise ValueError("out/dout must be bfloat16 and lse float32")
+    _check_bwd_inputs(q, k, v, out, lse, dout, t, hq, d)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    _check_grads(dq, dk, dv, q, k)
     ws = bwd_workspace(meta, hq, hkv, d) if workspace is None else workspace
     rc = lib().pk_attn_bwd(meta.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
                            hq, hkv, d, scale, float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv),
-                           _ptr(ws), ws.numel(), _stream_ptr(stream))
+                           _ptr(ws), _ws_bytes(ws, q.device), _stream_ptr(stream))
     _lib.check("pk_attn_bwd", rc)
     return dq, dk, dv
 
@@ -198,8 +233,7 @@ def dense_mask(meta: PackedMeta, out=None, stream=None):
     torch = _torch()
     t = meta.total_tokens
     out = torch.empty((t, t), dtype=torch.bool, device=meta.device) if out is None else out
-    if out.dtype != torch.bool or tuple(out.shape) != (t, t) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [T, T] bool tensor")
+    _check_out("out", out, (t, t), torch.bool, meta.device)
     rc = lib().pk_dense_mask(meta.handle, _ptr(out), out.numel(), _stream_ptr(stream))
     _lib.check("pk_dense_mask", rc)
     return out
@@ -214,8 +248,7 @@ def rope_apply(meta: PackedMeta, x, rope_base: float = 10000.0, inverse: bool = 
     if x.dtype != torch.bfloat16 or x.dim() != 3 or x.shape[0] != meta.total_tokens:
         raise ValueError("x must be bf16 [T, h, d] with T the pack's token count")
     out = torch.empty_like(x) if out is None else out
-    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
-        raise ValueError("out must match x")
+    _check_out("out", out, x.shape, x.dtype, x.device)
     rc = lib().pk_rope_apply(meta.handle, _ptr(x), int(x.shape[1]), int(x.shape[2]),
                              float(rope_base), 1 if inverse else 0, _ptr(out), _stream_ptr(stream))
     _lib.check("pk_rope_apply", rc)
@@ -249,7 +282,7 @@ def moe_group(router_indices, n_experts: int, workspace=None, stream=None):
     ws = moe_workspace(m, n_experts, dev) if workspace is None else workspace
     rc = lib().pk_moe_group(_ptr(idx), n_tok, top_k, int(n_experts), _ptr(res["counts"]),
                             _ptr(res["offsets"]), _ptr(res["perm"]), _ptr(res["inv"]),
-                            _ptr(res["status"]), _ptr(ws), ws.numel(), _stream_ptr(stream))
+                            _ptr(res["status"]), _ptr(ws), _ws_bytes(ws, dev), _stream_ptr(stream))
     _lib.check("pk_moe_group", rc)
     return res
 
@@ -353,10 +386,13 @@ def lora_qkv(x, wt, at, bt, scale: float = 1.0, out=None, workspace=None, stream
     n, r = int(wt.shape[0]), int(at.shape[0])
     if wt.shape[1] != k or at.shape[1] != k or tuple(bt.shape) != (n, r):
         raise ValueError("shape mismatch")
+    if any(z.device != x.device for z in (wt, at, bt)):
+        raise ValueError("x, wt, at, bt must be on one device")
     out = torch.empty((t, n), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _check_out("out", out, (t, n), torch.bfloat16, x.device)
     ws = lora_workspace(t, k, n, r, x.device) if workspace is None else workspace
     rc = lib().pk_lora_qkv(_ptr(x), _ptr(wt), _ptr(at), _ptr(bt), t, k, n, r, float(scale), _ptr(out),
-                           _ptr(ws), ws.numel(), _stream_ptr(stream))
+                           _ptr(ws), _ws_bytes(ws, x.device), _stream_ptr(stream))
     _lib.check("pk_lora_qkv", rc)
     return out
 
@@ -369,22 +405,26 @@ def attn_bwd_prep(meta: PackedMeta, q, k, v, out, lse, dout, workspace,
     _check_inputs(meta, q, k, v, out, lse, dout, workspace)
     if t != meta.total_tokens or out.shape != q.shape or dout.shape != q.shape:
         raise ValueError("shape mismatch with the pack")
-    if dout.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or lse.dtype != torch.float32:
-        raise ValueError("out/dout must be bfloat16 and lse float32")
+    _check_bwd_inputs(q, k, v, out, lse, dout, t, hq, d)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     rc = lib().pk_attn_bwd_prep(meta.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
-                                hq, hkv, d, scale, float(rope_base), _ptr(workspace), workspace.numel(),
-                                _stream_ptr(stream))
+                                hq, hkv, d, scale, float(rope_base), _ptr(workspace),
+                                _ws_bytes(workspace, q.device), _stream_ptr(stream))
     _lib.check("pk_attn_bwd_prep", rc)
 
 
 def attn_bwd_main(meta: PackedMeta, hq: int, hkv: int, d: int, workspace, dq, dk, dv,
                   softmax_scale: Optional[float] = None, stream=None):
     """Second half of attn_bwd: dq, dk, dv from the operands attn_bwd_prep left in `workspace`."""
+    torch = _torch()
     _check_inputs(meta, workspace, dq, dk, dv)
+    t = meta.total_tokens
+    _check_out("dq", dq, (t, hq, d), torch.float32, meta.device)
+    _check_out("dk", dk, (t, hkv, d), torch.float32, meta.device)
+    _check_out("dv", dv, (t, hkv, d), torch.float32, meta.device)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     rc = lib().pk_attn_bwd_main(meta.handle, int(hq), int(hkv), int(d), scale, _ptr(dq), _ptr(dk), _ptr(dv),
-                                _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+                                _ptr(workspace), _ws_bytes(workspace, meta.device), _stream_ptr(stream))
     _lib.check("pk_attn_bwd_main", rc)
     return dq, dk, dv
 

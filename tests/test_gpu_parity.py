@@ -525,3 +525,34 @@ def test_layer_loop_in_a_hip_graph(name):
                 assert torch.equal(x[k_], r[k_]), (rep, k_)
             assert torch.allclose(x["dq"], r["dq"], atol=1e-5, rtol=0), rep
     del keep, captured
+
+
+def test_binding_rejects_mismatched_outputs_and_workspaces():
+    """Caller-supplied outputs and workspaces are checked in the binding before any launch."""
+    lengths = [37, 100, 5, 114]
+    t = sum(lengths)
+    meta = pk.build_meta(torch.tensor(lengths, dtype=torch.int32, device="cuda"), t)
+    q = torch.randn(t, 2, 64, device="cuda").bfloat16()
+    k = torch.randn(t, 1, 64, device="cuda").bfloat16()
+    v = torch.randn(t, 1, 64, device="cuda").bfloat16()
+    bad = [dict(out=torch.empty(t, 2, 32, device="cuda").bfloat16()),
+           dict(out=torch.empty(t, 2, 64, device="cuda")),
+           dict(lse=torch.empty(t, 2, device="cuda")),
+           dict(lse=torch.empty(2, 2 * t, device="cuda")[:, ::2]),
+           dict(workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda")[::2])]
+    for kw in bad:
+        say("attn_fwd rejects", sorted(kw))
+        with pytest.raises(ValueError):
+            pk.attn_fwd(meta, q, k, v, **kw)
+    out, lse = pk.attn_fwd(meta, q, k, v)
+    for kw in [dict(dq=torch.empty(t, 2, 64, device="cuda").bfloat16()),
+               dict(dk=torch.empty(t, 2, 64, device="cuda")),
+               dict(dv=torch.empty(t, 1, 32, device="cuda"))]:
+        say("attn_bwd rejects", sorted(kw))
+        with pytest.raises(ValueError):
+            pk.attn_bwd(meta, q, k, v, out, lse, out, **kw)
+    with pytest.raises(ValueError):
+        pk.attn_bwd(meta, q, k, v, out, lse, out.float())
+    with pytest.raises(ValueError):
+        pk.dense_mask(meta, out=torch.empty(t, t + 1, dtype=torch.bool, device="cuda"))
+    torch.cuda.synchronize()
