@@ -20,9 +20,12 @@
 // incoming gradient.  k_bwd_rows then writes the rotated Q (times scale * log2(e)) and K, V and
 // sigma * dout in fp16, -sigma * rowsum(dout * out) and -lse * log2(e).
 //
-// Thread layout of the two per-token kernels: one thread per (token t, group c of 4 rotation pairs);
-// the thread owns elements d in [4c, 4c+4) and their partners d + D/2 for every head, so each
-// rotation stays inside one thread and a token's D/8 threads read each half-row contiguously.
+// The table: inverse frequencies base^(-2i/d) in double precision (once per workgroup, in LDS),
+// each angle p * f in double, reduced modulo 2 pi in double, and its cosine and sine taken in
+// float.  Thread layout: k_fwd_prep has one thread per (token, KV head, group c of 4 rotation
+// pairs), the table blocks of k_bwd_pre one per (token, c); a thread owns elements d in
+// [4c, 4c+4) and their partners d + D/2, so each rotation stays inside one thread and a token's
+// threads read each half-row contiguously.
 #include <algorithm>
 
 #include "pk_internal.h"
@@ -32,24 +35,36 @@ namespace {
 
 using pkd::zero_bf16x8;
 
+// Inverse frequencies base^(-2i/D) of the D/2 rotation pairs, in double precision, into the
+// workgroup's LDS (every thread of the workgroup must call this before any returns).
+template <int D>
+__device__ __forceinline__ void rope_inv_freq(float base, double *s_inv) {
+    if (threadIdx.x < D / 2) s_inv[threadIdx.x] = exp2(-(2.0 * threadIdx.x / D) * log2((double)base));
+    __syncthreads();
+}
+
+// cos and sin of the angles of pairs [4c, 4c + 4) of token t: p * f formed in double, reduced
+// modulo 2 pi in double (a two-part 2 pi), then sine and cosine of the reduced angle in float
+// (the fp32 table needs no more).  Written to the table when `write`.
 template <int D>
 __device__ __forceinline__ void rope_factors(const int32_t *__restrict__ pos, int64_t t, int c,
-                                             float base, float2 *__restrict__ table, float cs[4],
-                                             float sn[4]) {
+                                             const double *s_inv, float2 *__restrict__ table,
+                                             bool write, float cs[4], float sn[4]) {
+    constexpr double kTwoPiHi = 6.283185307179586, kTwoPiLo = 2.4492935982947064e-16;
+    constexpr double kInvTwoPi = 0.15915494309189535;
     const double p = (double)pos[t];
-    const double lb = log2((double)base);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int i = 4 * c + k;
-        const double inv_freq = exp2(-(2.0 * i / D) * lb);
-        double s, co;
-        sincos(p * inv_freq, &s, &co);
-        cs[k] = (float)co;
-        sn[k] = (float)s;
+        const double a = p * s_inv[4 * c + k];
+        const double n = rint(a * kInvTwoPi);
+        const double r = fma(-n, kTwoPiLo, fma(-n, kTwoPiHi, a));
+        sincosf((float)r, &sn[k], &cs[k]);
     }
-    float4 *dst = reinterpret_cast<float4 *>(table + t * (D / 2) + 4 * c);
-    dst[0] = make_float4(cs[0], sn[0], cs[1], sn[1]);
-    dst[1] = make_float4(cs[2], sn[2], cs[3], sn[3]);
+    if (write) {
+        float4 *dst = reinterpret_cast<float4 *>(table + t * (D / 2) + 4 * c);
+        dst[0] = make_float4(cs[0], sn[0], cs[1], sn[1]);
+        dst[1] = make_float4(cs[2], sn[2], cs[3], sn[3]);
+    }
 }
 
 __device__ __forceinline__ void load4(const bf16 *p, float x[4]) {
@@ -92,6 +107,8 @@ __device__ __forceinline__ void rotate_row(const bf16 *__restrict__ src, f16 *__
     store4(dst + D / 2 + 4 * c, y2);
 }
 
+// One thread per (token t, KV head h, group c of 4 rotation pairs), c fastest so that a wave's
+// loads and stores are contiguous; the threads of head 0 also write the table.
 template <int D>
 __global__ __launch_bounds__(256) void k_fwd_prep(const int32_t *__restrict__ pos, int64_t T,
                                                   int hkv, float base,
@@ -101,17 +118,19 @@ __global__ __launch_bounds__(256) void k_fwd_prep(const int32_t *__restrict__ po
                                                   f16 *__restrict__ vh,
                                                   float2 *__restrict__ table) {
     constexpr int G = D / 8;
+    __shared__ double s_inv[D / 2];
+    rope_inv_freq<D>(base, s_inv);
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t t = gid / G;
     const int c = (int)(gid % G);
+    const int64_t rest = gid / G;
+    const int h = (int)(rest % hkv);
+    const int64_t t = rest / hkv;
     if (t >= T) return;
     float cs[4], sn[4];
-    rope_factors<D>(pos, t, c, base, table, cs, sn);
-    for (int h = 0; h < hkv; ++h) {
-        const int64_t off = (t * hkv + h) * D;
-        rotate_row<D>(k + off, krot + off, c, cs, sn);
-        convert_row<D>(v + off, vh + off, c);
-    }
+    rope_factors<D>(pos, t, c, s_inv, table, h == 0, cs, sn);
+    const int64_t off = (t * hkv + h) * D;
+    rotate_row<D>(k + off, krot + off, c, cs, sn);
+    convert_row<D>(v + off, vh + off, c);
 }
 
 // max|dout| per block over the flattened [T * hq * d] tensor, 8 elements per thread step.
@@ -154,11 +173,13 @@ template <int D>
 __device__ __forceinline__ void rope_table_block(const int32_t *__restrict__ pos, int64_t T, float base,
                                                  float2 *__restrict__ table, int b) {
     constexpr int G = D / 8;
+    __shared__ double s_inv[D / 2];
+    rope_inv_freq<D>(base, s_inv);
     const int64_t gid = (int64_t)b * 256 + threadIdx.x;
     const int64_t t = gid / G;
     if (t >= T) return;
     float cs[4], sn[4];
-    rope_factors<D>(pos, t, (int)(gid % G), base, table, cs, sn);
+    rope_factors<D>(pos, t, (int)(gid % G), s_inv, table, true, cs, sn);
 }
 
 // First launch of the backward prologue, two independent jobs in one grid (one launch fewer,
@@ -303,7 +324,7 @@ unsigned dmax_blocks(int64_t T, int hq, int d) {
 
 hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, const void *v, void *krot, void *vh,
                            void *rope, hipStream_t s) {
-    const unsigned g = prep_blocks(r.T, r.d);
+    const unsigned g = (unsigned)((r.T * r.hkv * (r.d / 8) + 255) / 256);
     if (r.d == 128)
         k_fwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hkv, r.rope_base, (const bf16 *)k,
                                            (const bf16 *)v, (f16 *)krot, (f16 *)vh, (float2 *)rope);
