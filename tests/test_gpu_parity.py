@@ -94,6 +94,8 @@ SMALL_CASES = [
     ([64, 1, 63, 130, 2, 250], 8, 2, 64),    # boundaries inside tiles at many offsets
     ("short", 4, 1, 128),                    # many short sequences (1..16), skew-like
     ([2000, 47], 2, 1, 64),                  # long sequence, d = 64
+    ([200, 56, 1], 16, 1, 64),               # 16 query heads on one KV head
+    ([129, 127], 1, 1, 128),                 # a single head, boundaries one off the tile edge
 ]
 
 
