@@ -13,11 +13,12 @@
 //
 // Rotated q and k, v, and the scaled dout are written as fp16, the matrix-core operand format of
 // the attention kernels, so those can copy tiles straight into LDS.  The backward prologue first
-// reduces max|dout| per block (k_bwd_pre, whose other blocks write the (cos, sin) table);
-// k_bwd_scale turns the maxima into a power of two sigma with
-// max|dout| * sigma in [1, 2), so the backward's fp16 gradient operands (dout and dS, both scaled
+// reduces max|dout| per block (k_bwd_pre, whose other blocks write the (cos, sin) table).
+// k_bwd_rows then turns the maxima into a power of two sigma with max|dout| * sigma in [1, 2)
+// (each of its workgroups that holds query rows reduces the maxima itself, which costs less
+// than a launch of its own), so the backward's fp16 gradient operands (dout and dS, both scaled
 // by sigma, unscaled exactly at the end) stay inside fp16's range whatever the magnitude of the
-// incoming gradient.  k_bwd_rows then writes the rotated Q (times scale * log2(e)) and K, V and
+// incoming gradient, and writes the rotated Q (times scale * log2(e)) and K, V and
 // sigma * dout in fp16, -sigma * rowsum(dout * out) and -lse * log2(e).
 //
 // The table: inverse frequencies base^(-2i/d) in double precision (once per workgroup, in LDS),
@@ -211,6 +212,29 @@ __device__ __forceinline__ void table8(const float2 *__restrict__ table, int64_t
     }
 }
 
+// The dout scale, computed by every workgroup that needs it from the per-block maxima (at most
+// 1024 floats, an L2-resident read): sigma = 2^e with max|dout| * sigma in [1, 2) (sigma = 1
+// when the maximum is 0 or not finite).  Every thread of the workgroup must call it; all get
+// the same sigma.
+__device__ __forceinline__ float block_sigma(const float *__restrict__ blockmax, int nb) {
+    __shared__ float s_max[4];
+    float m = 0.f;
+    for (int i = threadIdx.x; i < nb; i += 256) m = fmaxf(m, blockmax[i]);
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    float sigma = 1.f;
+    if (m > 0.f && m <= 3.0e38f) {
+        int ex = 0;
+        (void)frexpf(m, &ex);           // m = f * 2^ex, f in [0.5, 1)
+        ex = min(max(1 - ex, -100), 100);
+        sigma = ldexpf(1.f, ex);
+    }
+    return sigma;
+}
+
 // Per-row work of the backward prologue, one thread per (row, group c of 8 rotation pairs): the
 // thread owns elements [8c, 8c + 8) of a head row and their partners + D/2, read and written as
 // 16-byte vectors.  Rows [0, T * hkv) are K rows (rotated) with their V rows (converted); rows
@@ -227,7 +251,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
                                                   const bf16 *__restrict__ out,
                                                   const bf16 *__restrict__ dout,
                                                   const float *__restrict__ lse,
-                                                  const float *__restrict__ dscale,
+                                                  const float *__restrict__ blockmax, int nb,
+                                                  float *__restrict__ dscale,
                                                   f16 *__restrict__ qrot,
                                                   f16 *__restrict__ krot,
                                                   f16 *__restrict__ vh,
@@ -239,6 +264,17 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
     const int c = (int)(gid % G);
     int64_t row = gid / G;
     const int64_t nkv = T * hkv;
+    // sigma, in the workgroups that hold query rows (a workgroup-uniform test); the first of
+    // them also stores {sigma, 1/sigma} for the attention kernels
+    float sigma = 1.f;
+    const int64_t first_q_block = nkv * G / 256;
+    if ((int64_t)blockIdx.x >= first_q_block) {
+        sigma = block_sigma(blockmax, nb);
+        if ((int64_t)blockIdx.x == first_q_block && threadIdx.x == 0) {
+            dscale[0] = sigma;
+            dscale[1] = 1.f / sigma;
+        }
+    }
     float cs[8], sn[8];
     auto rotate = [&](const bf16 *src, f16 *dst, float mult) {
         const bf16x8 x1 = pkd::load_bf16x8(src + 8 * c), x2 = pkd::load_bf16x8(src + D / 2 + 8 * c);
@@ -270,7 +306,6 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
     table8<D>(table, t, c, cs, sn);
     const int64_t off = row * D;
     rotate(q + off, qrot + off, qscale);
-    const float sigma = dscale[0];
     const bf16x8 o1 = pkd::load_bf16x8(out + off + 8 * c), o2 = pkd::load_bf16x8(out + off + D / 2 + 8 * c);
     const bf16x8 g1 = pkd::load_bf16x8(dout + off + 8 * c), g2 = pkd::load_bf16x8(dout + off + D / 2 + 8 * c);
     pkd::store_f16x8(dout16 + off + 8 * c, pkd::bf16x8_to_f16x8(g1, sigma));
@@ -283,31 +318,6 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
     if (c == 0) {
         dsum[(int64_t)h * T + t] = -part * sigma;   // stored negated: the dP products start from it
         lse2[(int64_t)h * T + t] = -lse[(int64_t)h * T + t] * pkd::kLog2e;
-    }
-}
-
-// One workgroup: sigma = 2^e with max|dout| * sigma in [1, 2) (sigma = 1 when the maximum is 0
-// or not finite); writes {sigma, 1/sigma}.
-__global__ __launch_bounds__(256) void k_bwd_scale(const float *__restrict__ blockmax, int nb,
-                                                   float *__restrict__ scale) {
-    __shared__ float s_max[4];
-    float m = 0.f;
-    for (int i = threadIdx.x; i < nb; i += 256) m = fmaxf(m, blockmax[i]);
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-        int ex = 0;
-        float sigma = 1.f;
-        if (m > 0.f && m <= 3.0e38f) {
-            (void)frexpf(m, &ex);           // m = f * 2^ex, f in [0.5, 1)
-            ex = min(max(1 - ex, -100), 100);
-            sigma = ldexpf(1.f, ex);
-        }
-        scale[0] = sigma;
-        scale[1] = 1.f / sigma;
     }
 }
 
@@ -350,18 +360,18 @@ hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, cons
                                               r.rope_base, (float2 *)rope);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_bwd_scale<<<1, 256, 0, s>>>(blockmax, (int)nb, scale);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (r.d == 128) {
         k_bwd_rows<128><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
                                             (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
-                                            (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
-                                            (f16 *)vh, (f16 *)dout16, dsum, lse2, qscale);
+                                            (const bf16 *)dout, lse, blockmax, (int)nb, scale,
+                                            (f16 *)qrot, (f16 *)krot, (f16 *)vh, (f16 *)dout16,
+                                            dsum, lse2, qscale);
     } else {
         k_bwd_rows<64><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
                                            (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
-                                           (const bf16 *)dout, lse, scale, (f16 *)qrot, (f16 *)krot,
-                                           (f16 *)vh, (f16 *)dout16, dsum, lse2, qscale);
+                                           (const bf16 *)dout, lse, blockmax, (int)nb, scale,
+                                           (f16 *)qrot, (f16 *)krot, (f16 *)vh, (f16 *)dout16,
+                                           dsum, lse2, qscale);
     }
     return hipGetLastError();
 }
