@@ -110,7 +110,49 @@ def _lora_scale_dropped(x, w, a, b, scale=1.0):
     """Mistake: the adapter scale ignored."""
     return _orig_lora(x, w, a, b, 1.0)
 
+_orig_probs = O._sequence_probs
+
+
+def _probs_unscaled(qr, kr, scale):
+    """Mistake: the softmax scale never applied to the scores."""
+    return _orig_probs(qr, kr, 1.0)
+
+
+def _probs_scale_squared(qr, kr, scale):
+    """Mistake: 1/d where 1/sqrt(d) is meant (the scale applied twice)."""
+    return _orig_probs(qr, kr, scale * scale)
+
+
+def _meta_cu_inclusive(lengths, total_tokens, tile_rows=O.TILE_ROWS):
+    """Mistake: cu_seqlens as an inclusive scan (no leading zero, the total repeated)."""
+    m = _orig_build(lengths, total_tokens, tile_rows)
+    cu = m["cu_seqlens"]
+    if cu.shape[0] > 1:
+        m["cu_seqlens"] = np.concatenate([cu[1:], cu[-1:]])
+    return m
+
+
+def _meta_max_is_sum(lengths, total_tokens, tile_rows=O.TILE_ROWS):
+    """Mistake: max_seqlen taken as the total token count."""
+    m = _orig_build(lengths, total_tokens, tile_rows)
+    m["max_seqlen"] = int(np.sum(np.asarray(lengths, np.int64)))
+    return m
+
+
+def _work_lists_ties_reversed(cu, seq_id, t, r=O.TILE_ROWS):
+    """Mistake: equal-cost items ordered by descending tile index (not a stable order)."""
+    f, b = _orig_work_lists(cu, seq_id, t, r)
+    def reorder(x):
+        return x[sorted(range(x.shape[0]), key=lambda i: (-x[i, 6], -x[i, 7]))]
+    return reorder(f), reorder(b)
+
+
 MUTATIONS = {
+    "softmax_scale_missing": ("_sequence_probs", _probs_unscaled),
+    "softmax_scale_squared": ("_sequence_probs", _probs_scale_squared),
+    "cu_seqlens_inclusive": ("build_meta", _meta_cu_inclusive),
+    "max_seqlen_is_total": ("build_meta", _meta_max_is_sum),
+    "worklist_ties_reversed": ("work_lists", _work_lists_ties_reversed),
     "gqa_interleaved_groups": ("kv_head_of", lambda h, g: h % g),
     "mask_excludes_diagonal": ("causal_keep", lambda n: np.tril(np.ones((n, n), bool), -1)),
     "mask_not_causal": ("causal_keep", lambda n: np.ones((n, n), bool)),
