@@ -301,6 +301,9 @@ class ReloadPipeline:
     def fetch(self, slot: int, dst, src) -> None:
         if not dst.is_cuda or src.is_cuda or not dst.is_contiguous() or not src.is_contiguous():
             raise ValueError("dst must be a contiguous CUDA tensor and src a contiguous host tensor")
+        if not src.is_pinned():
+            raise ValueError("src must be in pinned host memory (torch.empty(..., pin_memory=True)), "
+                             "or the copy cannot overlap the compute")
         n = dst.numel() * dst.element_size()
         if src.numel() * src.element_size() != n:
             raise ValueError("size mismatch")
