@@ -418,3 +418,47 @@ def test_dense_mask_flat_path_near_max():
         start = int(ref["cu_seqlens"][ref["seq_id"][r]])
         assert row[start:r + 1].all() and not row[:start].any() and not row[r + 1:].any(), r
     assert int(mask.sum(dtype=torch.int64).item()) == O.unmasked_pairs(lengths)
+
+
+def test_kernel_timing_from_two_host_threads():
+    """Launches recorded from two host threads at once (each on its own stream) are all counted,
+    and the recorded times are positive."""
+    import threading
+    lengths = [37, 100, 5, 114]
+    t = sum(lengths)
+    meta = pk.build_meta(torch.tensor(lengths, dtype=torch.int32, device="cuda"), t)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    q = torch.randn(t, 2, 64, device="cuda", generator=g).bfloat16()
+    k = torch.randn(t, 1, 64, device="cuda", generator=g).bfloat16()
+    v = torch.randn(t, 1, 64, device="cuda", generator=g).bfloat16()
+    torch.cuda.synchronize()
+    n_calls = 25
+    errors = []
+
+    def worker():
+        try:
+            s = torch.cuda.Stream()
+            ws = pk.fwd_workspace(meta, 2, 1, 64)
+            out = torch.empty_like(q)
+            lse = torch.empty((2, t), dtype=torch.float32, device="cuda")
+            for _ in range(n_calls):
+                pk.attn_fwd(meta, q, k, v, out=out, lse=lse, workspace=ws, stream=s)
+            s.synchronize()
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(e)
+
+    pk.prof_enable(True, ["fwd"])
+    pk.prof_reset()
+    try:
+        threads = [threading.Thread(target=worker) for _ in range(2)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        ms, n = pk.prof_query("fwd")
+    finally:
+        pk.prof_enable(False)
+        pk.prof_reset()
+    say("timed fwd launches", n, "total ms", ms)
+    assert not errors, errors
+    assert n == 2 * n_calls and ms > 0.0
