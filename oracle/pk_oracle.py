@@ -29,11 +29,11 @@ Readings where the pages are silent (each one is listed with its reason in the d
 Pins: every function here is checked by tests that do not reuse its code (complex-number RoPE,
 dense masked attention, torch's own scaled_dot_product_attention and autograd in float64,
 central finite differences, closed forms for length-1 sequences, brute-force coverage of the
-work lists).  Nothing here is "parity unpinned".
+work lists, a pair-by-pair count of the dense keep pattern for unmasked_pairs, printed kept-pair
+totals of the seeded packs).  No function here is left "parity unpinned".
 """
 from __future__ import annotations
 
-import math
 from typing import Dict, Iterable, Optional, Sequence
 
 import numpy as np
@@ -310,18 +310,9 @@ def sequence_probs(q, k, lengths, scale: float, base: float, seq: int, h: int) -
 
 
 # ----------------------------------------------------------------------------------------------
-# Algorithmic work, used by the benchmark's units
+# Kept pairs of the mask (the expected total of the materialised keep pattern)
 # ----------------------------------------------------------------------------------------------
 def unmasked_pairs(lengths) -> int:
-    """Number of (query, key) pairs the mask keeps: sum over sequences of n(n+1)/2."""
+    """Number of (query, key) pairs the mask keeps: a sequence of n tokens keeps, for its query at
+    position p, the p + 1 keys at positions 0..p, so it contributes n(n+1)/2."""
     return int(sum(int(n) * (int(n) + 1) // 2 for n in lengths))
-
-
-def attn_flops(lengths, hq: int, head_dim: int):
-    """(forward, backward) algorithmic FLOPs: 2 and 5 contractions over the kept pairs."""
-    p = unmasked_pairs(lengths)
-    return 4 * hq * head_dim * p, 10 * hq * head_dim * p
-
-
-def softmax_scale(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)

@@ -22,8 +22,6 @@ ARCH = "gfx950"
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "--offload-arch=" + ARCH,
-    # device float atomics as the hardware add (dq accumulation), not a CAS loop
-    "-munsafe-fp-atomics",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

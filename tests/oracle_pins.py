@@ -308,6 +308,34 @@ def pin_dense_mask():
                 assert keep[i, j] == (owner[i] == owner[j] and j <= i)
 
 
+def pin_unmasked_pairs():
+    """Kept-pair totals: a pair-by-pair count over random packs (same sequence, key not after the
+    query); a token walk over the seeded packs (a token at position p keeps p + 1 keys); and the
+    seed-0 totals of the five seeded packs as recorded when their generator was fixed."""
+    rng = np.random.default_rng(13)
+    for _ in range(25):
+        lens = rng.integers(1, 25, size=int(rng.integers(1, 9)))
+        owner = []
+        for s, n in enumerate(lens):
+            owner += [s] * int(n)
+        count = 0
+        for i in range(len(owner)):
+            for j in range(len(owner)):
+                count += int(owner[i] == owner[j] and j <= i)
+        assert O.unmasked_pairs(lens) == count
+    assert O.unmasked_pairs([]) == 0 and O.unmasked_pairs([1]) == 1 and O.unmasked_pairs([1] * 7) == 7
+    recorded = {"tiny": 12323, "llama1b": 278607, "qwen06b": 1983322, "qwen14b": 19425559,
+                "skewed": 134432516}
+    for name, total in recorded.items():
+        lens = synth.pack_lengths(name)
+        walk = 0
+        for n in lens:
+            for p in range(int(n)):
+                walk += p + 1
+        assert walk == total, name
+        assert O.unmasked_pairs(lens) == total, name
+
+
 # --------------------------------------------------------------------------- MoE grouping
 def pin_moe_golden():
     """A hand-derived grouping with an expert that receives nothing."""
@@ -398,6 +426,6 @@ ALL_PINS = [
     pin_meta_golden, pin_meta_bruteforce, pin_worklist_coverage, pin_rope,
     pin_fwd_dense_equals_per_sequence, pin_fwd_rows_and_closed_forms, pin_fwd_lse_reconstruction,
     pin_torch_sdpa_and_autograd, pin_bwd_finite_differences, pin_bwd_invariants,
-    pin_permutation_invariance, pin_dense_mask, pin_moe_golden, pin_moe_bruteforce,
+    pin_permutation_invariance, pin_dense_mask, pin_unmasked_pairs, pin_moe_golden, pin_moe_bruteforce,
     pin_moe_sort_and_bincount, pin_lora_scalar_loops, pin_lora_unmerged_and_zero_scale,
 ]

@@ -189,15 +189,18 @@ def test_moe_group_repeatable():
 @pytest.mark.parametrize("double", [False, True])
 def test_reload_pipeline_matches_resident(double):
     """Backward of several layers whose q, k, v, out, lse come back from pinned host memory
-    through the two-slot pipeline: bit-identical to the backward on resident tensors (the
-    kernels are deterministic), so no layer ever read a slot before its copy landed or after the
-    next copy overwrote it."""
+    through the two-slot pipeline ([UN-2026] §2 "用双缓冲检查点重载隐藏延迟"):
+      * when a slot is acquired, its bytes equal the pinned sources of its layer (checked by a
+        bitwise comparison enqueued on the compute stream right after the acquire, so it sees
+        exactly what the backward reads, with no host synchronisation in between);
+      * every layer's gradients are bit-identical to the backward on resident tensors;
+      * the first and the last reloaded layer match the float64 oracle at the parity gate."""
     w = synth.WORKLOADS["llama1b"]
     lengths = synth.pack_lengths("llama1b")
     t, n_layers = w.total_tokens, 6
     say("reload pipeline, double =", double)
     meta = _meta(lengths)
-    acts, douts, ref = [], [], []
+    acts, douts, ref, host = [], [], [], []
     for l in range(n_layers):
         q, k, v, do = (dev(a) for a in synth.layer_tensors(w, l))
         out, lse = pk.attn_fwd(meta, q, k, v)
@@ -205,9 +208,14 @@ def test_reload_pipeline_matches_resident(double):
         douts.append(do)
         ref.append(pk.attn_bwd(meta, q, k, v, out, lse, do))
     torch.cuda.synchronize()
+    # device copies of the pinned sources, for the acquire-time comparison (bit patterns)
+    bits = lambda x: x.view(torch.int16) if x.element_size() == 2 else x.view(torch.int32)
+    srcs = [[bits(a.to("cuda")) for a in layer] for layer in acts]
+    torch.cuda.synchronize()
     slots = [[torch.empty_like(a, device="cuda") for a in acts[0]] for _ in range(2)]
     pipe = pk.ReloadPipeline()
     got = [None] * n_layers
+    same = [None] * n_layers
     order = list(reversed(range(n_layers)))
 
     def fetch(slot, l):
@@ -223,14 +231,24 @@ def test_reload_pipeline_matches_resident(double):
         elif i + 1 < n_layers:
             fetch(1 - s, order[i + 1])
         pipe.acquire(s)
+        same[l] = torch.stack([torch.eq(bits(x), y).all() for x, y in zip(slots[s], srcs[l])])
         q, k, v, out, lse = slots[s]
         got[l] = pk.attn_bwd(meta, q, k, v, out, lse, douts[l])
         pipe.release(s)
     torch.cuda.synchronize()
     pipe.close()
     for l in range(n_layers):
+        assert bool(same[l].all().item()), "layer %d: slot bytes differ from the pinned sources %s" % (
+            l, same[l].tolist())
         for a, b in zip(got[l], ref[l]):
             assert torch.equal(a, b), "layer %d" % l
+    for l in (order[0], order[-1]):
+        q, k, v, do = synth.layer_tensors(w, l)
+        dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lengths, w.softmax_scale, w.rope_base)
+        say("  reloaded layer", l, "vs oracle")
+        compare("dq", to_np(got[l][0]), dq_ref)
+        compare("dk", to_np(got[l][1]), dk_ref)
+        compare("dv", to_np(got[l][2]), dv_ref)
 
 
 # ------------------------------------------------------------------- measured roofline aids

@@ -170,6 +170,7 @@ MUTATIONS = {
     "dK_transposed_operand": ("key_grad", lambda ds, qr, scale: scale * (ds @ qr)),
     "worklist_short_range": ("work_lists", _cost_off_by_one),
     "dense_mask_strict": ("dense_mask", _mask_strict),
+    "kept_pairs_strict": ("unmasked_pairs", lambda lengths: int(sum(int(n) * (int(n) - 1) // 2 for n in lengths))),
     "moe_slot_major": (MO, "group_by_expert", _group_slot_major),
     "moe_inclusive_offsets": (MO, "group_by_expert", _group_inclusive_offsets),
     "moe_unstable_order": (MO, "group_by_expert", _group_descending),
