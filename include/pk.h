@@ -9,14 +9,14 @@
  *             per-layer device-to-host synchronisation is allowed on the path.
  *             §3 (MoE routing): group once with a stable sort + counts instead of one dynamic
  *             query per group -- the pattern the work-list build follows, and pk_moe_group.
+ *             §2 "用双缓冲检查点重载隐藏延迟": two device buffers so that copying activations back
+ *             from pinned host memory overlaps the backward -- pk_reload_*.
  *   [UN-2023] "Introducing Unsloth：LLM 训练提速 30 倍" (dbyun.net/tutorial/10038),
  *             "手动 Autograd": A(X) = softmax(Q K^T / sqrt(d) + M) V;
  *             "OpenAI Triton kernels": rotate-half RoPE on the two halves of the head dim.
  *   [N1N-2026] "利用 Unsloth 和 NVIDIA 硬件加速 LLM 训练：技术深度解析" (explore.n1n.ai),
  *             §2 "FlashAttention-2 的深度集成": tiles kept on chip, softmax fused with the
  *             products, no N x N matrix stored.
- *             §2 (checkpoint reload): two device buffers so that copying activations back from
- *             pinned host memory overlaps the backward -- pk_reload_*.
  *   [MV] "UnSloth极速微调：底层CUDA优化带来的变革" (maplevalley.com.cn), RoPE paragraph:
  *             positions' rotation factors served from a precomputed table.
  *
@@ -61,6 +61,22 @@ typedef enum pk_status {
 /* Device-side status word bits, set by pk_build_meta for data only the device can see. */
 #define PK_META_BAD_LENGTH 1      /* some length < 1 */
 #define PK_META_BAD_TOTAL 2       /* the lengths do not sum to total_tokens */
+/* Operand-range flag, kept in a word of its own next to the status word: cleared by
+ * pk_build_meta, set (atomically, so concurrent calls may share the meta) by an attention call
+ * that meets an input its fp16 matrix operands cannot hold; the results of that call are then not
+ * meaningful.  Attention calls keep running on a meta with this flag set (it is not a pack error);
+ * pk_meta_check reports it together with the status bits.  The matrix-core operands are fp16
+ * with fp32 accumulation; the bounds that hold for every fp16 operand are:
+ *   forward:  |q|, |k| <= 65504 / sqrt(2) (a rotated element is at most sqrt(2) max|x|),
+ *             |v| <= 65504; P <= 256 (the online softmax's reference maximum moves when a score
+ *             exceeds it by 8 in the exp2 domain);
+ *   backward: dout and v enter scaled by powers of two sigma, tau with max|sigma dout| and
+ *             max|tau v| in [1, 2), so |sigma dout| < 2, |tau v| < 2, P <= 1 and
+ *             |sigma tau dS| < 8 d for any finite dout and v (dS = P (dout.v - D), where
+ *             |dout_i . v_j| and |D_i| are both at most |dout_i|_1 max|v|); the remaining inputs
+ *             need |R(q)| * softmax_scale * log2(e) <= 65504 and |R(k)| <= 65504.
+ * Inputs outside these bounds, or not finite, set the flag. */
+#define PK_META_FP16_RANGE 4
 
 /* Opaque handle: a small host object that points into the caller's meta buffer.  It is
  * immutable after pk_build_meta returns, so several streams may read it concurrently. */
@@ -105,8 +121,9 @@ pk_status pk_build_meta(const int32_t *lengths_dev, int32_t n_seqs, int64_t tota
 /* Fill *view (host) with the device pointers and sizes of a meta. */
 pk_status pk_meta_view(pk_meta_t meta, pk_meta_view_t *view /* host */);
 
-/* DEBUGGING AID, SYNCHRONISES `hip_stream`: copy the status word and max_seqlen to the host.
- * Returns PK_ERR_DEVICE when the status word is non-zero.  Either output pointer may be NULL. */
+/* DEBUGGING AID, SYNCHRONISES `hip_stream`: copy the status word (OR-ed with the operand-range
+ * flag PK_META_FP16_RANGE) and max_seqlen to the host.  Returns PK_ERR_DEVICE when that word is
+ * non-zero.  Either output pointer may be NULL. */
 pk_status pk_meta_check(pk_meta_t meta, void *hip_stream, int32_t *status_host,
                         int32_t *max_seqlen_host);
 

@@ -204,10 +204,15 @@ def attn_fwd(q, k, v, lengths, scale: float, base: float,
     return out, lse
 
 
-def score_grad(p: np.ndarray, do: np.ndarray, v: np.ndarray) -> np.ndarray:
+def score_grad(p: np.ndarray, do: np.ndarray, v: np.ndarray, o: Optional[np.ndarray] = None) -> np.ndarray:
     """dS for one sequence and head: with O = P V and D_i = sum_d dO_i * O_i,
-    dP = dO V^T and dS = P * (dP - D) (the softmax Jacobian applied to dP)."""
-    o = p @ v
+    dP = dO V^T and dS = P * (dP - D) (the softmax Jacobian applied to dP).  When `o` is given,
+    D is formed from it instead of from P V: the backward receives the forward's output as an
+    input and forms D from what it receives (the FlashAttention-2 form of the backward that
+    "利用 Unsloth 和 NVIDIA 硬件加速 LLM 训练" §2 names), so a test can hand the oracle the same
+    rounded output the fast path is given."""
+    if o is None:
+        o = p @ v
     dcap = np.sum(do * o, axis=1)
     dp = do @ v.T
     return p * (dp - dcap[:, None])
@@ -224,11 +229,13 @@ def key_grad(ds: np.ndarray, qr: np.ndarray, scale: float) -> np.ndarray:
 
 
 def attn_bwd(q, k, v, dout, lengths, scale: float, base: float,
-             seqs: Optional[Iterable[int]] = None, kv_heads: Optional[Iterable[int]] = None):
+             seqs: Optional[Iterable[int]] = None, kv_heads: Optional[Iterable[int]] = None,
+             out=None):
     """dQ [T, Hq, d], dK, dV [T, Hkv, d] in float64 for L = sum(O * dout).
 
     With `seqs`/`kv_heads`, only those sequences and KV heads (and the query heads of their
-    groups) are computed; other entries stay NaN."""
+    groups) are computed; other entries stay NaN.  With `out` [T, Hq, d], D = rowsum(dout * out)
+    is formed from that tensor (see score_grad); by default from the exact O."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -253,7 +260,7 @@ def attn_bwd(q, k, v, dout, lengths, scale: float, base: float,
                 continue
             p, _ = _sequence_probs(qr[a:b, h], kr[a:b, g], scale)
             do = dout[a:b, h]
-            ds = score_grad(p, do, v[a:b, g])
+            ds = score_grad(p, do, v[a:b, g], None if out is None else np.asarray(out, np.float64)[a:b, h])
             dv[a:b, g] += p.T @ do
             dqr[a:b, h] = query_grad(ds, kr[a:b, g], scale)
             dkr[a:b, g] += key_grad(ds, qr[a:b, h], scale)

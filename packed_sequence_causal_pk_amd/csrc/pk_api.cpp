@@ -135,8 +135,8 @@ BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d) {
     w.rope = off; off += align256((size_t)T * (d / 2) * 8);
     w.dsum = off; off += align256((size_t)T * hq * 4);
     w.lse2 = off; off += align256((size_t)T * hq * 4);
-    w.blockmax = off; off += align256((size_t)dmax_blocks(T, hq, d) * 4);
-    w.scale = off; off += align256(2 * 4);
+    w.blockmax = off; off += align256((size_t)(dmax_blocks(T, hq, d) + vmax_blocks(T, hkv, d)) * 4);
+    w.scale = off; off += align256(4 * 4);
     w.total = off;
     return w;
 }
@@ -216,13 +216,14 @@ pk_status pk_meta_check(pk_meta_t meta, void *hip_stream, int32_t *status_host,
                         int32_t *max_seqlen_host) {
     if (!meta) return PK_ERR_INVALID;
     if (!on_meta_device(meta)) return PK_ERR_INVALID;
-    int32_t hdr[2] = {0, 0};
+    int32_t hdr[3] = {0, 0, 0};
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     if (hipMemcpyAsync(hdr, meta->hdr, sizeof(hdr), hipMemcpyDeviceToHost, s) != hipSuccess) return PK_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return PK_ERR_HIP;
-    if (status_host) *status_host = hdr[0];
+    const int32_t status = hdr[0] | hdr[2];   // build status bits | operand-range flags
+    if (status_host) *status_host = status;
     if (max_seqlen_host) *max_seqlen_host = hdr[1];
-    return hdr[0] ? PK_ERR_DEVICE : PK_OK;
+    return status ? PK_ERR_DEVICE : PK_OK;
 }
 
 pk_status pk_meta_destroy(pk_meta_t meta) {
@@ -259,7 +260,7 @@ pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *
     hipError_t e;
     {
         ProfScope ps(PK_K_FWD_PREP, s);
-        e = pk::launch_fwd_prep(ra, k, v, w + W.krot, w + W.vh, w + W.rope, s);
+        e = pk::launch_fwd_prep(ra, k, v, w + W.krot, w + W.vh, w + W.rope, meta->hdr + 2, s);
     }
     if (e != hipSuccess) return PK_ERR_HIP;
     pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
@@ -291,7 +292,7 @@ pk_status pk_attn_bwd_prep(pk_meta_t meta, const void *q, const void *k, const v
         ra, q, k, v, out, dout, lse, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, w + W.rope,
         reinterpret_cast<float *>(w + W.dsum), reinterpret_cast<float *>(w + W.lse2),
         reinterpret_cast<float *>(w + W.blockmax), reinterpret_cast<float *>(w + W.scale),
-        softmax_scale * 1.4426950408889634f, s));
+        softmax_scale * 1.4426950408889634f, meta->hdr + 2, s));
 }
 
 pk_status pk_attn_bwd_main(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d,

@@ -28,9 +28,10 @@
 //
 // Common to both: the mask is applied element-wise only on tiles that straddle a sequence
 // boundary or the diagonal, and tiles outside a wave's visible range skip their products;
-// operands are fp16 with fp32 accumulation; dout enters scaled by the power of two sigma the
-// prologue chose (max|dout| * sigma in [1, 2)), so dP and dS are sigma-scaled and the results
-// are unscaled exactly by 1/sigma when written.  Q_rot is stored times scale * log2(e) (one fp16
+// operands are fp16 with fp32 accumulation; dout and v enter scaled by the powers of two sigma
+// and tau the prologue chose (max|dout| * sigma and max|v| * tau in [1, 2)), so dP and dS are
+// scaled by sigma tau (|sigma tau dS| < 8 d, inside fp16 for any finite input), dV by sigma, and
+// the results are unscaled exactly when written.  Q_rot is stored times scale * log2(e) (one fp16
 // rounding of the scaled value, as precise as rounding Q_rot itself), and the score and dP
 // products start from the per-row values -lse * log2(e) and -sigma D, so they end as the
 // exponent of P and as sigma (dP - D) with no further arithmetic.
@@ -49,11 +50,11 @@ using namespace pkd;
 struct BwdArgs {
     const f16 *qrot;      // [T, hq, D] fp16, R(q) * scale * log2(e)
     const f16 *krot;      // [T, hkv, D] fp16
-    const f16 *v;         // [T, hkv, D] fp16 copy of v
+    const f16 *v;         // [T, hkv, D] tau * v, fp16
     const f16 *dout16;    // [T, hq, D] sigma * dout, fp16
     const float *lse2;    // [hq, T] -lse * log2(e)
-    const float *dsum;    // [hq, T] -sigma * rowsum(dout * out)
-    const float *dscale;  // {sigma, 1/sigma}
+    const float *dsum;    // [hq, T] -sigma * tau * rowsum(dout * out)
+    const float *dscale;  // {sigma, 1/sigma, tau, 1/(sigma tau)}
     const float2 *rope;   // [T, D/2]
     const int32_t *items; // [n_items, 8] longest first (backward list for _kv, forward for _q)
     const int32_t *pos;   // [T]

@@ -124,7 +124,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
     if (key_base >= kv_end) return;              // (NS = 2) an item of 64 keys or fewer
     // Query blocks start at the first key of the workgroup: earlier rows see none of its keys.
     const int q_start = NS == 1 ? it[2] : it[2] + 64 * kh;
-    const float inv_sigma = a.dscale[1];
+    const float inv_sigma = a.dscale[1];        // dV unscale
+    const float inv_sigma_tau = a.dscale[3];    // dK unscale (dS carries sigma * tau)
 
     const int j = key_base + 32 * sub + n32;  // this lane's key
     const bool kvalid = j < kv_end;
@@ -394,8 +395,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
             for (int rr = 0; rr < 16; ++rr) acc[db][rr] += red[((slot * NDB + db) * 16 + rr) * 64 + lane];
     }
 
-    // epilogue: P waves write dV; dS waves write dK = R(-theta) (scale * dK_rot); both
-    // unscaled by 1/sigma
+    // epilogue: P waves write dV (unscaled by 1/sigma); dS waves write
+    // dK = R(-theta) (scale * dK_rot) (unscaled by 1/(sigma tau))
     if (kvalid) {
         const int64_t rowoff = ((int64_t)j * a.hkv + kvh) * D;
         if (p_role) {
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
             float *dkrow = a.dk + rowoff;
             const float2 *cs = a.rope + (int64_t)j * (D / 2);
             // Q_rot carries scale * log2(e), so scale * dK_rot = ln(2) * acc
-            const float kscale = kLn2 * inv_sigma;
+            const float kscale = kLn2 * inv_sigma_tau;
 #pragma unroll
             for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll

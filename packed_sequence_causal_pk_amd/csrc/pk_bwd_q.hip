@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     }
     const int q_start = it[0], q_end = it[1], kv_start = it[2];
     const int64_t T = a.T;
-    const float inv_sigma = a.dscale[1];
+    const float inv_sigma_tau = a.dscale[3];   // dS carries sigma * tau
 
     // this lane's query and its wave's query range
     const int i = q_start + 32 * w + n32;
@@ -189,11 +189,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
         if (k0 - BK >= kb_lo) step(std::integral_constant<int, 1>(), k0 - BK);
     }
 
-    // epilogue: dQ = R(-theta) (scale / sigma * dQ_rot), written once
+    // epilogue: dQ = R(-theta) (scale / (sigma tau) * dQ_rot), written once
     if (qvalid) {
         float *row = a.dq + ((int64_t)i * a.hq + h) * D;
         const float2 *cs = a.rope + (int64_t)i * (D / 2);
-        const float qscale = a.scale * inv_sigma;
+        const float qscale = a.scale * inv_sigma_tau;
 #pragma unroll
         for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll

@@ -47,6 +47,7 @@ struct FwdArgs {
     const int32_t *items; // [n_items, 8] longest first
     const int32_t *pos;   // [T]
     const int32_t *hdr;   // status, max_seqlen
+    int32_t *flags;       // the meta's operand-range word
     bf16 *out;            // [T, hq, D]
     float *lse;           // [hq, T]
     int64_t T;
@@ -104,9 +105,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     const int wlo_max = __builtin_amdgcn_readfirstlane(wave_active ? wq_last - a.pos[wq_last] : 0);
 
     // Q fragments (k operand of S^T = K Q^T), rotated in registers.  Chunk kk holds
-    // d in [16kk + 8hb, +8); chunk kk + NKK/2 holds the RoPE partners d + D/2.
+    // d in [16kk + 8hb, +8); chunk kk + NKK/2 holds the RoPE partners d + D/2.  A rotated value
+    // beyond fp16's range (|q| above 65504 / sqrt(2) can give one) sets the range flag.
     f16x8 qf[NKK];
     {
+        float qmax = 0.f;
         const bf16 *qrow = a.q + ((int64_t)(qvalid ? i : q_start) * a.hq + h) * D;
         const float2 *cs = a.rope + (int64_t)(qvalid ? i : q_start) * (D / 2);
 #pragma unroll
@@ -119,12 +122,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
             for (int s = 0; s < 8; ++s) {
                 const float2 f = cs[d0 + s];
                 const float a1 = (float)x1[s], a2 = (float)x2[s];
-                y1[s] = (f16)(qvalid ? a1 * f.x - a2 * f.y : 0.f);
-                y2[s] = (f16)(qvalid ? a2 * f.x + a1 * f.y : 0.f);
+                const float b1 = qvalid ? a1 * f.x - a2 * f.y : 0.f, b2 = qvalid ? a2 * f.x + a1 * f.y : 0.f;
+                qmax = fmaxf(qmax, fmaxf(fabsf(b1), fabsf(b2)));
+                y1[s] = (f16)b1;
+                y2[s] = (f16)b2;
             }
             qf[kk] = y1;
             qf[kk + NKK / 2] = y2;
         }
+        if (__builtin_expect(!(qmax <= 65504.f), 0)) atomicOr(a.flags, PK_META_FP16_RANGE);
     }
 
     float mref = -INFINITY;  // reference max of this query's scaled scores (log2 domain)
@@ -318,6 +324,7 @@ hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, co
     a.items = m.fwd_items;
     a.pos = m.pos;
     a.hdr = m.hdr;
+    a.flags = m.hdr + 2;
     a.out = (bf16 *)out;
     a.lse = lse;
     a.T = sh.T;

@@ -9,7 +9,7 @@
 // The host object behind pk_meta_t: pointers into the caller's meta buffer plus the sizes the
 // host already knows (so no launch ever needs a device read to size its grid).
 struct pk_meta_s {
-    int32_t *hdr;        // [0] = status bits, [1] = max_seqlen
+    int32_t *hdr;        // [0] = status bits, [1] = max_seqlen, [2] = operand-range flags
     int32_t *cu;         // [n_seqs + 1]
     int32_t *seq_id;     // [T]
     int32_t *pos;        // [T]
@@ -52,16 +52,20 @@ struct RopeArgs {
     int hq, hkv, d;
     float rope_base;
 };
+// `flags` (the meta's range word) receives PK_META_FP16_RANGE when an operand the kernels round
+// to fp16 lies outside its range.
 hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, const void *v, void *krot, void *vh,
-                           void *rope, hipStream_t s);
+                           void *rope, int32_t *flags, hipStream_t s);
 // Blocks of the per-token prologue/epilogue kernels (one thread per token and 4 rotation pairs).
 unsigned prep_blocks(int64_t T, int d);
-// Blocks of the max|dout| reduction (at most 1024).
+// Blocks of the max|dout| (at most 1024) and max|v| (at most 256) reductions.
 unsigned dmax_blocks(int64_t T, int hq, int d);
+unsigned vmax_blocks(int64_t T, int hkv, int d);
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *v,
                            const void *out, const void *dout, const float *lse, void *qrot,
                            void *krot, void *vh, void *dout16, void *rope, float *dsum,
-                           float *lse2, float *blockmax, float *scale, float qscale, hipStream_t s);
+                           float *lse2, float *blockmax, float *scale, float qscale,
+                           int32_t *flags, hipStream_t s);
 
 struct AttnShape {
     int64_t T;
@@ -70,8 +74,9 @@ struct AttnShape {
 };
 hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, const void *krot,
                       const void *v, const void *rope, void *out, float *lse, hipStream_t s);
-// qrot = R(q) * softmax_scale * log2(e) (fp16), dout16 = sigma * dout (fp16),
-// dsum = -sigma * rowsum(dout * out), lse2 = -lse * log2(e).
+// qrot = R(q) * softmax_scale * log2(e) (fp16), v16 = tau * v (fp16), dout16 = sigma * dout (fp16),
+// dsum = -sigma * tau * rowsum(dout * out), lse2 = -lse * log2(e),
+// scale = {sigma, 1/sigma, tau, 1/(sigma tau)}.
 // launch_bwd_kv writes dk and dv, launch_bwd_q writes dq.
 hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                          const void *krot, const void *v, const void *dout16, const float *lse2,

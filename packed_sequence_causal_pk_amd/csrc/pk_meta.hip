@@ -81,6 +81,8 @@ __global__ __launch_bounds__(kScanThreads) void k_meta_scan(const int32_t *__res
         if (total != T) status |= PK_META_BAD_TOTAL;
         hdr[0] = status;
         hdr[1] = gmax;
+        hdr[2] = 0;   // operand-range flags, set later by attention calls that see one
+        hdr[3] = 0;
     }
 }
 
@@ -181,7 +183,7 @@ MetaLayout meta_layout(int32_t n_seqs, int64_t T) {
     MetaLayout L;
     const size_t items = (size_t)n_tiles(T) * PK_ITEM_FIELDS * sizeof(int32_t);
     size_t off = 0;
-    L.hdr = off; off += align256(2 * sizeof(int32_t));
+    L.hdr = off; off += align256(4 * sizeof(int32_t));
     L.cu = off; off += align256((size_t)(n_seqs + 1) * sizeof(int32_t));
     L.seq_id = off; off += align256((size_t)T * sizeof(int32_t));
     L.pos = off; off += align256((size_t)T * sizeof(int32_t));

@@ -13,13 +13,16 @@
 //
 // Rotated q and k, v, and the scaled dout are written as fp16, the matrix-core operand format of
 // the attention kernels, so those can copy tiles straight into LDS.  The backward prologue first
-// reduces max|dout| per block (k_bwd_pre, whose other blocks write the (cos, sin) table).
-// k_bwd_rows then turns the maxima into a power of two sigma with max|dout| * sigma in [1, 2)
-// (each of its workgroups that holds query rows reduces the maxima itself, which costs less
-// than a launch of its own), so the backward's fp16 gradient operands (dout and dS, both scaled
-// by sigma, unscaled exactly at the end) stay inside fp16's range whatever the magnitude of the
-// incoming gradient, and writes the rotated Q (times scale * log2(e)) and K, V and
-// sigma * dout in fp16, -sigma * rowsum(dout * out) and -lse * log2(e).
+// reduces max|dout| and max|v| per block (k_bwd_pre, whose other blocks write the (cos, sin)
+// table).  k_bwd_rows then turns the maxima into powers of two sigma and tau with
+// max|dout| * sigma and max|v| * tau in [1, 2) (each workgroup reduces the maxima itself, which
+// costs less than a launch of its own), so the backward's fp16 operands (sigma dout, tau v, and
+// dS scaled by sigma tau, all unscaled exactly at the end) stay inside fp16's range whatever the
+// magnitude of the incoming gradient and of v (the bound is derived at k_bwd_rows), and writes
+// the rotated Q (times scale * log2(e)) and K, tau V and sigma * dout in fp16,
+// -sigma * tau * rowsum(dout * out) and -lse * log2(e).  Values the prologues round to fp16
+// without a scale (rotated q and k; v in the forward) are range-checked against 65504: one out of
+// range sets PK_META_FP16_RANGE in the meta's range word.
 //
 // The table: inverse frequencies base^(-2i/d) in double precision (once per workgroup, in LDS),
 // each angle p * f in double, reduced modulo 2 pi in double, and its cosine and sine taken in
@@ -68,6 +71,19 @@ __device__ __forceinline__ void rope_factors(const int32_t *__restrict__ pos, in
     }
 }
 
+// Largest magnitude an fp16 operand may take: the kernels round these values to fp16, which
+// overflows past it.  A value above it (or not finite) sets PK_META_FP16_RANGE in the meta's
+// range word; the results of that call are then not meaningful.
+constexpr float kF16Max = 65504.f;
+
+__device__ __forceinline__ void flag_range(bool bad, int32_t *flags) {
+    if (__builtin_expect(bad, 0)) atomicOr(flags, PK_META_FP16_RANGE);
+}
+
+__device__ __forceinline__ float amax4(const float x[4]) {
+    return fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+}
+
 __device__ __forceinline__ void load4(const bf16 *p, float x[4]) {
     const uint2 raw = *reinterpret_cast<const uint2 *>(p);
     const bf16 *b = reinterpret_cast<const bf16 *>(&raw);
@@ -82,20 +98,22 @@ __device__ __forceinline__ void store4(f16 *p, const float x[4]) {
     *reinterpret_cast<uint2 *>(p) = raw;
 }
 
-// Copy 4 + 4 elements of one head row as fp16 (no rotation).
+// Copy 4 + 4 elements of one head row as fp16 (no rotation); returns their largest magnitude.
 template <int D>
-__device__ __forceinline__ void convert_row(const bf16 *__restrict__ src, f16 *__restrict__ dst, int c) {
+__device__ __forceinline__ float convert_row(const bf16 *__restrict__ src, f16 *__restrict__ dst, int c) {
     float x1[4], x2[4];
     load4(src + 4 * c, x1);
     load4(src + D / 2 + 4 * c, x2);
     store4(dst + 4 * c, x1);
     store4(dst + D / 2 + 4 * c, x2);
+    return fmaxf(amax4(x1), amax4(x2));
 }
 
-// Rotate 4 pairs of one head row: row points at the head's element 0.
+// Rotate 4 pairs of one head row (row points at the head's element 0); returns the largest
+// magnitude of the rotated values.
 template <int D>
-__device__ __forceinline__ void rotate_row(const bf16 *__restrict__ src, f16 *__restrict__ dst,
-                                           int c, const float cs[4], const float sn[4]) {
+__device__ __forceinline__ float rotate_row(const bf16 *__restrict__ src, f16 *__restrict__ dst,
+                                            int c, const float cs[4], const float sn[4]) {
     float x1[4], x2[4], y1[4], y2[4];
     load4(src + 4 * c, x1);
     load4(src + D / 2 + 4 * c, x2);
@@ -106,6 +124,7 @@ __device__ __forceinline__ void rotate_row(const bf16 *__restrict__ src, f16 *__
     }
     store4(dst + 4 * c, y1);
     store4(dst + D / 2 + 4 * c, y2);
+    return fmaxf(amax4(y1), amax4(y2));
 }
 
 // One thread per (token t, KV head h, group c of 4 rotation pairs), c fastest so that a wave's
@@ -117,7 +136,8 @@ __global__ __launch_bounds__(256) void k_fwd_prep(const int32_t *__restrict__ po
                                                   const bf16 *__restrict__ v,
                                                   f16 *__restrict__ krot,
                                                   f16 *__restrict__ vh,
-                                                  float2 *__restrict__ table) {
+                                                  float2 *__restrict__ table,
+                                                  int32_t *__restrict__ flags) {
     constexpr int G = D / 8;
     __shared__ double s_inv[D / 2];
     rope_inv_freq<D>(base, s_inv);
@@ -130,12 +150,13 @@ __global__ __launch_bounds__(256) void k_fwd_prep(const int32_t *__restrict__ po
     float cs[4], sn[4];
     rope_factors<D>(pos, t, c, s_inv, table, h == 0, cs, sn);
     const int64_t off = (t * hkv + h) * D;
-    rotate_row<D>(k + off, krot + off, c, cs, sn);
-    convert_row<D>(v + off, vh + off, c);
+    const float m = fmaxf(rotate_row<D>(k + off, krot + off, c, cs, sn), convert_row<D>(v + off, vh + off, c));
+    flag_range(!(m <= kF16Max), flags);
 }
 
-// max|dout| per block over the flattened [T * hq * d] tensor, 8 elements per thread step.
-__device__ __forceinline__ void bwd_dmax_block(const bf16 *__restrict__ dout, int64_t n8,
+// max|x| per block over a flattened bf16 tensor of n8 groups of 8 elements (dout, v), 8 elements
+// per thread step; block b of nb.
+__device__ __forceinline__ void bwd_amax_block(const bf16 *__restrict__ dout, int64_t n8,
                                                float *__restrict__ blockmax, int b, int nb) {
     __shared__ float s_max[4];
     float amax = 0.f;
@@ -183,18 +204,23 @@ __device__ __forceinline__ void rope_table_block(const int32_t *__restrict__ pos
     rope_factors<D>(pos, t, (int)(gid % G), s_inv, table, true, cs, sn);
 }
 
-// First launch of the backward prologue, two independent jobs in one grid (one launch fewer,
-// which small packs feel): blocks [0, nb) reduce max|dout| per block, the rest write the RoPE
-// table (one thread per token and group of 4 rotation pairs).
+// First launch of the backward prologue, three independent jobs in one grid (fewer launches,
+// which small packs feel): blocks [0, nb) reduce max|dout| per block, blocks [nb, nb + nbv)
+// max|v| per block (into blockmax[nb ..]), the rest write the RoPE table (one thread per token
+// and group of 4 rotation pairs).
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_pre(const bf16 *__restrict__ dout, int64_t n8,
-                                                 float *__restrict__ blockmax, int nb,
+                                                 const bf16 *__restrict__ v, int64_t n8v,
+                                                 float *__restrict__ blockmax, int nb, int nbv,
                                                  const int32_t *__restrict__ pos, int64_t T,
                                                  float base, float2 *__restrict__ table) {
-    if ((int)blockIdx.x < nb)
-        bwd_dmax_block(dout, n8, blockmax, (int)blockIdx.x, nb);
+    const int b = (int)blockIdx.x;
+    if (b < nb)
+        bwd_amax_block(dout, n8, blockmax, b, nb);
+    else if (b < nb + nbv)
+        bwd_amax_block(v, n8v, blockmax + nb, b - nb, nbv);
     else
-        rope_table_block<D>(pos, T, base, table, (int)blockIdx.x - nb);
+        rope_table_block<D>(pos, T, base, table, b - nb - nbv);
 }
 
 // Rotation factors of pairs [8c, 8c + 8) of token t from the table.
@@ -212,12 +238,14 @@ __device__ __forceinline__ void table8(const float2 *__restrict__ table, int64_t
     }
 }
 
-// The dout scale, computed by every workgroup that needs it from the per-block maxima (at most
-// 1024 floats, an L2-resident read): sigma = 2^e with max|dout| * sigma in [1, 2) (sigma = 1
-// when the maximum is 0 or not finite).  Every thread of the workgroup must call it; all get
-// the same sigma.
-__device__ __forceinline__ float block_sigma(const float *__restrict__ blockmax, int nb) {
+// A power-of-two scale computed by every workgroup that needs it from per-block maxima (at most
+// 1024 floats, an L2-resident read): 2^e with max * 2^e in [1, 2) (1 when the maximum is 0; 1
+// and a range flag when it is not finite).  Used for sigma (from max|dout|) and tau (from
+// max|v|).  Every thread of the workgroup must call it; all get the same value.
+__device__ __forceinline__ float block_pow2_scale(const float *__restrict__ blockmax, int nb,
+                                                  int32_t *__restrict__ flags) {
     __shared__ float s_max[4];
+    __syncthreads();   // s_max may still be read by a previous call
     float m = 0.f;
     for (int i = threadIdx.x; i < nb; i += 256) m = fmaxf(m, blockmax[i]);
 #pragma unroll
@@ -225,23 +253,33 @@ __device__ __forceinline__ float block_sigma(const float *__restrict__ blockmax,
     if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-    float sigma = 1.f;
+    float scale = 1.f;
     if (m > 0.f && m <= 3.0e38f) {
         int ex = 0;
         (void)frexpf(m, &ex);           // m = f * 2^ex, f in [0.5, 1)
         ex = min(max(1 - ex, -100), 100);
-        sigma = ldexpf(1.f, ex);
+        scale = ldexpf(1.f, ex);
     }
-    return sigma;
+    if (threadIdx.x == 0) flag_range(!(m <= 3.0e38f), flags);
+    return scale;
 }
 
 // Per-row work of the backward prologue, one thread per (row, group c of 8 rotation pairs): the
 // thread owns elements [8c, 8c + 8) of a head row and their partners + D/2, read and written as
-// 16-byte vectors.  Rows [0, T * hkv) are K rows (rotated) with their V rows (converted); rows
-// [T * hkv, T * (hkv + hq)) are query-head rows: Q rotated and multiplied by qscale (the softmax
-// scale times log2(e), so that the backward's score products come out in the exp2 domain),
-// sigma * dout, and the row values -sigma * sum(dout * out) and -lse * log2(e), stored negated
-// because the backward's products start from them.
+// 16-byte vectors.  Rows [0, T * hkv) are K rows (rotated) with their V rows (converted, times
+// tau); rows [T * hkv, T * (hkv + hq)) are query-head rows: Q rotated and multiplied by qscale
+// (the softmax scale times log2(e), so that the backward's score products come out in the exp2
+// domain), sigma * dout, and the row values -sigma * tau * sum(dout * out) and -lse * log2(e),
+// stored negated because the backward's products start from them.
+//
+// sigma and tau are powers of two from the maxima k_bwd_pre reduced: max|sigma dout| and
+// max|tau v| lie in [1, 2).  With them every fp16 operand of the backward has a bound that holds
+// for any finite dout and v:  |sigma dout| < 2, |tau v| < 2, P <= 1, and
+//     |sigma tau dS_ij| = P_ij |sigma tau (dout_i . v_j - D_i)| < 2 d * 2 + 2 d * 2 = 8 d
+// (|dout_i . v_j| <= |dout_i|_1 max|v|, and |D_i| <= |dout_i|_1 max|out_i| <= |dout_i|_1 max|v|
+// because out_i is a convex combination of v rows), i.e. < 1024 for d = 128.  The remaining
+// inputs are range-checked here: |R(q)| * qscale and |R(k)| above 65504 (or not finite) set the
+// range flag.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
                                                   const float2 *__restrict__ table,
@@ -251,50 +289,60 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
                                                   const bf16 *__restrict__ out,
                                                   const bf16 *__restrict__ dout,
                                                   const float *__restrict__ lse,
-                                                  const float *__restrict__ blockmax, int nb,
+                                                  const float *__restrict__ blockmax, int nb, int nbv,
                                                   float *__restrict__ dscale,
                                                   f16 *__restrict__ qrot,
                                                   f16 *__restrict__ krot,
                                                   f16 *__restrict__ vh,
                                                   f16 *__restrict__ dout16,
                                                   float *__restrict__ dsum,
-                                                  float *__restrict__ lse2, float qscale) {
+                                                  float *__restrict__ lse2, float qscale,
+                                                  int32_t *__restrict__ flags) {
     constexpr int G = D / 16;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int c = (int)(gid % G);
     int64_t row = gid / G;
     const int64_t nkv = T * hkv;
-    // sigma, in the workgroups that hold query rows (a workgroup-uniform test); the first of
-    // them also stores {sigma, 1/sigma} for the attention kernels
+    // tau in every workgroup (its V rows or its dsum rows need it); sigma in the workgroups that
+    // hold query rows (a workgroup-uniform test); the first of them also stores
+    // {sigma, 1/sigma, tau, 1/(sigma tau)} for the attention kernels
+    const float tau = block_pow2_scale(blockmax + nb, nbv, flags);
     float sigma = 1.f;
     const int64_t first_q_block = nkv * G / 256;
     if ((int64_t)blockIdx.x >= first_q_block) {
-        sigma = block_sigma(blockmax, nb);
+        sigma = block_pow2_scale(blockmax, nb, flags);
         if ((int64_t)blockIdx.x == first_q_block && threadIdx.x == 0) {
             dscale[0] = sigma;
             dscale[1] = 1.f / sigma;
+            dscale[2] = tau;
+            dscale[3] = 1.f / (sigma * tau);
         }
     }
     float cs[8], sn[8];
+    // rotate 8 pairs, scale, store as fp16; returns the largest magnitude stored
     auto rotate = [&](const bf16 *src, f16 *dst, float mult) {
         const bf16x8 x1 = pkd::load_bf16x8(src + 8 * c), x2 = pkd::load_bf16x8(src + D / 2 + 8 * c);
         f16x8 y1, y2;
+        float m = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float a1 = (float)x1[e], a2 = (float)x2[e];
-            y1[e] = (f16)((a1 * cs[e] - a2 * sn[e]) * mult);
-            y2[e] = (f16)((a2 * cs[e] + a1 * sn[e]) * mult);
+            const float b1 = (a1 * cs[e] - a2 * sn[e]) * mult, b2 = (a2 * cs[e] + a1 * sn[e]) * mult;
+            m = fmaxf(m, fmaxf(fabsf(b1), fabsf(b2)));
+            y1[e] = (f16)b1;
+            y2[e] = (f16)b2;
         }
         pkd::store_f16x8(dst + 8 * c, y1);
         pkd::store_f16x8(dst + D / 2 + 8 * c, y2);
+        return m;
     };
     if (row < nkv) {
         table8<D>(table, row / hkv, c, cs, sn);
         const int64_t off = row * D;
-        rotate(k + off, krot + off, 1.0f);
-        pkd::store_f16x8(vh + off + 8 * c, pkd::bf16x8_to_f16x8(pkd::load_bf16x8(v + off + 8 * c)));
+        flag_range(!(rotate(k + off, krot + off, 1.0f) <= kF16Max), flags);
+        pkd::store_f16x8(vh + off + 8 * c, pkd::bf16x8_to_f16x8(pkd::load_bf16x8(v + off + 8 * c), tau));
         pkd::store_f16x8(vh + off + D / 2 + 8 * c,
-                         pkd::bf16x8_to_f16x8(pkd::load_bf16x8(v + off + D / 2 + 8 * c)));
+                         pkd::bf16x8_to_f16x8(pkd::load_bf16x8(v + off + D / 2 + 8 * c), tau));
         return;
     }
     row -= nkv;
@@ -305,7 +353,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
     const int h = (int)(row % hq);
     table8<D>(table, t, c, cs, sn);
     const int64_t off = row * D;
-    rotate(q + off, qrot + off, qscale);
+    flag_range(!(rotate(q + off, qrot + off, qscale) <= kF16Max), flags);
     const bf16x8 o1 = pkd::load_bf16x8(out + off + 8 * c), o2 = pkd::load_bf16x8(out + off + D / 2 + 8 * c);
     const bf16x8 g1 = pkd::load_bf16x8(dout + off + 8 * c), g2 = pkd::load_bf16x8(dout + off + D / 2 + 8 * c);
     pkd::store_f16x8(dout16 + off + 8 * c, pkd::bf16x8_to_f16x8(g1, sigma));
@@ -316,7 +364,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(int64_t T, int hq, int hkv,
 #pragma unroll
     for (int sh = G / 2; sh > 0; sh >>= 1) part += __shfl_xor(part, sh, 64);
     if (c == 0) {
-        dsum[(int64_t)h * T + t] = -part * sigma;   // stored negated: the dP products start from it
+        // stored negated: the dP products start from it
+        dsum[(int64_t)h * T + t] = -part * (sigma * tau);
         lse2[(int64_t)h * T + t] = -lse[(int64_t)h * T + t] * pkd::kLog2e;
     }
 }
@@ -332,46 +381,56 @@ unsigned dmax_blocks(int64_t T, int hq, int d) {
     return (unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, (n8 + 255) / 256));
 }
 
+unsigned vmax_blocks(int64_t T, int hkv, int d) {
+    const int64_t n8 = T * hkv * d / 8;
+    return (unsigned)std::max<int64_t>(1, std::min<int64_t>(256, (n8 + 1023) / 1024));
+}
+
 hipError_t launch_fwd_prep(const RopeArgs &r, const void *k, const void *v, void *krot, void *vh,
-                           void *rope, hipStream_t s) {
+                           void *rope, int32_t *flags, hipStream_t s) {
     const unsigned g = (unsigned)((r.T * r.hkv * (r.d / 8) + 255) / 256);
     if (r.d == 128)
         k_fwd_prep<128><<<g, 256, 0, s>>>(r.pos, r.T, r.hkv, r.rope_base, (const bf16 *)k,
-                                           (const bf16 *)v, (f16 *)krot, (f16 *)vh, (float2 *)rope);
+                                           (const bf16 *)v, (f16 *)krot, (f16 *)vh, (float2 *)rope,
+                                           flags);
     else
         k_fwd_prep<64><<<g, 256, 0, s>>>(r.pos, r.T, r.hkv, r.rope_base, (const bf16 *)k,
-                                          (const bf16 *)v, (f16 *)krot, (f16 *)vh, (float2 *)rope);
+                                          (const bf16 *)v, (f16 *)krot, (f16 *)vh, (float2 *)rope,
+                                          flags);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, const void *v,
                            const void *out, const void *dout, const float *lse, void *qrot,
                            void *krot, void *vh, void *dout16, void *rope, float *dsum,
-                           float *lse2, float *blockmax, float *scale, float qscale, hipStream_t s) {
-    const int64_t n8 = r.T * r.hq * r.d / 8;
-    const unsigned nb = dmax_blocks(r.T, r.hq, r.d);
+                           float *lse2, float *blockmax, float *scale, float qscale,
+                           int32_t *flags, hipStream_t s) {
+    const int64_t n8 = r.T * r.hq * r.d / 8, n8v = r.T * r.hkv * r.d / 8;
+    const unsigned nb = dmax_blocks(r.T, r.hq, r.d), nbv = vmax_blocks(r.T, r.hkv, r.d);
     const unsigned gt = prep_blocks(r.T, r.d);
     const unsigned gr = (unsigned)((r.T * (r.hq + r.hkv) * (r.d / 16) + 255) / 256);
     if (r.d == 128)
-        k_bwd_pre<128><<<nb + gt, 256, 0, s>>>((const bf16 *)dout, n8, blockmax, (int)nb, r.pos, r.T,
-                                               r.rope_base, (float2 *)rope);
+        k_bwd_pre<128><<<nb + nbv + gt, 256, 0, s>>>((const bf16 *)dout, n8, (const bf16 *)v, n8v,
+                                                     blockmax, (int)nb, (int)nbv, r.pos, r.T,
+                                                     r.rope_base, (float2 *)rope);
     else
-        k_bwd_pre<64><<<nb + gt, 256, 0, s>>>((const bf16 *)dout, n8, blockmax, (int)nb, r.pos, r.T,
-                                              r.rope_base, (float2 *)rope);
+        k_bwd_pre<64><<<nb + nbv + gt, 256, 0, s>>>((const bf16 *)dout, n8, (const bf16 *)v, n8v,
+                                                    blockmax, (int)nb, (int)nbv, r.pos, r.T,
+                                                    r.rope_base, (float2 *)rope);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (r.d == 128) {
         k_bwd_rows<128><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
                                             (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
-                                            (const bf16 *)dout, lse, blockmax, (int)nb, scale,
-                                            (f16 *)qrot, (f16 *)krot, (f16 *)vh, (f16 *)dout16,
-                                            dsum, lse2, qscale);
+                                            (const bf16 *)dout, lse, blockmax, (int)nb, (int)nbv,
+                                            scale, (f16 *)qrot, (f16 *)krot, (f16 *)vh,
+                                            (f16 *)dout16, dsum, lse2, qscale, flags);
     } else {
         k_bwd_rows<64><<<gr, 256, 0, s>>>(r.T, r.hq, r.hkv, (const float2 *)rope, (const bf16 *)q,
                                            (const bf16 *)k, (const bf16 *)v, (const bf16 *)out,
-                                           (const bf16 *)dout, lse, blockmax, (int)nb, scale,
-                                           (f16 *)qrot, (f16 *)krot, (f16 *)vh, (f16 *)dout16,
-                                           dsum, lse2, qscale);
+                                           (const bf16 *)dout, lse, blockmax, (int)nb, (int)nbv,
+                                           scale, (f16 *)qrot, (f16 *)krot, (f16 *)vh,
+                                           (f16 *)dout16, dsum, lse2, qscale, flags);
     }
     return hipGetLastError();
 }

@@ -272,6 +272,45 @@ def pin_bwd_invariants():
                 assert np.allclose(dv[a, g], do[a, 3 * g:3 * g + 3].astype(float).sum(axis=0), atol=1e-12)
 
 
+def pin_bwd_given_output():
+    """D formed from a given forward output: handed the exact O it changes nothing; handed
+    another tensor X, dV is unchanged and each query's dQ_rot moves by the closed form
+    -scale * (dout_i . (X_i - O_i)) * sum_j P_ij k_rot_j, because D enters dS = P (dP - D) as
+    a per-row shift (checked on a length-1 sequence, where P = 1 and dQ_rot = scale *
+    dout . (v - X) k_rot, and on every row of a longer pack)."""
+    lens, q, k, v, do = _problem(31, [5, 1, 9], hq=4, hkv=2, d=8)
+    sc = 0.4
+    o, _ = O.attn_fwd(q, k, v, lens, sc, 1e4)
+    base = O.attn_bwd(q, k, v, do, lens, sc, 1e4)
+    same = O.attn_bwd(q, k, v, do, lens, sc, 1e4, out=o)
+    for a, b in zip(base, same):
+        assert np.allclose(a, b, rtol=0, atol=1e-12)
+    x = o + np.random.default_rng(5).standard_normal(o.shape) * 0.1
+    dq2, dk2, dv2 = O.attn_bwd(q, k, v, do, lens, sc, 1e4, out=x)
+    assert np.allclose(dv2, base[2], rtol=0, atol=1e-12)
+    pos = np.concatenate([np.arange(n) for n in lens])
+    th = O.rope_angles(pos, 8, 1e4)
+    c_, s_ = np.cos(th), np.sin(th)
+    kr = np.concatenate([k[..., :4] * c_[:, None] - k[..., 4:] * s_[:, None],
+                         k[..., 4:] * c_[:, None] + k[..., :4] * s_[:, None]], -1)
+    rot = lambda y: np.concatenate([y[..., :4] * c_[:, None] - y[..., 4:] * s_[:, None],
+                                    y[..., 4:] * c_[:, None] + y[..., :4] * s_[:, None]], -1)
+    dqr_base, dqr2 = rot(base[0]), rot(dq2)
+    cu = [0, 5, 6, 15]
+    for s_i in range(3):
+        a, b = cu[s_i], cu[s_i + 1]
+        for h in range(4):
+            g = h // 2
+            p = O.sequence_probs(q, k, lens, sc, 1e4, s_i, h)
+            shift = -sc * np.sum(do[a:b, h] * (x[a:b, h] - o[a:b, h]), axis=1)[:, None] * (p @ kr[a:b, g])
+            assert np.allclose(dqr2[a:b, h], dqr_base[a:b, h] + shift, rtol=0, atol=1e-10)
+    # length-1 sequence (token 5): dQ_rot = scale * (dout . (v - X)) k_rot
+    for h in range(4):
+        g = h // 2
+        want = sc * float(np.dot(do[5, h], v[5, g] - x[5, h])) * kr[5, g]
+        assert np.allclose(dqr2[5, h], want, rtol=0, atol=1e-10)
+
+
 def pin_permutation_invariance():
     """Reordering the sequences of a pack reorders the outputs and changes nothing else."""
     lens, q, k, v, do = _problem(51, [4, 10, 1, 7], 2, 1, 16)
@@ -426,6 +465,6 @@ ALL_PINS = [
     pin_meta_golden, pin_meta_bruteforce, pin_worklist_coverage, pin_rope,
     pin_fwd_dense_equals_per_sequence, pin_fwd_rows_and_closed_forms, pin_fwd_lse_reconstruction,
     pin_torch_sdpa_and_autograd, pin_bwd_finite_differences, pin_bwd_invariants,
-    pin_permutation_invariance, pin_dense_mask, pin_unmasked_pairs, pin_moe_golden, pin_moe_bruteforce,
+    pin_bwd_given_output, pin_permutation_invariance, pin_dense_mask, pin_unmasked_pairs, pin_moe_golden, pin_moe_bruteforce,
     pin_moe_sort_and_bincount, pin_lora_scalar_loops, pin_lora_unmerged_and_zero_scale,
 ]

@@ -13,7 +13,7 @@ import torch
 import packed_sequence_causal_pk_amd as pk
 from oracle import pk_oracle as O
 from packed_sequence_causal_pk_amd import synth
-from tests.gpu_helpers import LSE_MAX_ABS, compare, dev, meta_to_np, run_pk, say, to_np
+from tests.gpu_helpers import LSE_MAX_ABS, MAX_ABS, compare, dev, meta_to_np, run_pk, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -195,6 +195,109 @@ def test_gradient_scale_invariance(log2_scale):
     compare("dq", to_np(res["dq"]) / f, dq_ref)
     compare("dk", to_np(res["dk"]) / f, dk_ref)
     compare("dv", to_np(res["dv"]) / f, dv_ref)
+
+
+def _bf16(x):
+    """Round float32 values to bfloat16 (nearest even), kept as float32 (exact bf16 values)."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).bfloat16().float().numpy()
+
+
+def _magnitude_gate(name, got, ref, max_abs=MAX_ABS):
+    """The parity gate applied relative to the tensor's magnitude: the absolute max-abs bound
+    was set for tensors of unit spread (scores and lse of order 1), so here it is scaled by
+    max(1, max|ref| / 4); the relative-L2 bound is unchanged."""
+    s = max(1.0, float(np.nanmax(np.abs(ref))) / 4.0)
+    compare(name, np.asarray(got) / s, np.asarray(ref) / s, max_abs=max_abs)
+
+
+def test_outlier_channels():
+    """q and k with a few channels 4x larger and v with a few channels 512x larger (values to
+    about 1600), the way trained projections concentrate magnitude in a few channels: results
+    match the oracle (gate relative to each tensor's magnitude) and no range flag is raised.
+    v's magnitude costs nothing (the backward scales v and dS by powers of two); the precision
+    limit is the scores' magnitude, which fp16 operands resolve to about 2^-11 of their size
+    (measured: q/k channels 8x larger put the backward at up to 7e-2 of this gate)."""
+    lens, q, k, v, do = synth.small_problem(900, [300, 1, 170, 45, 512], 4, 2, 128)
+    qk_ch, v_ch = [3, 64 + 3, 17, 100], [5, 70, 90, 127]
+    q, k, v = q.copy(), k.copy(), v.copy()
+    q[..., qk_ch] *= 4.0
+    k[..., qk_ch] *= 4.0
+    v[..., v_ch] *= 512.0
+    say("outlier channels: max|q| %.1f max|k| %.1f max|v| %.1f" % (np.abs(q).max(), np.abs(k).max(), np.abs(v).max()))
+    scale = 1.0 / math.sqrt(128)
+    res = run_pk(lens, q, k, v, do, scale)
+    status, _ = res["meta"].check()
+    assert status == 0, status
+    o_ref, lse_ref = O.attn_fwd(q, k, v, lens, scale, 1e4)
+    # the backward forms D = rowsum(dout * out) from the bf16 out it is handed; on outlier
+    # channels near 1600 that rounding alone (2^-9 relative) moves dq by up to 1.4e-2 of the
+    # scaled gate, so the backward is compared with the oracle handed the same out
+    dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, scale, 1e4, out=to_np(res["out"]))
+    _magnitude_gate("out", to_np(res["out"]), o_ref)
+    _magnitude_gate("lse", to_np(res["lse"]), lse_ref, max_abs=LSE_MAX_ABS)
+    _magnitude_gate("dq", to_np(res["dq"]), dq_ref)
+    _magnitude_gate("dk", to_np(res["dk"]), dk_ref)
+    _magnitude_gate("dv", to_np(res["dv"]), dv_ref)
+
+
+@pytest.mark.parametrize("log2_v", [14, 40])
+def test_backward_large_v(log2_v):
+    """The backward with v multiplied by 2^e, past fp16's range (2^14 takes max|v| to about
+    7e4, 2^40 to about 5e12): its fp16 copy of v and its dS are scaled by the power of two tau,
+    so dQ and dK come out multiplied by 2^e and dV unchanged, with no range flag.  The forward
+    outputs for the large v are formed exactly from a forward on the original v (O is linear in
+    v and 2^e is exact in bf16; lse does not depend on v)."""
+    lens, q, k, v, do = synth.small_problem(910, [400, 3, 250], 4, 2, 128)
+    f = 2.0 ** log2_v
+    scale = 1.0 / math.sqrt(128)
+    meta = pk.build_meta(torch.tensor(lens, device="cuda"), int(lens.sum()))
+    tq, tk, tv, tdo = dev(q), dev(k), dev(v), dev(do)
+    out, lse = pk.attn_fwd(meta, tq, tk, tv, scale)
+    big_v, big_out = tv * f, out * f
+    say("v x 2^%d: max|v| %.3g" % (log2_v, float(big_v.float().abs().max())))
+    dq, dk, dv = pk.attn_bwd(meta, tq, tk, big_v, big_out, lse, tdo, scale)
+    torch.cuda.synchronize()
+    status, _ = meta.check()
+    assert status == 0, status
+    dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, scale, 1e4)
+    compare("dq", to_np(dq) / f, dq_ref)
+    compare("dk", to_np(dk) / f, dk_ref)
+    compare("dv", to_np(dv), dv_ref)
+
+
+def test_range_flag():
+    """Inputs the fp16 operands cannot hold set PK_META_FP16_RANGE in the meta's range word,
+    which pk_meta_check reports; the flag does not stop later calls, and a rebuild clears it."""
+    lens, q, k, v, do = synth.small_problem(920, [100, 50], 2, 1, 64)
+    lens_d = torch.tensor(lens, device="cuda")
+    t = int(lens.sum())
+    cases = []
+    for what, idx, val in (("v", (10, 0, 5), 1.0e5), ("k", (0, 0, 3), 7.0e4), ("q", (100, 1, 7), 7.0e4)):
+        qq, kk, vv = q.copy(), k.copy(), v.copy()
+        {"q": qq, "k": kk, "v": vv}[what][idx] = val   # token 0 and 100 start sequences: position 0
+        cases.append((what, qq, kk, vv))
+    for what, qq, kk, vv in cases:
+        meta = pk.build_meta(lens_d, t)
+        assert meta.check()[0] == 0
+        say("range flag from", what)
+        pk.attn_fwd(meta, dev(qq), dev(kk), dev(vv))
+        torch.cuda.synchronize()
+        assert meta.check()[0] == 4, what   # PK_META_FP16_RANGE
+        out, lse = pk.attn_fwd(meta, dev(q), dev(k), dev(v))   # still runs on a flagged meta
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all().item()
+        assert pk.build_meta(lens_d, t).check()[0] == 0
+    # the backward flags a rotated q that exceeds the range once scaled: softmax scale 4 puts
+    # |q| * scale * log2(e) past 65504 for |q| = 2e4 while the forward's unscaled copy holds it
+    qq = q.copy()
+    qq[0, 0, 2] = 2.0e4
+    meta = pk.build_meta(lens_d, t)
+    out, lse = pk.attn_fwd(meta, dev(qq), dev(k), dev(v), 4.0)
+    torch.cuda.synchronize()
+    assert meta.check()[0] == 0
+    pk.attn_bwd(meta, dev(qq), dev(k), dev(v), out, lse, dev(do), 4.0)
+    torch.cuda.synchronize()
+    assert meta.check()[0] == 4
 
 
 def _sub_pack(lengths, seqs):

@@ -139,6 +139,9 @@ def _meta_max_is_sum(lengths, total_tokens, tile_rows=O.TILE_ROWS):
     return m
 
 
+_orig_score_grad = O.score_grad
+
+
 def _work_lists_ties_reversed(cu, seq_id, t, r=O.TILE_ROWS):
     """Mistake: equal-cost items ordered by descending tile index (not a stable order)."""
     f, b = _orig_work_lists(cu, seq_id, t, r)
@@ -164,8 +167,9 @@ MUTATIONS = {
     "rope_backward_not_transposed": ("rope_apply", lambda x, pos, base, inverse=False: _orig_rope(x, pos, base)),
     "positions_not_reset": ("build_meta", _global_positions),
     "lse_without_max": ("_softmax_rows", lambda s: (_orig_softmax(s)[0], np.log(np.exp(s - s.max(1)[:, None]).sum(1)))),
-    "dS_dropped_D": ("score_grad", lambda p, do, v: p * (do @ v.T)),
-    "dS_sign": ("score_grad", lambda p, do, v: p * (np.sum(do * (p @ v), 1)[:, None] - do @ v.T)),
+    "dS_dropped_D": ("score_grad", lambda p, do, v, o=None: p * (do @ v.T)),
+    "dS_sign": ("score_grad", lambda p, do, v, o=None: p * (np.sum(do * (p @ v), 1)[:, None] - do @ v.T)),
+    "dS_given_output_ignored": ("score_grad", lambda p, do, v, o=None: _orig_score_grad(p, do, v)),
     "dQ_missing_scale": ("query_grad", lambda ds, kr, scale: ds @ kr),
     "dK_transposed_operand": ("key_grad", lambda ds, qr, scale: scale * (ds @ qr)),
     "worklist_short_range": ("work_lists", _cost_off_by_one),
