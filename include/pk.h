@@ -144,6 +144,25 @@ pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *
                       int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float rope_base,
                       void *out, float *lse, void *ws, size_t ws_bytes, void *hip_stream);
 
+/* Largest workspace pk_attn_fwd_noalloc can use: 128 MiB, i.e. T * hkv * d * 4 + T * d * 4 bytes
+ * (plus 256-byte alignment of each part) up to this size -- e.g. T = 16384 tokens with 8 KV heads
+ * of d = 128 (76 MiB), or T = 32768 with 4 KV heads of d = 128 (80 MiB). */
+#define PK_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* pk_attn_fwd for callers that cannot allocate device memory (code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation): the same computation and the
+ * same kernels, with the workspace taken from a fixed array of PK_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device it runs on (from its load until the process ends) instead of from
+ * the caller.  It allocates nothing (no hipMalloc, no allocating library call); the caller still
+ * passes q, k, v, out and lse.  Returns PK_ERR_CAPACITY, enqueueing nothing, when
+ * pk_attn_fwd_workspace_bytes(meta, hq, hkv, d) exceeds PK_NOALLOC_SCRATCH_BYTES.  Every call
+ * on one device shares that device's array and overwrites it before reading it: calls that may
+ * overlap on one device (other streams, other host threads) race and must be ordered by the
+ * caller; the array keeps the last call's contents. */
+pk_status pk_attn_fwd_noalloc(pk_meta_t meta, const void *q, const void *k, const void *v,
+                              int32_t hq, int32_t hkv, int32_t d, float softmax_scale,
+                              float rope_base, void *out, float *lse, void *hip_stream);
+
 /* Workspace bytes pk_attn_bwd needs: the fp16 operands (rotated Q and K, V, scaled dout), the
  * RoPE table, per-row values (rowsum(dout * out), lse) and the dout scale with its per-block
  * maxima. */

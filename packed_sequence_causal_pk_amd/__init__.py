@@ -20,7 +20,7 @@ __all__ = ["PackedMeta", "build_meta", "attn_fwd", "attn_bwd", "fwd_workspace", 
            "PackedCausalAttention", "PkError", "tile_rows", "prof_enable", "prof_reset",
            "prof_query", "dense_mask", "rope_apply", "moe_group", "moe_workspace",
            "ReloadPipeline", "peak_mfma_tflops", "peak_hbm_gbps", "lora_qkv", "lora_workspace",
-           "attn_bwd_prep", "attn_bwd_main"]
+           "attn_bwd_prep", "attn_bwd_main", "attn_fwd_noalloc"]
 
 
 def _torch():
@@ -185,6 +185,27 @@ def attn_fwd(meta: PackedMeta, q, k, v, softmax_scale: Optional[float] = None,
                            float(rope_base), _ptr(out), _ptr(lse), _ptr(ws), _ws_bytes(ws, q.device),
                            _stream_ptr(stream))
     _lib.check("pk_attn_fwd", rc)
+    return out, lse
+
+
+def attn_fwd_noalloc(meta: PackedMeta, q, k, v, out, lse, softmax_scale: Optional[float] = None,
+                     rope_base: float = 10000.0, stream=None):
+    """pk_attn_fwd_noalloc: the forward with the library's fixed per-device workspace, for
+    callers that cannot allocate; out (bf16 [T,hq,d]) and lse (float32 [hq,T]) are the caller's
+    and nothing is allocated here either.  Calls that overlap on one device race."""
+    torch = _torch()
+    t, hq, hkv, d = _dims(q, k)
+    _check_inputs(meta, q, k, v)
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("q, k, v must be bfloat16")
+    if t != meta.total_tokens or k.shape != v.shape or k.shape[0] != t or k.shape[2] != d:
+        raise ValueError("shape mismatch with the pack")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _check_out("out", out, q.shape, torch.bfloat16, q.device)
+    _check_out("lse", lse, (hq, t), torch.float32, q.device)
+    rc = lib().pk_attn_fwd_noalloc(meta.handle, _ptr(q), _ptr(k), _ptr(v), hq, hkv, d, scale,
+                                   float(rope_base), _ptr(out), _ptr(lse), _stream_ptr(stream))
+    _lib.check("pk_attn_fwd_noalloc", rc)
     return out, lse
 
 

@@ -28,6 +28,7 @@ PK_MOE_MAX_EXPERTS = 1024
 PK_MOE_MAX_ASSIGN = 1 << 26
 PK_MOE_BAD_EXPERT = 1
 PK_LORA_MAX_RANK = 64
+PK_NOALLOC_SCRATCH_BYTES = 128 << 20
 PK_PROF_ALL = (1 << len(KERNEL_KINDS)) - 1
 
 # every function pk.h declares, with (restype, argtypes)
@@ -55,6 +56,7 @@ SIGNATURES = {
     "pk_meta_destroy": (_i32, [_vp]),
     "pk_attn_fwd_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
     "pk_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "pk_attn_fwd_noalloc": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp]),
     "pk_attn_bwd_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
     "pk_attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32,
                            _vp, _vp, _vp, _vp, _sz, _vp]),

@@ -11,6 +11,13 @@
 
 #include "pk_internal.h"
 
+// ------------------------------------------------------------------ allocation-free workspace
+// The workspace of pk_attn_fwd_noalloc: a file-scope device array, one copy per device, held
+// from the library's load until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory, so it is never passed anywhere: its device address is looked up
+// once per device (with that device current, scratch_address below) and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[PK_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
@@ -108,6 +115,21 @@ SideStream *side_stream(int dev) {  // caller holds g_side_mu
 bool on_meta_device(const pk_meta_s *m) {
     int dev = -1;
     return hipGetDevice(&dev) == hipSuccess && dev == m->device;
+}
+
+void *g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device `dev` (the current device), or null on a HIP error.
+void *scratch_address(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch[dev] = p;
+    }
+    return g_scratch[dev];
 }
 
 }  // namespace
@@ -242,20 +264,12 @@ size_t pk_attn_bwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int3
     return pk::bwd_workspace(meta->total_tokens, hq, hkv, d).total;
 }
 
-pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *v, int32_t hq,
-                      int32_t hkv, int32_t d, float softmax_scale, float rope_base, void *out,
-                      float *lse, void *ws, size_t ws_bytes, void *hip_stream) {
-    if (!meta) return PK_ERR_INVALID;
-    if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
-    if (!(softmax_scale > 0.f) || !(rope_base > 0.f)) return PK_ERR_INVALID;
+// The forward on a workspace `w` the caller has checked for size and alignment.
+static pk_status attn_fwd_on(pk_meta_t meta, const void *q, const void *k, const void *v, int32_t hq,
+                             int32_t hkv, int32_t d, float softmax_scale, float rope_base, void *out,
+                             float *lse, char *w, hipStream_t s) {
     const int64_t T = meta->total_tokens;
-    if (T == 0) return PK_OK;
-    if (!q || !k || !v || !out || !lse || !ws || !aligned256(ws)) return PK_ERR_INVALID;
     const pk::FwdWorkspace W = pk::fwd_workspace(T, hq, hkv, d);
-    if (ws_bytes < W.total) return PK_ERR_CAPACITY;
-    if (!on_meta_device(meta)) return PK_ERR_INVALID;
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    char *w = static_cast<char *>(ws);
     pk::RopeArgs ra{meta->pos, T, hq, hkv, d, rope_base};
     hipError_t e;
     {
@@ -269,6 +283,38 @@ pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *
         e = pk::launch_fwd(sh, *meta, q, w + W.krot, w + W.vh, w + W.rope, out, lse, s);
     }
     return hip_status(e);
+}
+
+pk_status pk_attn_fwd(pk_meta_t meta, const void *q, const void *k, const void *v, int32_t hq,
+                      int32_t hkv, int32_t d, float softmax_scale, float rope_base, void *out,
+                      float *lse, void *ws, size_t ws_bytes, void *hip_stream) {
+    if (!meta) return PK_ERR_INVALID;
+    if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.f) || !(rope_base > 0.f)) return PK_ERR_INVALID;
+    const int64_t T = meta->total_tokens;
+    if (T == 0) return PK_OK;
+    if (!q || !k || !v || !out || !lse || !ws || !aligned256(ws)) return PK_ERR_INVALID;
+    if (ws_bytes < pk::fwd_workspace(T, hq, hkv, d).total) return PK_ERR_CAPACITY;
+    if (!on_meta_device(meta)) return PK_ERR_INVALID;
+    return attn_fwd_on(meta, q, k, v, hq, hkv, d, softmax_scale, rope_base, out, lse,
+                       static_cast<char *>(ws), static_cast<hipStream_t>(hip_stream));
+}
+
+pk_status pk_attn_fwd_noalloc(pk_meta_t meta, const void *q, const void *k, const void *v,
+                              int32_t hq, int32_t hkv, int32_t d, float softmax_scale,
+                              float rope_base, void *out, float *lse, void *hip_stream) {
+    if (!meta) return PK_ERR_INVALID;
+    if (!shape_supported(hq, hkv, d)) return PK_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.f) || !(rope_base > 0.f)) return PK_ERR_INVALID;
+    const int64_t T = meta->total_tokens;
+    if (T == 0) return PK_OK;
+    if (!q || !k || !v || !out || !lse) return PK_ERR_INVALID;
+    if (pk::fwd_workspace(T, hq, hkv, d).total > (size_t)PK_NOALLOC_SCRATCH_BYTES) return PK_ERR_CAPACITY;
+    if (!on_meta_device(meta)) return PK_ERR_INVALID;
+    char *w = static_cast<char *>(scratch_address(meta->device));
+    if (!w) return PK_ERR_HIP;
+    return attn_fwd_on(meta, q, k, v, hq, hkv, d, softmax_scale, rope_base, out, lse, w,
+                       static_cast<hipStream_t>(hip_stream));
 }
 
 pk_status pk_attn_bwd_prep(pk_meta_t meta, const void *q, const void *k, const void *v,

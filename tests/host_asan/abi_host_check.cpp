@@ -50,6 +50,8 @@ int main() {
     expect((long)pk_attn_bwd_workspace_bytes(nullptr, 2, 1, 64), 0, "bwd ws");
     expect(pk_attn_fwd(nullptr, fake, fake, fake, 2, 1, 64, 0.125f, 1e4f, fake, (float *)fake, fake, 1 << 20,
                        nullptr), PK_ERR_INVALID, "fwd");
+    expect(pk_attn_fwd_noalloc(nullptr, fake, fake, fake, 2, 1, 64, 0.125f, 1e4f, fake, (float *)fake, nullptr),
+           PK_ERR_INVALID, "fwd noalloc");
     expect(pk_attn_bwd(nullptr, fake, fake, fake, fake, (const float *)fake, fake, 2, 1, 64, 0.125f, 1e4f,
                        (float *)fake, (float *)fake, (float *)fake, fake, 1 << 20, nullptr), PK_ERR_INVALID, "bwd");
     expect(pk_attn_bwd_prep(nullptr, fake, fake, fake, fake, (const float *)fake, fake, 2, 1, 64, 0.125f, 1e4f,

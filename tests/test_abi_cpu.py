@@ -59,6 +59,7 @@ def test_host_side_rejections(lib):
     assert h.value is None
     args_fwd = [None, fake, fake, fake, 2, 1, 64, 0.125, 1e4, fake, fake, fake, 1 << 20, None]
     assert lib.pk_attn_fwd(*args_fwd) == _lib.PK_ERR_INVALID
+    assert lib.pk_attn_fwd_noalloc(None, fake, fake, fake, 2, 1, 64, 0.125, 1e4, fake, fake, None) == _lib.PK_ERR_INVALID
     args_bwd = [None, fake, fake, fake, fake, fake, fake, 2, 1, 64, 0.125, 1e4, fake, fake, fake, fake, 1 << 20, None]
     assert lib.pk_attn_bwd(*args_bwd) == _lib.PK_ERR_INVALID
     args_prep = [None, fake, fake, fake, fake, fake, fake, 2, 1, 64, 0.125, 1e4, fake, 1 << 20, None]
