@@ -173,7 +173,8 @@ def min_bytes(w, T):
 KINDS = ("meta", "fwd_prep", "fwd", "bwd_prep", "bwd", "bwd_dq")
 
 
-def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False, graph=False):
+def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False, graph=False,
+            ds_compare=False):
     """Time `steps` steps (after `warmup`) of one workload, timing the kernel kinds
     `timed_kinds` inside that region; a second, shorter pass times every kind for the
     per-kernel breakdown.  Returns the timings and shapes."""
@@ -205,7 +206,9 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
     lengths_d = torch.tensor(lengths, dtype=torch.int32, device=dev)
     meta0 = pk.build_meta(lengths_d, T)
     ws_f = pk.fwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
-    ws_b = pk.bwd_workspace(meta0, w.hq, w.hkv, w.head_dim)
+    # the backward recomputes S and dP for dQ (measured faster than the dS store on this part;
+    # the store, sized from the pack's longest sequence, is timed beside it when ds_compare)
+    ws_b = pk.bwd_workspace(meta0, w.hq, w.hkv, w.head_dim, store=False)
     meta0.close()
     if calibrate_mib > 0:
         nbytes = calibrate_mib << 20
@@ -313,6 +316,35 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
             g.replay()
         graph_ms = timed(steps, (), fn=g.replay)[0]
         del g
+    ds_store = None
+    if ds_compare:
+        # the backward layer loop with the dS store against the recomputing dQ, alternating,
+        # same inputs and process: per-layer kernel times and wall time
+        meta_c = pk.build_meta(lengths_d, T)
+        ws_s = pk.bwd_workspace(meta_c, w.hq, w.hkv, w.head_dim, max_seqlen=int(max(lengths)))
+        for x in layers:
+            pk.attn_fwd(meta_c, x["q"], x["k"], x["v"], w.softmax_scale, w.rope_base,
+                        out=x["out"], lse=x["lse"], workspace=ws_f)
+
+        def bwd_loop(ws):
+            def run():
+                for x in reversed(layers):
+                    pk.attn_bwd(meta_c, x["q"], x["k"], x["v"], x["out"], x["lse"], x["do"],
+                                w.softmax_scale, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws)
+                return meta_c
+            return run
+
+        ds_store = {"store_bytes": int(ws_s.numel()), "plain_bytes": int(ws_b.numel())}
+        res = {"recompute": [], "store": []}
+        for rep in range(2):
+            for key, ws in (("recompute", ws_b), ("store", ws_s)):
+                ms, _, kk = timed(1, ["bwd", "bwd_dq"], fn=bwd_loop(ws))
+                res[key].append((ms / L, kk["bwd"]["avg_us"], kk["bwd_dq"]["avg_us"]))
+        for key, vals in res.items():
+            ds_store[key] = {"bwd_loop_us_per_layer": round(1000.0 * min(v[0] for v in vals), 1),
+                             "dkdv_us": round(min(v[1] for v in vals), 1),
+                             "dq_us": round(min(v[2] for v in vals), 1)}
+        del ws_s, meta_c
     uncached_ms = None
     if uncached:
         uncached_ms = {}
@@ -328,6 +360,7 @@ def measure(name, steps, warmup, calibrate_mib=0, timed_kinds=(), uncached=False
     fwd_flops, bwd_flops = attn_flops(lengths, w.hq, w.head_dim)
     layer_ms = step_ms / L
     return {"w": w, "lengths": lengths, "T": T, "L": L, "steps": nb, "step_ms": step_ms,
+            "ds_store": ds_store,
             "main_kern": main_kern, "uncached_step_ms": uncached_ms, "graph_step_ms": graph_ms,
             "layer_ms": layer_ms, "kern": kern, "fwd_flops": fwd_flops, "bwd_flops": bwd_flops,
             "tflops": (fwd_flops + bwd_flops) * L / (step_ms * 1e-3) / 1e12}
@@ -411,7 +444,7 @@ def measure_reload(name="qwen06b", reps=3):
     dq = torch.empty(T, w.hq, w.head_dim, dtype=torch.float32, device=dev)
     dk = torch.empty(T, w.hkv, w.head_dim, dtype=torch.float32, device=dev)
     dv = torch.empty_like(dk)
-    ws = pk.bwd_workspace(meta, w.hq, w.hkv, w.head_dim)
+    ws = pk.bwd_workspace(meta, w.hq, w.hkv, w.head_dim, max_seqlen=int(max(lengths)))
     pipe = pk.ReloadPipeline()
     layer_bytes = sum(a.numel() * a.element_size() for a in acts[0])
 
@@ -583,7 +616,8 @@ def main():
           file=sys.stderr, flush=True)
     # the dK/dV kernel dominates the step on every pack measured here: its launches are timed
     # inside the timed region for the roofline
-    m = measure(args.workload, args.steps, args.warmup, args.calibrate_copy_mib, timed_kinds=("bwd",))
+    m = measure(args.workload, args.steps, args.warmup, args.calibrate_copy_mib, timed_kinds=("bwd",),
+                ds_compare=not args.no_sweep)
     w, lengths, T, L, kern = m["w"], m["lengths"], m["T"], m["L"], m["kern"]
     s = summary(m)
 
@@ -642,6 +676,12 @@ def main():
             "traffic": measured_traffic(),
         },
     }
+    if m["ds_store"] is not None:
+        result["bwd_ds_store_vs_recompute"] = dict(
+            m["ds_store"], note="the backward layer loop of this workload with the dS store "
+                                "(pk_attn_bwd_workspace_bytes_ds, sized from the longest sequence) "
+                                "and with the recomputing dQ kernel (the step above), alternating in "
+                                "one process; best of 2 passes each")
     if not args.no_sweep:
         # the other packs, a few steps each (their own figures; `value` is the workload above)
         other = {}

@@ -97,6 +97,10 @@ typedef struct pk_meta_view {
     int32_t n_items;              /* ceil(T / PK_TILE_ROWS) */
     int64_t total_tokens;
     int32_t device;               /* HIP device the meta was built on */
+    const int32_t *ds_off;        /* [n_items + 1], tile order: ds_off[u] = sum over key tiles
+                                     u' < u of ceil((q_end - q_start) / PK_DS_BLOCK_ROWS) of their
+                                     backward items (the first block of tile u in the backward's
+                                     dS store); ds_off[n_items] = the total */
 } pk_meta_view_t;
 
 /* Work-list granularity (PK_TILE_ROWS), exported for bindings. */
@@ -168,12 +172,32 @@ pk_status pk_attn_fwd_noalloc(pk_meta_t meta, const void *q, const void *k, cons
  * maxima. */
 size_t pk_attn_bwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d);
 
+/* Query rows per block of the backward's dS store. */
+#define PK_DS_BLOCK_ROWS 64
+
+/* Workspace bytes for pk_attn_bwd with a dS store sized for packs whose sequences are at most
+ * `max_seqlen_bound` tokens long (<= 0: no bound, sized for one sequence of T tokens): the
+ * bytes pk_attn_bwd_workspace_bytes gives, followed by room for
+ *   hq * sum over key tiles u of min(ceil((T - 128 u) / 64), ceil((max_seqlen_bound + 127) / 64))
+ * blocks of 128 x 64 fp16 (16 KiB) -- a tile's backward item spans at most the rest of the last
+ * sequence that starts inside the tile.  (The Qwen3-14B-shaped pack, 16384 tokens, 40 query
+ * heads, longest sequence 3523: 4.6 GiB.)  0 for unsupported arguments. */
+size_t pk_attn_bwd_workspace_bytes_ds(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d,
+                                      int64_t max_seqlen_bound);
+
 /* Backward of pk_attn_fwd for the loss sum(out * dout): float32 dq [T,hq,d], dk and dv
  * [T,hkv,d] (dk, dv summed over the query heads of each KV group).  `out` and `lse` are the
- * forward's outputs for the same inputs.  dq, dk and dv are fully overwritten.
- * On packs too small to fill the device, the dQ kernel runs on a library-owned stream of the
- * same device (default priority, created on first use), forked from and joined back into
- * `hip_stream` with events, so every result is ordered on `hip_stream` as if it ran there. */
+ * forward's outputs for the same inputs (D = rowsum(dout * out) is formed from the given out).
+ * dq, dk and dv are fully overwritten.
+ * The first pk_attn_bwd_workspace_bytes bytes of `ws` hold the backward's operands; whatever
+ * `ws_bytes` leaves after them is a dS store.  When the store holds the pack's blocks
+ * (hq * ds_off[n_items] blocks of 16 KiB, a test made on the device, so nothing is read back),
+ * the dK/dV kernel writes its fp16 dS there and the dQ kernel computes dQ = dS K from it; else
+ * the dQ kernel recomputes S and dP (two more products).  Both give dq within the same rounding.
+ * Without a store, on packs too small to fill the device, the dQ kernel runs on a library-owned
+ * stream of the same device (default priority, created on first use), forked from and joined
+ * back into `hip_stream` with events, so every result is ordered on `hip_stream` as if it ran
+ * there. */
 pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *v,
                       const void *out, const float *lse, const void *dout,
                       int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float rope_base,

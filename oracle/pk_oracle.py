@@ -81,7 +81,26 @@ def build_meta(lengths: Sequence[int], total_tokens: int, tile_rows: int = TILE_
     fwd, bwd = work_lists(cu, seq_id, total_tokens, tile_rows)
     out["fwd_items"] = fwd
     out["bwd_items"] = bwd
+    out["ds_off"] = ds_block_offsets(bwd, total_tokens, tile_rows)
     return out
+
+
+DS_BLOCK_ROWS = 64       # query rows per block of the fast path's dS store
+
+
+def ds_block_offsets(bwd_items: np.ndarray, total_tokens: int, tile_rows: int = TILE_ROWS,
+                     block_rows: int = DS_BLOCK_ROWS) -> np.ndarray:
+    """Where the fast path's backward keeps dS (an index layout of this build, not of the pages,
+    like rule W): key tile u owns ceil((q_end - q_start) / block_rows) consecutive blocks, one per
+    block of its backward item's query rows, in tile order; off[u] is the first, off[n] the
+    total."""
+    n_items = -(-total_tokens // tile_rows)
+    blocks = np.zeros(n_items, dtype=np.int64)
+    for item in bwd_items:
+        blocks[int(item[7])] = -(-(int(item[3]) - int(item[2])) // block_rows)
+    off = np.zeros(n_items + 1, dtype=np.int64)
+    off[1:] = np.cumsum(blocks)
+    return off
 
 
 def work_lists(cu: np.ndarray, seq_id: np.ndarray, total_tokens: int, tile_rows: int = TILE_ROWS):

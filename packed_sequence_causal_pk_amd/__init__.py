@@ -45,13 +45,17 @@ def tile_rows() -> int:
 class PackedMeta:
     """B for one pack: a libpk handle plus the device buffer it lives in (kept alive here)."""
 
-    def __init__(self, handle: ctypes.c_void_p, buf, lengths, total_tokens: int, n_seqs: int):
+    def __init__(self, handle: ctypes.c_void_p, buf, lengths, total_tokens: int, n_seqs: int,
+                 max_seqlen: Optional[int] = None):
         self._handle = handle
         self.buf = buf
         self.lengths = lengths
         self.total_tokens = total_tokens
         self.n_seqs = n_seqs
         self.device = buf.device
+        # host-side bound on the longest sequence (the caller's packer knows it), used to size
+        # the backward's dS store; None: no store unless a bound is given to bwd_workspace
+        self.max_seqlen_bound = max_seqlen
 
     @property
     def handle(self) -> ctypes.c_void_p:
@@ -80,6 +84,7 @@ class PackedMeta:
             "fwd_items": sl(v.fwd_items, v.n_items * 8).view(v.n_items, 8),
             "bwd_items": sl(v.bwd_items, v.n_items * 8).view(v.n_items, 8),
             "n_items": v.n_items,
+            "ds_off": sl(v.ds_off, v.n_items + 1),
         }
 
     def check(self, stream=None) -> Tuple[int, int]:
@@ -102,9 +107,13 @@ class PackedMeta:
             pass
 
 
-def build_meta(lengths, total_tokens: Optional[int] = None, stream=None) -> PackedMeta:
+def build_meta(lengths, total_tokens: Optional[int] = None, stream=None,
+               max_seqlen: Optional[int] = None) -> PackedMeta:
     """Build B on the device from int32 `lengths` (a CUDA tensor).  `total_tokens` is T, the
-    token count of the pack as the caller's q/k/v hold it (never read back from the device)."""
+    token count of the pack as the caller's q/k/v hold it (never read back from the device).
+    `max_seqlen`, when the caller knows it, is a host-side bound on the longest sequence that
+    the backward uses to size its dS store (a wrong bound is safe: the device then falls back to
+    recomputing)."""
     torch = _torch()
     if lengths.dtype != torch.int32 or not lengths.is_cuda or lengths.dim() != 1:
         raise ValueError("lengths must be a 1-D int32 CUDA tensor")
@@ -120,7 +129,8 @@ def build_meta(lengths, total_tokens: Optional[int] = None, stream=None) -> Pack
     rc = lib().pk_build_meta(_ptr(lengths), n, int(total_tokens), _ptr(buf), nbytes,
                              _stream_ptr(stream), ctypes.byref(h))
     _lib.check("pk_build_meta", rc)
-    return PackedMeta(h, buf, lengths, int(total_tokens), n)
+    return PackedMeta(h, buf, lengths, int(total_tokens), n,
+                      None if max_seqlen is None else int(max_seqlen))
 
 
 def _dims(q, k):
@@ -134,9 +144,16 @@ def fwd_workspace(meta: PackedMeta, hq: int, hkv: int, d: int):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=meta.device)
 
 
-def bwd_workspace(meta: PackedMeta, hq: int, hkv: int, d: int):
+def bwd_workspace(meta: PackedMeta, hq: int, hkv: int, d: int, store: bool = True,
+                  max_seqlen: Optional[int] = None):
+    """Backward workspace; with `store` and a max_seqlen bound (given here, or the meta's), it
+    includes the dS store sized by pk_attn_bwd_workspace_bytes_ds."""
     torch = _torch()
-    n = int(lib().pk_attn_bwd_workspace_bytes(meta.handle, hq, hkv, d))
+    bound = meta.max_seqlen_bound if max_seqlen is None else max_seqlen
+    if store and bound is not None:
+        n = int(lib().pk_attn_bwd_workspace_bytes_ds(meta.handle, hq, hkv, d, int(bound)))
+    else:
+        n = int(lib().pk_attn_bwd_workspace_bytes(meta.handle, hq, hkv, d))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=meta.device)
 
 

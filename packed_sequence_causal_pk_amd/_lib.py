@@ -29,6 +29,7 @@ PK_MOE_MAX_ASSIGN = 1 << 26
 PK_MOE_BAD_EXPERT = 1
 PK_LORA_MAX_RANK = 64
 PK_NOALLOC_SCRATCH_BYTES = 128 << 20
+PK_DS_BLOCK_ROWS = 64
 PK_PROF_ALL = (1 << len(KERNEL_KINDS)) - 1
 
 # every function pk.h declares, with (restype, argtypes)
@@ -44,6 +45,7 @@ class MetaView(ctypes.Structure):
         ("cu_seqlens", _vp), ("max_seqlen", _vp), ("status", _vp), ("seq_id", _vp), ("pos", _vp),
         ("fwd_items", _vp), ("bwd_items", _vp),
         ("n_seqs", _i32), ("n_items", _i32), ("total_tokens", _i64), ("device", _i32),
+        ("ds_off", _vp),
     ]
 
 
@@ -58,6 +60,7 @@ SIGNATURES = {
     "pk_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "pk_attn_fwd_noalloc": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp]),
     "pk_attn_bwd_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
+    "pk_attn_bwd_workspace_bytes_ds": (_sz, [_vp, _i32, _i32, _i32, _i64]),
     "pk_attn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32,
                            _vp, _vp, _vp, _vp, _sz, _vp]),
     "pk_dense_mask": (_i32, [_vp, _vp, _sz, _vp]),

@@ -3,6 +3,7 @@
 // device except pk_meta_check and pk_prof_query, which say so in pk.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <mutex>
@@ -163,6 +164,18 @@ BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d) {
     return w;
 }
 
+int64_t ds_bound_blocks(int64_t T, int64_t max_seqlen_bound) {
+    // A key tile u's backward item spans the queries from its first row to the end of the last
+    // sequence it touches; that sequence starts inside the tile, so the span is at most
+    // min(T - 128 u, max_seqlen + 127) rows.
+    const int64_t L = (max_seqlen_bound > 0 && max_seqlen_bound < T) ? max_seqlen_bound : T;
+    const int64_t per_item = (L + PK_TILE_ROWS - 1 + PK_DS_BLOCK_ROWS - 1) / PK_DS_BLOCK_ROWS;
+    int64_t total = 0;
+    for (int64_t u = 0; u * PK_TILE_ROWS < T; ++u)
+        total += std::min<int64_t>((T - PK_TILE_ROWS * u + PK_DS_BLOCK_ROWS - 1) / PK_DS_BLOCK_ROWS, per_item);
+    return total;
+}
+
 }  // namespace pk
 
 extern "C" {
@@ -199,6 +212,7 @@ pk_status pk_build_meta(const int32_t *lengths_dev, int32_t n_seqs, int64_t tota
     m->bwd_items = reinterpret_cast<int32_t *>(base + L.bwd_items);
     m->fwd_raw = reinterpret_cast<int32_t *>(base + L.fwd_raw);
     m->bwd_raw = reinterpret_cast<int32_t *>(base + L.bwd_raw);
+    m->ds_off = reinterpret_cast<int32_t *>(base + L.ds_off);
     m->n_seqs = n_seqs;
     m->total_tokens = total_tokens;
     m->n_items = (int32_t)pk::n_tiles(total_tokens);
@@ -231,6 +245,7 @@ pk_status pk_meta_view(pk_meta_t meta, pk_meta_view_t *view) {
     view->n_items = meta->n_items;
     view->total_tokens = meta->total_tokens;
     view->device = meta->device;
+    view->ds_off = meta->ds_off;
     return PK_OK;
 }
 
@@ -262,6 +277,14 @@ size_t pk_attn_fwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int3
 size_t pk_attn_bwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d) {
     if (!meta || !shape_supported(hq, hkv, d)) return 0;
     return pk::bwd_workspace(meta->total_tokens, hq, hkv, d).total;
+}
+
+size_t pk_attn_bwd_workspace_bytes_ds(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d,
+                                      int64_t max_seqlen_bound) {
+    if (!meta || !shape_supported(hq, hkv, d)) return 0;
+    const int64_t T = meta->total_tokens;
+    const size_t blocks = (size_t)pk::ds_bound_blocks(T, max_seqlen_bound);
+    return pk::bwd_workspace(T, hq, hkv, d).total + align256(blocks * (size_t)hq * pk::kDsBlockBytes);
 }
 
 // The forward on a workspace `w` the caller has checked for size and alignment.
@@ -359,6 +382,26 @@ pk_status pk_attn_bwd_main(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d,
     const float *lse2 = reinterpret_cast<const float *>(w + W.lse2);
     const float *scale = reinterpret_cast<const float *>(w + W.scale);
     pk::AttnShape sh{T, hq, hkv, d, meta->n_items, softmax_scale};
+    // the rest of the workspace, if any, is the dS store
+    pk::DsStore ds{nullptr, 0};
+    if (ws_bytes > W.total) {
+        ds.cap_blocks = (int64_t)((ws_bytes - W.total) / ((size_t)hq * pk::kDsBlockBytes));
+        if (ds.cap_blocks > 0) ds.ptr = w + W.total;
+    }
+    if (ds.ptr) {
+        // dK/dV first (it writes the store when the pack's blocks fit), then dQ on the same
+        // stream; the device falls back to the recomputing dQ when they do not
+        hipError_t e;
+        {
+            ProfScope ps(PK_K_BWD, s);
+            e = pk::launch_bwd_kv(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2,
+                                  dsum, scale, w + W.rope, dk, dv, ds, s);
+        }
+        if (e != hipSuccess) return PK_ERR_HIP;
+        ProfScope ps(PK_K_BWD_DQ, s);
+        return hip_status(pk::launch_bwd_q(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16,
+                                           lse2, dsum, scale, w + W.rope, dq, ds, s));
+    }
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream *side = side_stream(meta->device);
     hipStream_t sq = s;   // stream of the dQ kernel
@@ -370,13 +413,13 @@ pk_status pk_attn_bwd_main(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d,
     {
         ProfScope ps(PK_K_BWD_DQ, sq);
         e = pk::launch_bwd_q(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
-                             scale, w + W.rope, dq, sq);
+                             scale, w + W.rope, dq, ds, sq);
     }
     hipError_t e2;
     {
         ProfScope ps(PK_K_BWD, s);
         e2 = pk::launch_bwd_kv(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
-                               scale, w + W.rope, dk, dv, s);
+                               scale, w + W.rope, dk, dv, ds, s);
     }
     if (sq != s) {
         // join: the caller's stream continues only after the dQ kernel

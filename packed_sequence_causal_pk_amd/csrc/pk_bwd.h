@@ -9,7 +9,8 @@
 // formula in [UN-2023] "Introducing Unsloth：LLM 训练提速 30 倍", "手动 Autograd" (which derives
 // its gradients by hand), applied to A = softmax(Q K^T / sqrt(d) + M) V.
 //
-// Two kernels, neither with atomics, so every gradient is written exactly once:
+// Two kernels, neither with atomics, so every gradient is written exactly once (and, when the
+// caller's workspace holds it, a dS store that hands dS from the first kernel to the second):
 //   k_attn_bwd_kv  one workgroup per backward work item (128 keys) x KV head, 8 waves split by
 //                  role over four 32-key sub-tiles; K_rot and V of a sub-tile's keys are the k
 //                  operands of S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_f16), dK^T and dV^T
@@ -22,9 +23,13 @@
 //                  the forward: S^T = K Q^T and dP^T = V dO^T give each lane one query, so its
 //                  lse and D are per-lane scalars; dQ^T += K^T dS^T accumulates in registers and
 //                  dQ is rotated back by R(-theta) and written once.
-// Recomputing S and dP in the second kernel costs two extra products; it replaces float atomics
-// on dQ (whose throughput, about 2.6 TB/s on this part, made them slower than the recompute),
-// a zero-fill of dq and a separate inverse-rotation pass.
+// dQ needs dS summed over keys, while k_attn_bwd_kv holds it laid out for sums over queries.
+// With a dS store, k_attn_bwd_kv writes its fp16 dS^T blocks and k_attn_bwd_q computes
+// dQ^T = K^T dS^T from them (one product, streaming dS from HBM; ds_read_b64_tr_b16 does the
+// transpose on the way out of LDS).  Without one, k_attn_bwd_q recomputes S and dP (two extra
+// products).  Either replaces float atomics on dQ (whose throughput, about 2.6 TB/s on this
+// part, made them slower than the recompute), a zero-fill of dq and a separate inverse-rotation
+// pass.
 //
 // Common to both: the mask is applied element-wise only on tiles that straddle a sequence
 // boundary or the diagonal, and tiles outside a wave's visible range skip their products;
@@ -58,7 +63,10 @@ struct BwdArgs {
     const float2 *rope;   // [T, D/2]
     const int32_t *items; // [n_items, 8] longest first (backward list for _kv, forward for _q)
     const int32_t *pos;   // [T]
-    const int32_t *hdr;
+    const int32_t *hdr;   // [3] = blocks of the pack's dS store
+    f16 *ds;              // the dS store (null: none), see PK_DS_BLOCK_ROWS
+    const int32_t *ds_off;// [n_items + 1] first block of each key tile (tile order)
+    int64_t ds_cap;       // blocks (of all hq heads) the store can hold
     float *dq;            // [T, hq, D]
     float *dk;            // [T, hkv, D]
     float *dv;            // [T, hkv, D]
@@ -83,6 +91,9 @@ inline BwdArgs make_bwd_args(const pk::AttnShape &sh, const pk_meta_s &m, const 
     a.items = nullptr;
     a.pos = m.pos;
     a.hdr = m.hdr;
+    a.ds = nullptr;
+    a.ds_off = m.ds_off;
+    a.ds_cap = 0;
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
@@ -92,6 +103,22 @@ inline BwdArgs make_bwd_args(const pk::AttnShape &sh, const pk_meta_s &m, const 
     a.group = sh.hq / sh.hkv;
     a.scale = sh.scale;
     return a;
+}
+
+// Layout of one stored block (128 keys x 64 queries, fp16, 16 KB): 16 chunks of 1 KB, chunk
+// c = 4 s + 2 hf + e for the 32-key sub-tile s, the 32-query half hf and e; inside a chunk,
+// lane l = n + 32 b holds the 8 queries 32 hf + 16 e + 8 b .. + 7 of key 32 s + n (16 bytes at
+// 16 l).  That is the order in which the dK/dV kernel's dS waves hold dS (one 1 KB store per
+// (hf, e)); the dQ kernel gathers the 16-byte pieces into a row-major [key][query] LDS tile.
+__device__ __forceinline__ int ds_piece_offset(int key, int qchunk) {   // halves, in a block
+    const int s = key >> 5, n = key & 31, hf = qchunk >> 2, e = (qchunk >> 1) & 1, b = qchunk & 1;
+    return ((4 * s + 2 * hf + e) * 64 + n + 32 * b) * 8;
+}
+
+// The dS store is used when the caller gave one that holds the pack's blocks (a wave-uniform
+// test on the meta's block total; both kernels reach the same decision).
+__device__ __forceinline__ bool ds_stored(const BwdArgs &a) {
+    return a.ds != nullptr && (int64_t)a.hdr[3] <= a.ds_cap;
 }
 
 }  // namespace pkb

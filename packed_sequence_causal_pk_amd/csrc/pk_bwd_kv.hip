@@ -135,6 +135,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
 
     const int nqb = (q_end - q_start + BQ - 1) / BQ;
     const int n_iter = a.group * nqb;
+    // dS store: block (key tile u, query block m, head h) sits at block index
+    // (ds_off[u] + m) * hq + h and holds dS of 128 keys x 64 queries in the register order of the
+    // dS waves (layout in pk_bwd.h), so each store instruction writes 1 KB contiguous
+    static_assert(BQ == PK_DS_BLOCK_ROWS, "dS store blocks are the kernel's query blocks");
+    const bool store = pkb::ds_stored(a);
+    f16 *ds_tile = store ? a.ds + (int64_t)a.ds_off[it[7]] * a.hq * (PK_TILE_ROWS * BQ) : nullptr;
+    const int ds_sub = (j - kv_start) >> 5;           // 32-key sub-tile of the 128-key tile
+    const int ds_lane = ds_sub * 2048 + 8 * lane;     // halves, inside a block
     const uint32_t loff = tile_copy_lane_off<D, 8>((int64_t)a.hq * D);
     // iteration itn: head (itn / nqb) of the group, query block (itn % nqb)
     auto iter_row = [&](int itn) { return q_start + (itn % nqb) * BQ; };
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
     // One 64-row block in buffer BUF.  Result register rr of the 32x32 products of half hf
     // belongs to block row 32 hf + 8 hb + (rr % 8) + 16 (rr / 8) (the row_perm order of the row
     // operand), so each lane's per-row values are two runs of 8 consecutive rows.
-    auto block = [&](auto bufc, int qb) __attribute__((always_inline)) {
+    auto block = [&](auto bufc, int qb, int itn) __attribute__((always_inline)) {
         constexpr int BUF = decltype(bufc)::value;
         const char *cq = reinterpret_cast<const char *>(sm.q[BUF]);
         const char *cg = reinterpret_cast<const char *>(sm.dO[BUF]);
@@ -266,6 +274,18 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
 #pragma unroll
                 for (int x = 0; x < 8; ++x) pb[hf][e][x] = (f16)sp[hf][8 * e + x];
         };
+        // dS waves with a store: write dS^T of half hf (zeros when `zero`) to block (u, m) of head
+        // h, m = (qb - first query row of the item) / BQ
+        auto store_ds = [&](int hf, bool zero) __attribute__((always_inline)) {
+            const int m = (qb - q_start) / BQ + (NS == 1 ? 0 : kh);   // block of the key tile
+            f16 *dst = ds_tile + ((int64_t)m * a.hq + iter_head(itn)) * (PK_TILE_ROWS * BQ) +
+                       ds_lane + 1024 * hf;
+            // streaming stores: the store is read once, by the dQ kernel, and left in the caches
+            // it would evict the query blocks other workgroups are about to re-read
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                __builtin_nontemporal_store(zero ? zero_f16x8() : pb[hf][e], reinterpret_cast<f16x8 *>(dst + 512 * e));
+        };
         // the second product of half hf: dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves);
         // queries are the k dimension and the transposed operand comes straight from the tile
         auto grads = [&](int hf) __attribute__((always_inline)) {
@@ -329,6 +349,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
                         pb[hf][1] = zero_f16x8();
                     }
                 }
+                if constexpr (!p_role) {
+                    if (store) {
+                        store_ds(0, false);
+                        store_ds(1, false);
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 grads(0);
                 grads(1);
@@ -339,6 +365,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            } else if constexpr (!p_role) {
+                // no row of the block sees these keys: their part of the store is zero
+                if (store) {
+                    store_ds(0, true);
+                    store_ds(1, true);
+                }
             }
         } else {
 #pragma unroll
@@ -348,7 +380,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
                     dscore(hf);
                 else
                     pconv(hf);
+                if constexpr (!p_role) {
+                    if (store) store_ds(hf, false);
+                }
                 grads(hf);
+            }
+            if constexpr (!p_role) {
+                if (store && !run[hf_own]) store_ds(hf_own, true);
             }
         }
     };
@@ -357,10 +395,19 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
     auto step = [&](auto bufc, int itn) __attribute__((always_inline)) {
         constexpr int BUF = decltype(bufc)::value;
         const int qb = iter_row(itn);
-        lds_copy_wait();
+        // wait for this block's copies; a dS wave's stores of the previous block (issued after
+        // those copies, and counted by vmcnt in order with them) may stay in flight
+        if constexpr (!p_role) {
+            if (store && itn > 0)
+                lds_copy_wait_keep<NS == 1 ? 4 : 2>();
+            else
+                lds_copy_wait();
+        } else {
+            lds_copy_wait();
+        }
         __syncthreads();   // B0: this block is in LDS; every wave is done with the other buffer
         if (itn + 1 < n_iter) kv_issue_block<D>(a, sm, BUF ^ 1, iter_head(itn + 1), iter_row(itn + 1), loff);
-        block(bufc, qb);
+        block(bufc, qb, itn);
     };
     for (int itn = 0; itn < n_iter; itn += 2) {
         step(std::integral_constant<int, 0>(), itn);
@@ -446,10 +493,12 @@ constexpr unsigned kSplitGrid = 256;
 hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                          const void *krot, const void *v, const void *dout16, const float *lse2,
                          const float *dsum, const float *scale, const void *rope, float *dk,
-                         float *dv, hipStream_t s) {
+                         float *dv, const DsStore &ds, hipStream_t s) {
     BwdArgs a = pkb::make_bwd_args(sh, m, qrot, krot, v, dout16, lse2, dsum, scale, rope, nullptr,
                                    dk, dv);
     a.items = m.bwd_items;
+    a.ds = (f16 *)ds.ptr;
+    a.ds_cap = ds.cap_blocks;
     const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hkv;
     const bool split = grid <= kSplitGrid;
     if (sh.d == 128) {

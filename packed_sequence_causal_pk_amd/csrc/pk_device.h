@@ -250,6 +250,14 @@ __device__ __forceinline__ f16x8 tile_tr_at(const char *t, const uint32_t (&off)
 
 __device__ __forceinline__ void lds_copy_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait for every vector memory operation of the wave but the last N (vmcnt counts them in
+// issue order): lets N global stores issued after the copies being waited for stay in flight.
+template <int N>
+__device__ __forceinline__ void lds_copy_wait_keep() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Make the compiler complete the pending global load of x here.  Used on values loaded before a
 // loop that keeps asynchronous LDS copies in flight: left alone, the compiler's wait for such a
 // value sits inside the loop, where a full vmcnt wait would also drain those copies.

@@ -17,6 +17,7 @@ struct pk_meta_s {
     int32_t *bwd_items;  // [n_items * 8], longest first
     int32_t *fwd_raw;    // [n_items * 8], tile order (build scratch)
     int32_t *bwd_raw;    // [n_items * 8], tile order (build scratch)
+    int32_t *ds_off;     // [n_items + 1], tile order: first dS block of each key tile; [n] = total
     int32_t n_seqs;
     int32_t n_items;
     int64_t total_tokens;
@@ -27,8 +28,14 @@ namespace pk {
 
 // Byte layout of the meta buffer; every region starts on a 256-byte boundary.
 struct MetaLayout {
-    size_t hdr, cu, seq_id, pos, fwd_items, bwd_items, fwd_raw, bwd_raw, total;
+    size_t hdr, cu, seq_id, pos, fwd_items, bwd_items, fwd_raw, bwd_raw, ds_off, total;
 };
+
+// The backward's dS store: the dK/dV kernel writes, for each key tile u and each block of
+// PK_DS_BLOCK_ROWS query rows in its backward item's range, and for each query head, the fp16
+// block dS^T [128 keys][64 queries] (16 KB); block (u, m) of head h sits at block index
+// (ds_off[u] + m) * hq + h.  The dQ kernel reads them back instead of recomputing S and dP.
+constexpr size_t kDsBlockBytes = (size_t)PK_TILE_ROWS * PK_DS_BLOCK_ROWS * 2;
 MetaLayout meta_layout(int32_t n_seqs, int64_t total_tokens);
 
 // Byte layout of the attention workspaces.
@@ -40,6 +47,9 @@ struct BwdWorkspace {
 };
 FwdWorkspace fwd_workspace(int64_t T, int hq, int hkv, int d);
 BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d);
+// Upper bound on the dS store's blocks (per head) for a pack of T tokens whose sequences are at
+// most max_seqlen_bound long (<= 0: no bound, i.e. T).
+int64_t ds_bound_blocks(int64_t T, int64_t max_seqlen_bound);
 
 inline int64_t n_tiles(int64_t T) { return (T + PK_TILE_ROWS - 1) / PK_TILE_ROWS; }
 
@@ -78,14 +88,20 @@ hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, co
 // dsum = -sigma * tau * rowsum(dout * out), lse2 = -lse * log2(e),
 // scale = {sigma, 1/sigma, tau, 1/(sigma tau)}.
 // launch_bwd_kv writes dk and dv, launch_bwd_q writes dq.
+// The dS store region of a backward workspace: `cap_blocks` blocks of kDsBlockBytes for each of
+// the hq heads (null / 0: none).
+struct DsStore {
+    void *ptr;
+    int64_t cap_blocks;
+};
 hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                          const void *krot, const void *v, const void *dout16, const float *lse2,
                          const float *dsum, const float *scale, const void *rope, float *dk,
-                         float *dv, hipStream_t s);
+                         float *dv, const DsStore &ds, hipStream_t s);
 hipError_t launch_bwd_q(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                         const void *krot, const void *v, const void *dout16, const float *lse2,
                         const float *dsum, const float *scale, const void *rope, float *dq,
-                        hipStream_t s);
+                        const DsStore &ds, hipStream_t s);
 
 // Steps around the attention path (pk_aux.hip, pk_moe.hip).
 hipError_t launch_dense_mask(const pk_meta_s &m, uint8_t *mask, hipStream_t s);

@@ -14,7 +14,8 @@
 //                  the backward item (key tile -> query range)
 //   k_meta_rank    one thread per tile: rank = #items with larger cost + #earlier items with the
 //                  same cost, i.e. a stable sort by cost, largest first -- the same "group once,
-//                  then use the offsets" idea as the routing change in [UN-2026] §3.
+//                  then use the offsets" idea as the routing change in [UN-2026] §3 -- and the
+//                  offsets of each key tile's blocks in the backward's dS store.
 #include "pk_internal.h"
 #include "pk_device.h"
 
@@ -139,22 +140,34 @@ __global__ __launch_bounds__(256) void k_meta_items(const int32_t *__restrict__ 
     }
 }
 
+// Query blocks of PK_DS_BLOCK_ROWS rows a backward item spans: ceil((q_end - q_start) / 64).
+__device__ __forceinline__ int item_query_blocks(const int32_t *item) {
+    return (item[3] - item[2] + PK_DS_BLOCK_ROWS - 1) / PK_DS_BLOCK_ROWS;
+}
+
+// Also, per key tile u (tile order), the offset of its first block in the backward's dS store:
+// ds_off[u] = sum over tiles u' < u of their query blocks, and ds_off[n_items] = the total, copied
+// to hdr[3] (an exclusive prefix sum formed in the same pass over the items as the ranks).
 __global__ __launch_bounds__(256) void k_meta_rank(const int32_t *__restrict__ fwd_raw,
                                                    const int32_t *__restrict__ bwd_raw,
                                                    int32_t n_items, int32_t *__restrict__ fwd,
-                                                   int32_t *__restrict__ bwd) {
+                                                   int32_t *__restrict__ bwd,
+                                                   int32_t *__restrict__ ds_off,
+                                                   int32_t *__restrict__ hdr) {
     __shared__ int s_cf[256];
     __shared__ int s_cb[256];
+    __shared__ int s_nb[256];
     const int tid = threadIdx.x;
     const int i = blockIdx.x * blockDim.x + tid;
     const int my_f = i < n_items ? fwd_raw[i * PK_ITEM_FIELDS + 6] : 0;
     const int my_b = i < n_items ? bwd_raw[i * PK_ITEM_FIELDS + 6] : 0;
-    int rank_f = 0, rank_b = 0;
+    int rank_f = 0, rank_b = 0, off = 0;
     for (int base = 0; base < n_items; base += 256) {
         __syncthreads();
         const int j = base + tid;
         s_cf[tid] = j < n_items ? fwd_raw[j * PK_ITEM_FIELDS + 6] : 0;
         s_cb[tid] = j < n_items ? bwd_raw[j * PK_ITEM_FIELDS + 6] : 0;
+        s_nb[tid] = j < n_items ? item_query_blocks(bwd_raw + j * PK_ITEM_FIELDS) : 0;
         __syncthreads();
         const int m = min(256, n_items - base);
         for (int x = 0; x < m; ++x) {
@@ -162,6 +175,7 @@ __global__ __launch_bounds__(256) void k_meta_rank(const int32_t *__restrict__ f
             const int cf = s_cf[x], cb = s_cb[x];
             rank_f += (cf > my_f) | ((cf == my_f) & (jj < i));
             rank_b += (cb > my_b) | ((cb == my_b) & (jj < i));
+            off += (jj < i) ? s_nb[x] : 0;
         }
     }
     if (i < n_items) {
@@ -169,6 +183,12 @@ __global__ __launch_bounds__(256) void k_meta_rank(const int32_t *__restrict__ f
         for (int k = 0; k < PK_ITEM_FIELDS; ++k) {
             fwd[rank_f * PK_ITEM_FIELDS + k] = fwd_raw[i * PK_ITEM_FIELDS + k];
             bwd[rank_b * PK_ITEM_FIELDS + k] = bwd_raw[i * PK_ITEM_FIELDS + k];
+        }
+        ds_off[i] = off;
+        if (i == n_items - 1) {
+            const int total = off + item_query_blocks(bwd_raw + i * PK_ITEM_FIELDS);
+            ds_off[n_items] = total;
+            hdr[3] = total;
         }
     }
 }
@@ -191,6 +211,7 @@ MetaLayout meta_layout(int32_t n_seqs, int64_t T) {
     L.bwd_items = off; off += align256(items);
     L.fwd_raw = off; off += align256(items);
     L.bwd_raw = off; off += align256(items);
+    L.ds_off = off; off += align256((size_t)(n_tiles(T) + 1) * sizeof(int32_t));
     L.total = off;
     return L;
 }
@@ -206,7 +227,8 @@ hipError_t launch_meta(const int32_t *lengths, const pk_meta_s &m, hipStream_t s
     const unsigned g = (unsigned)((m.n_items + 255) / 256);
     k_meta_items<<<g, 256, 0, stream>>>(m.cu, m.seq_id, T, m.n_items, m.hdr, m.fwd_raw, m.bwd_raw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_meta_rank<<<g, 256, 0, stream>>>(m.fwd_raw, m.bwd_raw, m.n_items, m.fwd_items, m.bwd_items);
+    k_meta_rank<<<g, 256, 0, stream>>>(m.fwd_raw, m.bwd_raw, m.n_items, m.fwd_items, m.bwd_items,
+                                       m.ds_off, m.hdr);
     return hipGetLastError();
 }
 

@@ -23,17 +23,24 @@ def dev(x, dtype=torch.bfloat16):
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype).contiguous()
 
 
-def run_pk(lengths, q, k, v, dout, scale, base=10000.0, meta=None, bwd=True):
-    """Build the meta (unless given) and run fwd (+ bwd) through libpk; numpy float64 outputs."""
+def run_pk(lengths, q, k, v, dout, scale, base=10000.0, meta=None, bwd=True, store=True):
+    """Build the meta (unless given) and run fwd (+ bwd) through libpk.  With `store` the
+    backward's workspace includes the dS store, sized from the pack's longest sequence (the
+    path the benchmark takes); without it the dQ kernel recomputes S and dP."""
     t = q.shape[0]
     if meta is None:
-        meta = pk.build_meta(torch.tensor(np.asarray(lengths, np.int32), device="cuda"), t)
+        lens = np.asarray(lengths, np.int32)
+        meta = pk.build_meta(torch.tensor(lens, device="cuda"), t,
+                             max_seqlen=int(lens.max()) if lens.size else 0)
     tq, tk, tv = dev(q), dev(k), dev(v)
     out, lse = pk.attn_fwd(meta, tq, tk, tv, scale, base)
     res = {"meta": meta, "out": out, "lse": lse}
     if bwd:
         tdo = dev(dout)
-        dq, dk, dv = pk.attn_bwd(meta, tq, tk, tv, out, lse, tdo, scale, base)
+        hq, hkv, d = q.shape[1], k.shape[1], q.shape[2]
+        ws = pk.bwd_workspace(meta, hq, hkv, d, store=store,
+                              max_seqlen=None if meta.max_seqlen_bound is not None else t)
+        dq, dk, dv = pk.attn_bwd(meta, tq, tk, tv, out, lse, tdo, scale, base, workspace=ws)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return res

@@ -98,6 +98,31 @@ def pin_worklist_coverage():
 
 
 # ----------------------------------------------------------------------------------------- RoPE
+def pin_ds_block_offsets():
+    """The dS store's block offsets by walking the pack: key tile u's first block comes after
+    every block of tiles before it, and tile u has one block per 64 query rows from its first
+    token to the end of the last sequence it touches (found by stepping token by token)."""
+    rng = np.random.default_rng(17)
+    for trial in range(12):
+        n = int(rng.integers(1, 9))
+        lengths = rng.integers(1, 300, size=n)
+        t = int(lengths.sum())
+        m = O.build_meta(lengths, t)
+        owner = np.repeat(np.arange(n), lengths)
+        tiles = -(-t // 128)
+        want = [0]
+        for u in range(tiles):
+            last = owner[min(128 * (u + 1), t) - 1]
+            end = 128 * u
+            while end < t and owner[end] <= last:
+                end += 1
+            rows = end - 128 * u
+            want.append(want[-1] + (rows + 63) // 64)
+        assert m["ds_off"].tolist() == want, (trial, lengths.tolist())
+    # one sequence of 300 tokens: tiles of 300, 172 and 44 rows -> 5, 3 and 1 blocks
+    assert O.build_meta([300], 300)["ds_off"].tolist() == [0, 5, 8, 9]
+
+
 def _rope_complex(x, pos, base):
     """Rotate-half RoPE as complex multiplication: (x1 + i x2) * exp(i theta)."""
     d = x.shape[-1]
@@ -462,7 +487,7 @@ def pin_lora_unmerged_and_zero_scale():
 
 
 ALL_PINS = [
-    pin_meta_golden, pin_meta_bruteforce, pin_worklist_coverage, pin_rope,
+    pin_meta_golden, pin_meta_bruteforce, pin_worklist_coverage, pin_ds_block_offsets, pin_rope,
     pin_fwd_dense_equals_per_sequence, pin_fwd_rows_and_closed_forms, pin_fwd_lse_reconstruction,
     pin_torch_sdpa_and_autograd, pin_bwd_finite_differences, pin_bwd_invariants,
     pin_bwd_given_output, pin_permutation_invariance, pin_dense_mask, pin_unmasked_pairs, pin_moe_golden, pin_moe_bruteforce,

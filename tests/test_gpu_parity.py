@@ -29,6 +29,8 @@ def _meta_matches_oracle(lengths, t):
     assert np.array_equal(got["pos"], ref["pos"])
     assert np.array_equal(got["fwd_items"], ref["fwd_items"])
     assert np.array_equal(got["bwd_items"], ref["bwd_items"])
+    if ref["status"] == 0:
+        assert np.array_equal(got["ds_off"], ref["ds_off"])
     return meta
 
 
@@ -99,15 +101,16 @@ SMALL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("store", [True, False], ids=["ds_store", "recompute"])
 @pytest.mark.parametrize("case", range(len(SMALL_CASES)))
-def test_fwd_bwd_small(case):
+def test_fwd_bwd_small(case, store):
     lengths, hq, hkv, d = SMALL_CASES[case]
     if lengths == "short":
         lengths = synth.random_lengths(np.random.default_rng(5), 120, 1, 16)
-    say("small case", case, "T", int(np.sum(lengths)), "hq/hkv/d", hq, hkv, d)
+    say("small case", case, "T", int(np.sum(lengths)), "hq/hkv/d", hq, hkv, d, "dS store", store)
     lens, q, k, v, do = synth.small_problem(100 + case, lengths, hq, hkv, d)
     scale = 1.0 / math.sqrt(d)
-    res = run_pk(lens, q, k, v, do, scale)
+    res = run_pk(lens, q, k, v, do, scale, store=store)
     o_ref, lse_ref = O.attn_fwd(q, k, v, lens, scale, 1e4)
     dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, scale, 1e4)
     compare("out", to_np(res["out"]), o_ref)
@@ -195,6 +198,33 @@ def test_gradient_scale_invariance(log2_scale):
     compare("dq", to_np(res["dq"]) / f, dq_ref)
     compare("dk", to_np(res["dk"]) / f, dk_ref)
     compare("dv", to_np(res["dv"]) / f, dv_ref)
+
+
+@pytest.mark.parametrize("name", ["llama1b", "qwen06b"])
+def test_ds_store_paths_agree(name):
+    """The backward with a dS store, without one, and with one too small for the pack (the
+    device then falls back to recomputing): dk and dv bitwise equal in all three (the store only
+    adds writes), dq bitwise equal between the no-store and fall-back runs, and dq from the
+    store within the gate of the oracle and of the recomputed dq."""
+    w = synth.WORKLOADS[name]
+    lengths = synth.pack_lengths(name)
+    q, k, v, do = (dev(x) for x in synth.layer_tensors(w, 2))
+    meta = pk.build_meta(torch.tensor(lengths, device="cuda"), w.total_tokens, max_seqlen=int(lengths.max()))
+    out, lse = pk.attn_fwd(meta, q, k, v, w.softmax_scale)
+    plain = pk.bwd_workspace(meta, w.hq, w.hkv, w.head_dim, store=False)
+    full = pk.bwd_workspace(meta, w.hq, w.hkv, w.head_dim)
+    small = torch.empty(plain.numel() + w.hq * 16384 * 4, dtype=torch.uint8, device="cuda")  # 4 blocks
+    say("dS store paths", name, "workspace bytes", plain.numel(), full.numel(), small.numel())
+    res = {}
+    for key, ws in (("plain", plain), ("store", full), ("fallback", small)):
+        res[key] = pk.attn_bwd(meta, q, k, v, out, lse, do, w.softmax_scale, workspace=ws)
+    torch.cuda.synchronize()
+    for key in ("store", "fallback"):
+        assert torch.equal(res[key][1], res["plain"][1]) and torch.equal(res[key][2], res["plain"][2]), key
+    assert torch.equal(res["fallback"][0], res["plain"][0])
+    compare("dq~", to_np(res["store"][0]), to_np(res["plain"][0]))
+    dq_ref, _, _ = O.attn_bwd(*synth.layer_tensors(w, 2), lengths, w.softmax_scale, w.rope_base)
+    compare("dq", to_np(res["store"][0]), dq_ref)
 
 
 def _bf16(x):

@@ -142,6 +142,15 @@ def _meta_max_is_sum(lengths, total_tokens, tile_rows=O.TILE_ROWS):
 _orig_score_grad = O.score_grad
 
 
+def _ds_floor(bwd, t, r, br):
+    """Mistake: a tile's partial last query block not counted."""
+    n = -(-t // r)
+    blocks = np.zeros(n, dtype=np.int64)
+    for item in bwd:
+        blocks[int(item[7])] = (int(item[3]) - int(item[2])) // br
+    return np.concatenate([[0], np.cumsum(blocks)])
+
+
 def _work_lists_ties_reversed(cu, seq_id, t, r=O.TILE_ROWS):
     """Mistake: equal-cost items ordered by descending tile index (not a stable order)."""
     f, b = _orig_work_lists(cu, seq_id, t, r)
@@ -174,6 +183,7 @@ MUTATIONS = {
     "dK_transposed_operand": ("key_grad", lambda ds, qr, scale: scale * (ds @ qr)),
     "worklist_short_range": ("work_lists", _cost_off_by_one),
     "dense_mask_strict": ("dense_mask", _mask_strict),
+    "ds_blocks_floor": ("ds_block_offsets", lambda b, t, r=O.TILE_ROWS, br=O.DS_BLOCK_ROWS: _ds_floor(b, t, r, br)),
     "kept_pairs_strict": ("unmasked_pairs", lambda lengths: int(sum(int(n) * (int(n) - 1) // 2 for n in lengths))),
     "moe_slot_major": (MO, "group_by_expert", _group_slot_major),
     "moe_inclusive_offsets": (MO, "group_by_expert", _group_inclusive_offsets),
