@@ -24,6 +24,10 @@ COMMON_FLAGS = [
     "--offload-arch=" + ARCH,
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a 64-bit value narrowed to 32 bits is an error: __builtin_amdgcn_readfirstlane takes an int,
+    # and a pointer passed through it keeps only its low half (a variant of the LoRA tile copy
+    # that did so addressed an unmapped page)
+    "-Werror=shorten-64-to-32",
 ]
 
 

@@ -22,6 +22,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace pkd {
 
+// 64-bit minimum (the device min() overloads take int: int64_t arguments would be truncated).
+__device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -217,7 +220,7 @@ __device__ __forceinline__ void tile_issue(f16 *tile, const f16 *x, int H, int h
         tile_copy_async_whole<D, ROWS, NW>(tile, x + (int64_t)row0 * stride + (int64_t)h * D, stride, lane_off);
     } else {
         tile_copy_async<D, ROWS>(tile, NW, [&](int row) {
-            return x + min((int64_t)(row0 + row), T - 1) * stride + (int64_t)h * D;
+            return x + min64((int64_t)row0 + row, T - 1) * stride + (int64_t)h * D;
         });
     }
 }

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256, MINWG) void k_gemm_nt(GemmArgs g) {
         } else {
             // the last row tile: rows past M read row M - 1 (finite data, never stored)
             tile_copy_async<kBK, kBM>(lds_a[buf], 4, [&](int row) {
-                return ab + min(m0 + row, g.M - 1) * ld + kk;
+                return ab + min64(m0 + row, g.M - 1) * ld + kk;
             });
         }
         tile_copy_async_whole<kBK, BN, 4>(lds_b[buf], bb + (int64_t)n0 * ld + kk, ld,

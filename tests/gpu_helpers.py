@@ -23,10 +23,10 @@ def dev(x, dtype=torch.bfloat16):
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype).contiguous()
 
 
-def run_pk(lengths, q, k, v, dout, scale, base=10000.0, meta=None, bwd=True, store=True):
-    """Build the meta (unless given) and run fwd (+ bwd) through libpk.  With `store` the
-    backward's workspace includes the dS store, sized from the pack's longest sequence (the
-    path the benchmark takes); without it the dQ kernel recomputes S and dP."""
+def run_pk(lengths, q, k, v, dout, scale, base=10000.0, meta=None, bwd=True, store=False):
+    """Build the meta (unless given) and run fwd (+ bwd) through libpk.  Without `store` the dQ
+    kernel recomputes S and dP (the path the benchmark times); with it the backward's workspace
+    includes the dS store, sized from the pack's longest sequence."""
     t = q.shape[0]
     if meta is None:
         lens = np.asarray(lengths, np.int32)

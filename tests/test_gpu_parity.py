@@ -336,13 +336,13 @@ def _sub_pack(lengths, seqs):
     return [int(lengths[s]) for s in seqs], idx
 
 
-def _check_workload(name, layer, seqs=None, kv_heads=None):
+def _check_workload(name, layer, seqs=None, kv_heads=None, store=False):
     w = synth.WORKLOADS[name]
     lengths = synth.pack_lengths(name)
     q, k, v, do = synth.layer_tensors(w, layer)
     say("workload", name, "layer", layer, "seqs", "all" if seqs is None else len(seqs),
-        "kv heads", "all" if kv_heads is None else list(kv_heads))
-    res = run_pk(lengths, q, k, v, do, w.softmax_scale, w.rope_base)
+        "kv heads", "all" if kv_heads is None else list(kv_heads), "dS store", store)
+    res = run_pk(lengths, q, k, v, do, w.softmax_scale, w.rope_base, store=store)
     if seqs is None:
         seqs = list(range(len(lengths)))
     sub_len, idx = _sub_pack(lengths, seqs)
@@ -374,11 +374,12 @@ def test_workload_qwen06b(layer):
     _check_workload("qwen06b", layer)
 
 
-@pytest.mark.parametrize("layer", [0, 39])
-def test_workload_qwen14b_sampled(layer):
+@pytest.mark.parametrize("layer,store", [(0, False), (39, False), (0, True)])
+def test_workload_qwen14b_sampled(layer, store):
     # the first and the last layer; the longest, the shortest and the last sequence plus one
-    # from the middle of the pack; four of the eight KV-head groups (both ends and two inside)
-    _check_workload("qwen14b", layer, seqs=[0, 4, 7, 9], kv_heads=[0, 3, 4, 7])
+    # from the middle of the pack; four of the eight KV-head groups (both ends and two inside);
+    # layer 0 also through the dS store
+    _check_workload("qwen14b", layer, seqs=[0, 4, 7, 9], kv_heads=[0, 3, 4, 7], store=store)
 
 
 def test_workload_skewed_sampled():
