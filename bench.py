@@ -444,7 +444,7 @@ def measure_reload(name="qwen06b", reps=3):
     dq = torch.empty(T, w.hq, w.head_dim, dtype=torch.float32, device=dev)
     dk = torch.empty(T, w.hkv, w.head_dim, dtype=torch.float32, device=dev)
     dv = torch.empty_like(dk)
-    ws = pk.bwd_workspace(meta, w.hq, w.hkv, w.head_dim, max_seqlen=int(max(lengths)))
+    ws = pk.bwd_workspace(meta, w.hq, w.hkv, w.head_dim, store=False)
     pipe = pk.ReloadPipeline()
     layer_bytes = sum(a.numel() * a.element_size() for a in acts[0])
 
@@ -490,10 +490,18 @@ def measure_reload(name="qwen06b", reps=3):
         for l in range(L):
             bwd(0, l)
 
+    def copies_beside_compute():
+        # the L copies and the L backwards at once, with no ordering between them: how much
+        # the copies slow down while the backward kernels run
+        for l in range(L):
+            fetch(l % 2, l)
+        compute_only()
+
     c = wall_ms(copies_only, reps) / L
     g = wall_ms(compute_only, reps) / L
     single = wall_ms(lambda: loop(False), reps)
     double = wall_ms(lambda: loop(True), reps)
+    beside = wall_ms(copies_beside_compute, reps)
     pipe.close()
     return {
         "workload": name, "layers": L, "reloaded_per_layer": "q, k, v, out (bf16), lse (fp32)",
@@ -503,6 +511,13 @@ def measure_reload(name="qwen06b", reps=3):
         "model_single_ms": round(L * (c + g), 3),
         "model_double_ms": round(c + (L - 1) * max(c, g) + g, 3),
         "saved_ms": round(single - double, 3), "model_saved_ms": round((L - 1) * min(c, g), 3),
+        "copies_beside_compute_ms": round(beside, 3),
+        "copies_beside_compute_note": "all L copies and all L backwards issued at once with no "
+                                      "ordering between them; against L c = %.3f ms alone" % (L * c),
+        # the model again with the raw copy time (no per-layer event ordering): c_raw = that run / L
+        "copy_ms_per_layer_raw": round(beside / L, 4),
+        "model_single_raw_ms": round(L * (beside / L + g), 3),
+        "model_double_raw_ms": round(beside / L + (L - 1) * max(beside / L, g) + g, 3),
     }
 
 

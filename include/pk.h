@@ -302,7 +302,9 @@ pk_status pk_reload_create(pk_reload_t *out /* host */);
 
 /* Enqueue on the pipeline's copy stream a copy of `bytes` from host memory `src_host` to device
  * memory `dst` (a buffer of slot `slot`, 0 or 1), after the compute work that the last
- * pk_reload_release(slot) marked.  Several fetches may fill one slot.  `src_host` should be
+ * pk_reload_release(slot) marked (the first fetch after a release makes the copy stream wait for
+ * it; the copy stream runs in order, so the slot's later fetches follow).  Several fetches may
+ * fill one slot.  `src_host` should be
  * page-locked (hipHostMalloc) memory: from pageable memory the runtime stages the copy through
  * the host and it no longer overlaps the compute (the Python binding requires pinned memory). */
 pk_status pk_reload_fetch(pk_reload_t r, int32_t slot, void *dst, const void *src_host,
