@@ -78,6 +78,44 @@ __device__ __forceinline__ void lds_row8(const T *p, T (&out)[8]) {
     }
 }
 
+// Writes one row of dK taken back through the rotation, y = R(-theta) (s * acc).  The lane holds dims 32 db + 8 g4 + 4 hb .. + 3 of the first half in acc[db] and their partners
+// (+ D/2) in acc[db + D/64].  Every cos/sin pair is loaded before the first store: the row and
+// the table may alias as far as the compiler knows, so a load placed after a store is kept
+// there, and its wait (vmcnt counts stores as well as loads) then also waits for the store --
+// one memory round trip per 16 bytes written instead of one for the row.
+template <int D>
+__device__ __forceinline__ void store_rotated_back(float *row, const float2 *cs, float s, int hb,
+                                                   const f32x16 (&acc)[D / 32]) {
+    constexpr int NH = D / 64;   // 32-dim blocks per half
+    float4 c[NH][4][2];
+#pragma unroll
+    for (int db = 0; db < NH; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 *p = reinterpret_cast<const float4 *>(cs + 32 * db + 8 * g4 + 4 * hb);
+            c[db][g4][0] = p[0];
+            c[db][g4][1] = p[1];
+        }
+#pragma unroll
+    for (int db = 0; db < NH; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int d = 32 * db + 8 * g4 + 4 * hb;
+            const float cx[4] = {c[db][g4][0].x, c[db][g4][0].z, c[db][g4][1].x, c[db][g4][1].z};
+            const float sx[4] = {c[db][g4][0].y, c[db][g4][0].w, c[db][g4][1].y, c[db][g4][1].w};
+            float y1[4], y2[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float x1 = acc[db][4 * g4 + x] * s;
+                const float x2 = acc[db + NH][4 * g4 + x] * s;
+                y1[x] = x1 * cx[x] + x2 * sx[x];
+                y2[x] = x2 * cx[x] - x1 * sx[x];
+            }
+            *reinterpret_cast<float4 *>(row + d) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+            *reinterpret_cast<float4 *>(row + d + D / 2) = make_float4(y2[0], y2[1], y2[2], y2[3]);
+        }
+}
+
 // The work of one (key tile, KV head) item is split by role over 8 waves; waves w and w + 4 own
 // the same 32 keys and share a SIMD:
 //   P waves (0..3)   S = Q K^T, the mask, P = exp2(S scale log2e - lse2), hand P over in LDS,
@@ -458,27 +496,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
                                     acc[db][4 * g4 + 2] * inv_sigma, acc[db][4 * g4 + 3] * inv_sigma);
                 }
         } else {
-            float *dkrow = a.dk + rowoff;
-            const float2 *cs = a.rope + (int64_t)j * (D / 2);
             // Q_rot carries scale * log2(e), so scale * dK_rot = ln(2) * acc
-            const float kscale = kLn2 * inv_sigma_tau;
-#pragma unroll
-            for (int db = 0; db < NDB / 2; ++db)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int d = 32 * db + 8 * g4 + 4 * hb;  // first half; partner d + D/2
-                    float y1[4], y2[4];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const float2 f = cs[d + x];
-                        const float x1 = acc[db][4 * g4 + x] * kscale;
-                        const float x2 = acc[db + NDB / 2][4 * g4 + x] * kscale;
-                        y1[x] = x1 * f.x + x2 * f.y;
-                        y2[x] = x2 * f.x - x1 * f.y;
-                    }
-                    *reinterpret_cast<float4 *>(dkrow + d) = make_float4(y1[0], y1[1], y1[2], y1[3]);
-                    *reinterpret_cast<float4 *>(dkrow + d + D / 2) = make_float4(y2[0], y2[1], y2[2], y2[3]);
-                }
+            store_rotated_back<D>(a.dk + rowoff, a.rope + (int64_t)j * (D / 2),
+                                       kLn2 * inv_sigma_tau, hb, acc);
         }
     }
 }
