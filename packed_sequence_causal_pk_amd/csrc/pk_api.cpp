@@ -160,6 +160,7 @@ BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d) {
     w.lse2 = off; off += align256((size_t)T * hq * 4);
     w.blockmax = off; off += align256((size_t)(dmax_blocks(T, hq, d) + vmax_blocks(T, hkv, d)) * 4);
     w.scale = off; off += align256(4 * 4);
+    w.sched = off; off += align256(kSchedInts * 4);
     w.total = off;
     return w;
 }
@@ -174,6 +175,29 @@ int64_t ds_bound_blocks(int64_t T, int64_t max_seqlen_bound) {
     for (int64_t u = 0; u * PK_TILE_ROWS < T; ++u)
         total += std::min<int64_t>((T - PK_TILE_ROWS * u + PK_DS_BLOCK_ROWS - 1) / PK_DS_BLOCK_ROWS, per_item);
     return total;
+}
+
+unsigned persistent_grid(const void *kernel, int threads) {
+    struct Entry {
+        int dev;
+        const void *kernel;
+        unsigned grid;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry &e : cache)
+        if (e.dev == dev && e.kernel == kernel) return e.grid;
+    int cus = 0, per_cu = 0;
+    unsigned grid = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) == hipSuccess &&
+        cus > 0 && per_cu > 0)
+        grid = (unsigned)(cus * per_cu) & ~7u;
+    cache.push_back({dev, kernel, grid});
+    return grid;
 }
 
 }  // namespace pk
@@ -361,7 +385,8 @@ pk_status pk_attn_bwd_prep(pk_meta_t meta, const void *q, const void *k, const v
         ra, q, k, v, out, dout, lse, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, w + W.rope,
         reinterpret_cast<float *>(w + W.dsum), reinterpret_cast<float *>(w + W.lse2),
         reinterpret_cast<float *>(w + W.blockmax), reinterpret_cast<float *>(w + W.scale),
-        softmax_scale * 1.4426950408889634f, meta->hdr + 2, s));
+        softmax_scale * 1.4426950408889634f, meta->hdr + 2, reinterpret_cast<int32_t *>(w + W.sched),
+        s));
 }
 
 pk_status pk_attn_bwd_main(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d,
@@ -395,7 +420,8 @@ pk_status pk_attn_bwd_main(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d,
         {
             ProfScope ps(PK_K_BWD, s);
             e = pk::launch_bwd_kv(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2,
-                                  dsum, scale, w + W.rope, dk, dv, ds, s);
+                                  dsum, scale, w + W.rope, dk, dv, ds,
+                                  reinterpret_cast<int32_t *>(w + W.sched), s);
         }
         if (e != hipSuccess) return PK_ERR_HIP;
         ProfScope ps(PK_K_BWD_DQ, s);
@@ -419,7 +445,8 @@ pk_status pk_attn_bwd_main(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d,
     {
         ProfScope ps(PK_K_BWD, s);
         e2 = pk::launch_bwd_kv(sh, *meta, w + W.qrot, w + W.krot, w + W.vh, w + W.dout16, lse2, dsum,
-                               scale, w + W.rope, dk, dv, ds, s);
+                               scale, w + W.rope, dk, dv, ds, reinterpret_cast<int32_t *>(w + W.sched),
+                               s);
     }
     if (sq != s) {
         // join: the caller's stream continues only after the dQ kernel

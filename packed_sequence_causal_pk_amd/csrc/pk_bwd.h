@@ -70,8 +70,9 @@ struct BwdArgs {
     float *dq;            // [T, hq, D]
     float *dk;            // [T, hkv, D]
     float *dv;            // [T, hkv, D]
+    int32_t *sched;       // per-launch work counters of a persistent launch
     int64_t T;
-    int hq, hkv, group;
+    int hq, hkv, group, n_items;
     float scale;
 };
 
@@ -97,10 +98,12 @@ inline BwdArgs make_bwd_args(const pk::AttnShape &sh, const pk_meta_s &m, const 
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
+    a.sched = nullptr;
     a.T = sh.T;
     a.hq = sh.hq;
     a.hkv = sh.hkv;
     a.group = sh.hq / sh.hkv;
+    a.n_items = sh.n_items;
     a.scale = sh.scale;
     return a;
 }

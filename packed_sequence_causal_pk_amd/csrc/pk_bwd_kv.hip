@@ -48,8 +48,8 @@ template <int D>
 __device__ __forceinline__ void kv_issue_block(const BwdArgs &a, KvSmem<D> &sm, int buf, int h,
                                                int qb, uint32_t loff) {
     using S = KvSmem<D>;
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = opaque_tid(), lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     tile_issue<D, S::BQ, 8>(sm.q[buf], a.qrot, a.hq, h, qb, a.T, loff);
     tile_issue<D, S::BQ, 8>(sm.dO[buf], a.dout16, a.hq, h, qb, a.T, loff);
     if (w == 0) {  // one wave: 64 rows x 4 bytes per array
@@ -134,22 +134,23 @@ __device__ __forceinline__ void store_rotated_back(float *row, const float2 *cs,
 // two halves' partial dK, dV are summed through LDS at the end.  Each block costs a wave half
 // the products, so the longest workgroup (which sets the time of a small pack) takes about half
 // as long.
-template <int D, int NS>
-__global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
+//
+// One unit: backward item r (key tile), key half kh (NS = 2) and KV head kvh.  claim() is called
+// as the last query block starts (persistent launches, pk_device.h).
+template <int D, int NS, typename Claim>
+__device__ __forceinline__ void kv_unit(const BwdArgs &a, KvSmem<D> &sm, int r, int kh, int kvh,
+                                        Claim &&claim) {
     static_assert(NS == 1 || NS == 2, "an item on one or two workgroups");
     using S = KvSmem<D>;
     constexpr int BQ = S::BQ;
     constexpr int NKK = D / 16, NDB = D / 32;
     constexpr uint32_t HALF = 32 * D * 2;    // bytes from row 0 to row 32 of a tile
-    __shared__ __attribute__((aligned(16))) S sm;
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = opaque_tid(), lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets bounds live in SGPRs
     const int w = wv & 3;              // P hand-off slot; with NS = 1 also the key sub-tile
     const bool p_role = wv < 4;
     const int n32 = lane & 31, hb = lane >> 5;
-    // workgroup -> (item r, key half kh, KV head kvh), heads fastest
-    const int r = blockIdx.x / (a.hkv * NS), kh = (blockIdx.x / a.hkv) % NS, kvh = blockIdx.x % a.hkv;
     const int sub = NS == 1 ? w : (w & 1);       // 32-key sub-tile of this wave
     const int hf_own = NS == 1 ? -1 : (w >> 1);  // with NS = 2: the query-block half of this wave
     const int32_t *it = a.items + (int64_t)r * PK_ITEM_FIELDS;
@@ -444,6 +445,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
             lds_copy_wait();
         }
         __syncthreads();   // B0: this block is in LDS; every wave is done with the other buffer
+        if (itn + 1 == n_iter) claim();
         if (itn + 1 < n_iter) kv_issue_block<D>(a, sm, BUF ^ 1, iter_head(itn + 1), iter_row(itn + 1), loff);
         block(bufc, qb, itn);
     };
@@ -503,35 +505,61 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
     }
 }
 
+// One workgroup per unit, or (PERSIST, NS = 1) a persistent grid of fewer workgroups that take
+// the units from per-XCD counters (pk_device.h).  Units are (item, KV head), heads fastest.
+template <int D, int NS, bool PERSIST>
+__global__ __launch_bounds__(512, 1) void k_attn_bwd_kv(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) KvSmem<D> sm;
+    if constexpr (PERSIST) {
+        static_assert(NS == 1, "persistent launches take whole items");
+        __shared__ int s_next[2];
+        persistent_units(a.sched, a.hkv * a.n_items, s_next,
+                         [&](int b, auto &claim) __attribute__((always_inline)) {
+                             const BwdArgs u = reload_args<BwdArgs>();
+                             kv_unit<D, 1>(u, sm, b / u.hkv, 0, b % u.hkv, claim);
+                         });
+    } else {
+        kv_unit<D, NS>(a, sm, blockIdx.x / (a.hkv * NS), (blockIdx.x / a.hkv) % NS, blockIdx.x % a.hkv,
+                       NoClaim());
+    }
+}
+
 }  // namespace
 
 namespace pk {
 
 // Items x KV heads up to which an item is split over two workgroups (NS = 2).
 constexpr unsigned kSplitGrid = 256;
+// Units per resident workgroup up to which the launch is persistent.
+constexpr unsigned kPersistentRounds = 8;
 
 hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                          const void *krot, const void *v, const void *dout16, const float *lse2,
                          const float *dsum, const float *scale, const void *rope, float *dk,
-                         float *dv, const DsStore &ds, hipStream_t s) {
+                         float *dv, const DsStore &ds, int32_t *sched, hipStream_t s) {
     BwdArgs a = pkb::make_bwd_args(sh, m, qrot, krot, v, dout16, lse2, dsum, scale, rope, nullptr,
                                    dk, dv);
     a.items = m.bwd_items;
     a.ds = (f16 *)ds.ptr;
     a.ds_cap = ds.cap_blocks;
-    const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hkv;
-    const bool split = grid <= kSplitGrid;
-    if (sh.d == 128) {
-        if (split)
-            k_attn_bwd_kv<128, 2><<<2 * grid, 512, 0, s>>>(a);
+    a.sched = sched;
+    const unsigned units = (unsigned)sh.n_items * (unsigned)sh.hkv;
+    auto go = [&](auto kernel, auto split, auto persistent) {
+        // A few long units per resident workgroup: a persistent grid of the resident workgroups.
+        // With many short ones the dispatcher's gaps are short too (measured on a pack of
+        // 8192-token sequences: no gain), and a plain launch is kept.
+        const unsigned slots = persistent_grid((const void *)persistent, 512);
+        if (units <= kSplitGrid)
+            split<<<2 * units, 512, 0, s>>>(a);
+        else if (slots && units > slots && units <= kPersistentRounds * slots)
+            persistent<<<slots, 512, 0, s>>>(a);
         else
-            k_attn_bwd_kv<128, 1><<<grid, 512, 0, s>>>(a);
-    } else {
-        if (split)
-            k_attn_bwd_kv<64, 2><<<2 * grid, 512, 0, s>>>(a);
-        else
-            k_attn_bwd_kv<64, 1><<<grid, 512, 0, s>>>(a);
-    }
+            kernel<<<units, 512, 0, s>>>(a);
+    };
+    if (sh.d == 128)
+        go(k_attn_bwd_kv<128, 1, false>, k_attn_bwd_kv<128, 2, false>, k_attn_bwd_kv<128, 1, true>);
+    else
+        go(k_attn_bwd_kv<64, 1, false>, k_attn_bwd_kv<64, 2, false>, k_attn_bwd_kv<64, 1, true>);
     return hipGetLastError();
 }
 

@@ -81,6 +81,68 @@ __device__ __forceinline__ void item_head_of_block(int b, int hq, int hkv, int &
     }
 }
 
+// threadIdx.x as a value the optimiser cannot hoist: in a persistent workgroup's loop over units
+// (below), the per-lane offsets a unit derives from it are recomputed per unit instead of being
+// held in registers across the whole loop.
+__device__ __forceinline__ int opaque_tid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// ---- Persistent workgroups -------------------------------------------------------------------
+// A persistent launch has G workgroups (a multiple of 8, as many as the device holds at once) for
+// more units than that.  Workgroup g serves the units b = 8 m + g % 8, the units a plain launch
+// would run on XCD g % 8 (workgroups go to the XCDs round-robin, so g itself runs there): first
+// m = g / 8, then, as it nears the end of a unit,
+// m = G / 8 + the value it takes from the class's counter sched[g % 8] (an atomic add).  So the
+// workgroup that finishes first takes the longest unit left in its class (the greedy longest-first
+// rule), and starts it at once instead of waiting for the dispatcher to start a new workgroup on
+// the freed slot.  The unit calls claim() as its last tile starts, which hides the add's latency
+// behind that tile; claiming earlier would reserve units for workgroups still busy with long ones.
+// (A unit that never calls claim() gets its next unit claimed when it ends.)  sched[8 + x] counts
+// the workgroups of class x that have left: the last one sets both counters back to zero, so every
+// launch finds them cleared (the prologue kernels also clear them, for a workspace's first use).
+// `unit(b, claim)` runs one unit with the whole workgroup; s_next is two LDS ints.
+template <typename F>
+__device__ __forceinline__ void persistent_units(int32_t *sched, int n_units, int *s_next, F &&unit) {
+    const int x = blockIdx.x & 7, wgs = gridDim.x >> 3;
+    const int count = n_units > x ? (n_units - x + 7) >> 3 : 0;   // units of class x
+    int m = blockIdx.x >> 3, par = 0;
+    while (m < count) {
+        int nxt = -1;   // (thread 0) the claimed next unit
+        auto claim = [&]() __attribute__((always_inline)) {
+            if (threadIdx.x == 0) nxt = wgs + atomicAdd(sched + x, 1);
+        };
+        unit(8 * m + x, claim);
+        if (threadIdx.x == 0) s_next[par] = nxt >= 0 ? nxt : wgs + atomicAdd(sched + x, 1);
+        __syncthreads();   // also: every wave is done with the unit's LDS
+        m = __builtin_amdgcn_readfirstlane(s_next[par]);
+        par ^= 1;
+    }
+    if (threadIdx.x == 0 && atomicAdd(sched + 8 + x, 1) == wgs - 1) {
+        atomicExch(sched + x, 0);
+        atomicExch(sched + 8 + x, 0);
+    }
+}
+
+// The claim() of a unit that is not part of a persistent launch.
+struct NoClaim {
+    __device__ void operator()() const {}
+};
+
+// The kernel's arguments, when they are its only parameter (so they sit at the start of the
+// kernel-argument segment), read afresh from that constant segment: a persistent loop that passes
+// this copy to its units reloads the fields each unit (a few scalar loads) instead of holding all
+// of them in scalar registers across the loop.
+template <typename Args>
+__device__ __forceinline__ Args reload_args() {
+    typedef __attribute__((address_space(4))) const Args *cptr;
+    cptr p = (cptr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    return *(const Args *)p;
+}
+
 // ---- Swizzled row-major fp16 LDS tiles ------------------------------------------------------
 // A tile holds rows of D halves with no padding; the 16-byte chunk c of row r is stored at chunk
 // position c ^ swz(r).  Two read patterns are conflict-free on the 64 LDS banks:

@@ -43,8 +43,14 @@ struct FwdWorkspace {
     size_t krot, vh, rope, total;
 };
 struct BwdWorkspace {
-    size_t qrot, krot, vh, dout16, rope, dsum, lse2, blockmax, scale, total;
+    size_t qrot, krot, vh, dout16, rope, dsum, lse2, blockmax, scale, sched, total;
 };
+// Work counters of the persistent dK/dV launch (int32, in the backward workspace), cleared by the
+// backward prologue.
+constexpr int kSchedInts = 16;
+// Workgroups of `kernel` (with `threads` threads each) the current device holds at once, rounded
+// down to a multiple of 8; 0 when the runtime cannot say.  Cached per device and kernel.
+unsigned persistent_grid(const void *kernel, int threads);
 FwdWorkspace fwd_workspace(int64_t T, int hq, int hkv, int d);
 BwdWorkspace bwd_workspace(int64_t T, int hq, int hkv, int d);
 // Upper bound on the dS store's blocks (per head) for a pack of T tokens whose sequences are at
@@ -75,7 +81,7 @@ hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, cons
                            const void *out, const void *dout, const float *lse, void *qrot,
                            void *krot, void *vh, void *dout16, void *rope, float *dsum,
                            float *lse2, float *blockmax, float *scale, float qscale,
-                           int32_t *flags, hipStream_t s);
+                           int32_t *flags, int32_t *sched, hipStream_t s);   // also clears sched
 
 struct AttnShape {
     int64_t T;
@@ -97,7 +103,7 @@ struct DsStore {
 hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                          const void *krot, const void *v, const void *dout16, const float *lse2,
                          const float *dsum, const float *scale, const void *rope, float *dk,
-                         float *dv, const DsStore &ds, hipStream_t s);
+                         float *dv, const DsStore &ds, int32_t *sched, hipStream_t s);
 hipError_t launch_bwd_q(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                         const void *krot, const void *v, const void *dout16, const float *lse2,
                         const float *dsum, const float *scale, const void *rope, float *dq,

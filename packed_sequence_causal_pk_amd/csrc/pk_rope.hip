@@ -207,14 +207,16 @@ __device__ __forceinline__ void rope_table_block(const int32_t *__restrict__ pos
 // First launch of the backward prologue, three independent jobs in one grid (fewer launches,
 // which small packs feel): blocks [0, nb) reduce max|dout| per block, blocks [nb, nb + nbv)
 // max|v| per block (into blockmax[nb ..]), the rest write the RoPE table (one thread per token
-// and group of 4 rotation pairs).
+// and group of 4 rotation pairs).  Block 0 also clears the work counters.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_pre(const bf16 *__restrict__ dout, int64_t n8,
                                                  const bf16 *__restrict__ v, int64_t n8v,
                                                  float *__restrict__ blockmax, int nb, int nbv,
                                                  const int32_t *__restrict__ pos, int64_t T,
-                                                 float base, float2 *__restrict__ table) {
+                                                 float base, float2 *__restrict__ table,
+                                                 int32_t *__restrict__ sched) {
     const int b = (int)blockIdx.x;
+    if (b == 0 && threadIdx.x < pk::kSchedInts) sched[threadIdx.x] = 0;
     if (b < nb)
         bwd_amax_block(dout, n8, blockmax, b, nb);
     else if (b < nb + nbv)
@@ -404,7 +406,7 @@ hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, cons
                            const void *out, const void *dout, const float *lse, void *qrot,
                            void *krot, void *vh, void *dout16, void *rope, float *dsum,
                            float *lse2, float *blockmax, float *scale, float qscale,
-                           int32_t *flags, hipStream_t s) {
+                           int32_t *flags, int32_t *sched, hipStream_t s) {
     const int64_t n8 = r.T * r.hq * r.d / 8, n8v = r.T * r.hkv * r.d / 8;
     const unsigned nb = dmax_blocks(r.T, r.hq, r.d), nbv = vmax_blocks(r.T, r.hkv, r.d);
     const unsigned gt = prep_blocks(r.T, r.d);
@@ -412,11 +414,11 @@ hipError_t launch_bwd_prep(const RopeArgs &r, const void *q, const void *k, cons
     if (r.d == 128)
         k_bwd_pre<128><<<nb + nbv + gt, 256, 0, s>>>((const bf16 *)dout, n8, (const bf16 *)v, n8v,
                                                      blockmax, (int)nb, (int)nbv, r.pos, r.T,
-                                                     r.rope_base, (float2 *)rope);
+                                                     r.rope_base, (float2 *)rope, sched);
     else
         k_bwd_pre<64><<<nb + nbv + gt, 256, 0, s>>>((const bf16 *)dout, n8, (const bf16 *)v, n8v,
                                                     blockmax, (int)nb, (int)nbv, r.pos, r.T,
-                                                    r.rope_base, (float2 *)rope);
+                                                    r.rope_base, (float2 *)rope, sched);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (r.d == 128) {

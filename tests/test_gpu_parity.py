@@ -547,6 +547,36 @@ def test_split_backward_overlapped_matches_fused(name):
         assert torch.equal(dq_a, dq_b), l
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("store", [False, True], ids=["recompute", "ds_store"])
+def test_bwd_main_repeats_on_one_prologue(store):
+    """The dK/dV kernel's persistent launch (Qwen3-14B-shaped pack: 1024 key-tile x KV-head units,
+    more than the resident workgroups) takes its units from work counters in the workspace.  The
+    prologue clears them (here over a workspace filled with 0xff bytes first), and the launch sets
+    them back to zero as it ends, so pk_attn_bwd_main run three times on one pk_attn_bwd_prep
+    gives bitwise the gradients of the fused pk_attn_bwd every time."""
+    name = "qwen14b"
+    w = synth.WORKLOADS[name]
+    lengths = synth.pack_lengths(name)
+    say("backward main x3 on one prologue", name, "store", store)
+    meta = pk.build_meta(torch.tensor(lengths, device="cuda"), w.total_tokens, max_seqlen=max(lengths))
+    q, k, v, do = (dev(x) for x in synth.layer_tensors(w, 0))
+    out, lse = pk.attn_fwd(meta, q, k, v, w.softmax_scale)
+    ref = pk.attn_bwd(meta, q, k, v, out, lse, do, w.softmax_scale,
+                      workspace=pk.bwd_workspace(meta, w.hq, w.hkv, w.head_dim, store=store))
+    ws = pk.bwd_workspace(meta, w.hq, w.hkv, w.head_dim, store=store)
+    ws.fill_(255)
+    pk.attn_bwd_prep(meta, q, k, v, out, lse, do, ws, w.softmax_scale)
+    for rep in range(3):
+        dq = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+        dk = torch.full((q.shape[0], w.hkv, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+        dv = torch.full_like(dk, float("nan"))
+        pk.attn_bwd_main(meta, w.hq, w.hkv, w.head_dim, ws, dq, dk, dv, w.softmax_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(dk, ref[1]) and torch.equal(dv, ref[2]), rep
+        assert torch.equal(dq, ref[0]), rep
+
+
 def test_layer_loop_makes_no_host_sync():
     """Building B once and running several layers' forward and backward through the binding
     issues no synchronising torch operation (torch's sync debug mode turns one into an error);
