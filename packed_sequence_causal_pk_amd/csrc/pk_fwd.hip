@@ -53,6 +53,8 @@ struct FwdArgs {
     int64_t T;
     int hq, hkv, group;
     float scale_log2;     // softmax scale * log2(e)
+    float inv_scale_log2; // its reciprocal (the rescale threshold is a heuristic: a rounding of
+                          // it only moves which tile rescales)
 };
 
 template <int D>
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
             for (int db = 0; db < NDB; ++db) o[db] *= alpha;
             mref = mnew;
             neg_m = mref == -INFINITY ? 0.f : -mref;
-            thr = (mref + 8.f) / a.scale_log2;
+            thr = (mref + 8.f) * a.inv_scale_log2;
         }
         // P in fp16 (the k operand of the second product); l sums the same fp16 weights, two at
         // a time with v_dot2_f32_f16 against (1, 1)
@@ -332,6 +334,7 @@ hipError_t launch_fwd(const AttnShape &sh, const pk_meta_s &m, const void *q, co
     a.hkv = sh.hkv;
     a.group = sh.hq / sh.hkv;
     a.scale_log2 = sh.scale * pkd::kLog2e;
+    a.inv_scale_log2 = (float)(1.0 / ((double)sh.scale * 1.4426950408889634));
     const unsigned grid = (unsigned)sh.n_items * (unsigned)sh.hq;
     const bool small = grid <= 2048;   // a few rounds of workgroups on a 256-CU device
     if (sh.d == 128) {
