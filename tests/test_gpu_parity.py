@@ -548,6 +548,30 @@ def test_split_backward_overlapped_matches_fused(name):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("d,store", [(64, False), (128, False), (128, True)],
+                         ids=["d64", "d128", "d128_ds_store"])
+def test_persistent_dkdv_launch(d, store):
+    """A pack whose (key tile, KV head) units outnumber the resident dK/dV workgroups (8506
+    tokens in 28 sequences of 64..512: 67 tiles x 8 KV heads = 536 units), so the dK/dV kernel
+    runs as a persistent grid taking units from its work counters: every output against the
+    oracle on the whole pack."""
+    lengths = synth.random_lengths(np.random.default_rng(7), 28, 64, 512)
+    hq, hkv = 16, 8
+    say("persistent dK/dV launch: T", int(np.sum(lengths)), "hq/hkv/d", hq, hkv, d, "dS store", store)
+    lens, q, k, v, do = synth.small_problem(300, lengths, hq, hkv, d)
+    assert -(-int(np.sum(lens)) // 128) * hkv > 256
+    scale = 1.0 / math.sqrt(d)
+    res = run_pk(lens, q, k, v, do, scale, store=store)
+    o_ref, lse_ref = O.attn_fwd(q, k, v, lens, scale, 1e4)
+    dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, scale, 1e4)
+    compare("out", to_np(res["out"]), o_ref)
+    compare("lse", to_np(res["lse"]), lse_ref, max_abs=LSE_MAX_ABS)
+    compare("dq", to_np(res["dq"]), dq_ref)
+    compare("dk", to_np(res["dk"]), dk_ref)
+    compare("dv", to_np(res["dv"]), dv_ref)
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("store", [False, True], ids=["recompute", "ds_store"])
 def test_bwd_main_repeats_on_one_prologue(store):
     """The dK/dV kernel's persistent launch (Qwen3-14B-shaped pack: 1024 key-tile x KV-head units,
