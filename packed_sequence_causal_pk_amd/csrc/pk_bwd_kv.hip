@@ -53,7 +53,7 @@ __device__ __forceinline__ void kv_issue_block(const BwdArgs &a, KvSmem<D> &sm, 
     tile_issue<D, S::BQ, 8>(sm.q[buf], a.qrot, a.hq, h, qb, a.T, loff);
     tile_issue<D, S::BQ, 8>(sm.dO[buf], a.dout16, a.hq, h, qb, a.T, loff);
     if (w == 0) {  // one wave: 64 rows x 4 bytes per array
-        if (qb + S::BQ <= a.T) {
+        if (qb + S::BQ <= (int)a.T) {   // T <= PK_MAX_TOKENS; a 32-bit test stays scalar
             lds_dma_s<4>(a.lse2 + (int64_t)h * a.T + qb, 4u * lane, lds_addr(sm.lse2[buf]));
             lds_dma_s<4>(a.dsum + (int64_t)h * a.T + qb, 4u * lane, lds_addr(sm.dd[buf]));
             lds_dma_s<4>(a.pos + qb, 4u * lane, lds_addr(sm.pos[buf]));

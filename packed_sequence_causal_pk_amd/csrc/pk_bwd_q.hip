@@ -107,7 +107,7 @@ __device__ __forceinline__ void q_from_store(const BwdArgs &a, char *lds, const 
     const f16 *kp = a.krot + ((int64_t)kb_hi * a.hkv + kvh) * D;
     auto issue_k = [&](int sidx, int buf) {
         const int k0 = kb_hi - BK * sidx;
-        if (k0 + BK <= T)
+        if (k0 + BK <= (int)T)
             tile_copy_async_whole<D, BK, 4>(lds_k + buf * BK * D, kp, (int64_t)a.hkv * D, loff);
         else
             tile_issue<D, BK>(lds_k + buf * BK * D, a.krot, a.hkv, kvh, k0, T, loff);
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_q(BwdArgs a) {
     const f16 *kp = a.krot + ((int64_t)kb_hi * a.hkv + kvh) * D;
     const f16 *vp = a.v + ((int64_t)kb_hi * a.hkv + kvh) * D;
     auto issue_tile = [&](int k0, int buf) {
-        if (k0 + BK <= T) {
+        if (k0 + BK <= (int)T) {
             tile_copy_async_whole<D, BK, 4>(lds_k[buf], kp, (int64_t)a.hkv * D, loff);
             tile_copy_async_whole<D, BK, 4>(lds_v[buf], vp, (int64_t)a.hkv * D, loff);
         } else {

@@ -278,7 +278,7 @@ template <int D, int ROWS, int NW = 4>
 __device__ __forceinline__ void tile_issue(f16 *tile, const f16 *x, int H, int h, int row0, int64_t T,
                                            uint32_t lane_off) {
     const int64_t stride = (int64_t)H * D;
-    if (row0 + ROWS <= T) {
+    if (row0 + ROWS <= (int)T) {   // T <= PK_MAX_TOKENS; a 32-bit test stays scalar
         tile_copy_async_whole<D, ROWS, NW>(tile, x + (int64_t)row0 * stride + (int64_t)h * D, stride, lane_off);
     } else {
         tile_copy_async<D, ROWS>(tile, NW, [&](int row) {

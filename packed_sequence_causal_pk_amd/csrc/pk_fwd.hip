@@ -162,10 +162,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     // from running pointers that step back one tile per issue, so an issue costs a 64-bit
     // subtraction instead of a multiply.
     const int64_t tstride = (int64_t)BK * a.hkv * D;
+    const int T32 = (int)T;   // (T <= PK_MAX_TOKENS: a 32-bit test is a scalar compare, a 64-bit
+                              // signed one takes vector instructions on this target)
     const f16 *kp = a.krot + ((int64_t)kb_hi * a.hkv + kvh) * D;
     const f16 *vp = a.v + ((int64_t)kb_hi * a.hkv + kvh) * D;
     auto issue_tile = [&](int k0, int buf) {
-        if (k0 + BK <= T) {
+        if (k0 + BK <= T32) {
             tile_copy_async_whole<D, BK, 4>(lds_k[buf], kp, (int64_t)a.hkv * D, loff);
             tile_copy_async_whole<D, BK, 4>(lds_v[buf], vp, (int64_t)a.hkv * D, loff);
         } else {
