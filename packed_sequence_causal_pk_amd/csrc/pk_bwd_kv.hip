@@ -530,8 +530,6 @@ namespace pk {
 
 // Items x KV heads up to which an item is split over two workgroups (NS = 2).
 constexpr unsigned kSplitGrid = 256;
-// Units per resident workgroup up to which the launch is persistent.
-constexpr unsigned kPersistentRounds = 8;
 
 hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qrot,
                          const void *krot, const void *v, const void *dout16, const float *lse2,
@@ -545,13 +543,11 @@ hipError_t launch_bwd_kv(const AttnShape &sh, const pk_meta_s &m, const void *qr
     a.sched = sched;
     const unsigned units = (unsigned)sh.n_items * (unsigned)sh.hkv;
     auto go = [&](auto kernel, auto split, auto persistent) {
-        // A few long units per resident workgroup: a persistent grid of the resident workgroups.
-        // With many short ones the dispatcher's gaps are short too (measured on a pack of
-        // 8192-token sequences: no gain), and a plain launch is kept.
+        // more units than resident workgroups: a persistent grid of the resident workgroups
         const unsigned slots = persistent_grid((const void *)persistent, 512);
         if (units <= kSplitGrid)
             split<<<2 * units, 512, 0, s>>>(a);
-        else if (slots && units > slots && units <= kPersistentRounds * slots)
+        else if (slots && units > slots)
             persistent<<<slots, 512, 0, s>>>(a);
         else
             kernel<<<units, 512, 0, s>>>(a);
