@@ -94,13 +94,13 @@ __device__ __forceinline__ int opaque_tid() {
 // A persistent launch has G workgroups (a multiple of 8, as many as the device holds at once) for
 // more units than that.  Workgroup g serves the units b = 8 m + g % 8, the units a plain launch
 // would run on XCD g % 8 (workgroups go to the XCDs round-robin, so g itself runs there): first
-// m = g / 8, then, as it nears the end of a unit,
-// m = G / 8 + the value it takes from the class's counter sched[g % 8] (an atomic add).  So the
-// workgroup that finishes first takes the longest unit left in its class (the greedy longest-first
-// rule), and starts it at once instead of waiting for the dispatcher to start a new workgroup on
-// the freed slot.  The unit calls claim() as its last tile starts, which hides the add's latency
-// behind that tile; claiming earlier would reserve units for workgroups still busy with long ones.
-// (A unit that never calls claim() gets its next unit claimed when it ends.)  sched[8 + x] counts
+// m = g / 8, then, as it nears the end of each unit, m = G / 8 + the value it takes from the
+// class's counter sched[g % 8] (an atomic add).  So the workgroup that finishes first takes the
+// longest unit left in its class (the greedy longest-first rule), and starts it at once instead
+// of waiting for the dispatcher to start a new workgroup on the freed slot.  The unit calls
+// claim() as its last block of work starts, which hides the add's latency behind that block;
+// claiming earlier would reserve units for workgroups still busy with long ones.  (A unit that
+// never calls claim() gets its next unit claimed when it ends.)  sched[8 + x] counts
 // the workgroups of class x that have left: the last one sets both counters back to zero, so every
 // launch finds them cleared (the prologue kernels also clear them, for a workspace's first use).
 // `unit(b, claim)` runs one unit with the whole workgroup; s_next is two LDS ints.
