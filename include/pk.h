@@ -168,8 +168,9 @@ pk_status pk_attn_fwd_noalloc(pk_meta_t meta, const void *q, const void *k, cons
                               float rope_base, void *out, float *lse, void *hip_stream);
 
 /* Workspace bytes pk_attn_bwd needs: the fp16 operands (rotated Q and K, V, scaled dout), the
- * RoPE table, per-row values (rowsum(dout * out), lse) and the dout scale with its per-block
- * maxima. */
+ * RoPE table, per-row values (rowsum(dout * out), lse), the dout and v scales with their
+ * per-block maxima, and the work counters of the dK/dV kernel's persistent launch (which the
+ * prologue clears and the launch leaves at zero; calls that overlap on one workspace race). */
 size_t pk_attn_bwd_workspace_bytes(pk_meta_t meta, int32_t hq, int32_t hkv, int32_t d);
 
 /* Query rows per block of the backward's dS store. */
@@ -209,7 +210,8 @@ pk_status pk_attn_bwd(pk_meta_t meta, const void *q, const void *k, const void *
  * matrix cores busy).  pk_attn_bwd_prep reads q, k, v, out, lse, dout and writes the backward's
  * operands into `ws`; pk_attn_bwd_main reads only `ws` (same size as pk_attn_bwd's) and writes
  * dq, dk, dv.  pk_attn_bwd = prep then main on one stream.  Between the two halves the caller
- * orders the streams (e.g. with events); two layers in flight need two workspaces. */
+ * orders the streams (e.g. with events); two layers in flight need two workspaces.
+ * pk_attn_bwd_main may run again on the same prologue (it leaves `ws`'s operands unchanged). */
 pk_status pk_attn_bwd_prep(pk_meta_t meta, const void *q, const void *k, const void *v,
                            const void *out, const float *lse, const void *dout, int32_t hq,
                            int32_t hkv, int32_t d, float softmax_scale, float rope_base, void *ws,
