@@ -9,9 +9,12 @@
 // formula in [UN-2023] "Introducing Unsloth：LLM 训练提速 30 倍", "手动 Autograd" (which derives
 // its gradients by hand), applied to A = softmax(Q K^T / sqrt(d) + M) V.
 //
-// Two kernels, neither with atomics, so every gradient is written exactly once (and, when the
-// caller's workspace holds it, a dS store that hands dS from the first kernel to the second):
-//   k_attn_bwd_kv  one workgroup per backward work item (128 keys) x KV head, 8 waves split by
+// Two kernels, neither with atomics on the results (the only atomics are a persistent launch's
+// work counters), so every gradient is written exactly once (and, when the caller's workspace
+// holds it, a dS store that hands dS from the first kernel to the second):
+//   k_attn_bwd_kv  one workgroup per backward work item (128 keys) x KV head (on packs with more
+//                  of these units than the device holds workgroups at once, a persistent grid that
+//                  takes them from per-XCD work counters, pk_device.h), 8 waves split by
 //                  role over four 32-key sub-tiles; K_rot and V of a sub-tile's keys are the k
 //                  operands of S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_f16), dK^T and dV^T
 //                  accumulate in registers over every query block AND every query head of the
