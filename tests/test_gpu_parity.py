@@ -548,17 +548,22 @@ def test_split_backward_overlapped_matches_fused(name):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("d,store", [(64, False), (128, False), (128, True)],
-                         ids=["d64", "d128", "d128_ds_store"])
-def test_persistent_dkdv_launch(d, store):
+@pytest.mark.parametrize("d,store,hkv", [(64, False, 8), (128, False, 8), (128, True, 8), (64, False, 2)],
+                         ids=["d64", "d128", "d128_ds_store", "d64_2kv"])
+def test_persistent_dkdv_launch(d, store, hkv):
     """A pack whose (key tile, KV head) units outnumber the resident dK/dV workgroups (8506
-    tokens in 28 sequences of 64..512: 67 tiles x 8 KV heads = 536 units), so the dK/dV kernel
-    runs as a persistent grid taking units from its work counters: every output against the
-    oracle on the whole pack."""
-    lengths = synth.random_lengths(np.random.default_rng(7), 28, 64, 512)
-    hq, hkv = 16, 8
+    tokens in 28 sequences of 64..512: 67 tiles x 8 KV heads = 536 units; or, with 2 KV heads,
+    40403 tokens in 140 sequences: 316 tiles x 2 = 632 units, so the XCD classes b mod 8 mix
+    tiles and heads), so the dK/dV kernel runs as a persistent grid taking units from its work
+    counters: every output against the oracle on the whole pack."""
+    if hkv == 8:
+        lengths = synth.random_lengths(np.random.default_rng(7), 28, 64, 512)
+        hq = 16
+    else:
+        lengths = synth.random_lengths(np.random.default_rng(11), 140, 64, 512)
+        hq = 4
     say("persistent dK/dV launch: T", int(np.sum(lengths)), "hq/hkv/d", hq, hkv, d, "dS store", store)
-    lens, q, k, v, do = synth.small_problem(300, lengths, hq, hkv, d)
+    lens, q, k, v, do = synth.small_problem(300 if hkv == 8 else 400, lengths, hq, hkv, d)
     assert -(-int(np.sum(lens)) // 128) * hkv > 256
     scale = 1.0 / math.sqrt(d)
     res = run_pk(lens, q, k, v, do, scale, store=store)
