@@ -547,6 +547,39 @@ def test_split_backward_overlapped_matches_fused(name):
         assert torch.equal(dq_a, dq_b), l
 
 
+def _fuzz_case(i):
+    """Seeded random pack and head layout: 1..40 sequences mixing lengths 1..8 and 9..700, KV
+    heads 1..8, query heads per KV head 1..6, d 64 or 128, the dS store on odd cases."""
+    rng = np.random.default_rng(9000 + i)
+    n = int(rng.integers(1, 41))
+    short = rng.random(n) < 0.4
+    lengths = np.where(short, rng.integers(1, 9, n), rng.integers(9, 701, n)).astype(np.int32)
+    hkv = int(rng.integers(1, 9))
+    group = int(rng.integers(1, 7))
+    d = int(rng.choice([64, 128]))
+    return lengths, hkv * group, hkv, d, bool(i % 2)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(16))
+def test_random_packs_against_oracle(case):
+    """Random packs and GQA layouts (including group sizes 3 and 5..6 and KV head counts that do
+    not divide the 8 XCDs): every output against the oracle."""
+    lengths, hq, hkv, d, store = _fuzz_case(case)
+    say("fuzz case", case, "n_seqs", len(lengths), "T", int(lengths.sum()), "hq/hkv/d", hq, hkv, d,
+        "dS store", store)
+    lens, q, k, v, do = synth.small_problem(500 + case, lengths, hq, hkv, d)
+    scale = 1.0 / math.sqrt(d)
+    res = run_pk(lens, q, k, v, do, scale, store=store)
+    o_ref, lse_ref = O.attn_fwd(q, k, v, lens, scale, 1e4)
+    dq_ref, dk_ref, dv_ref = O.attn_bwd(q, k, v, do, lens, scale, 1e4)
+    compare("out", to_np(res["out"]), o_ref)
+    compare("lse", to_np(res["lse"]), lse_ref, max_abs=LSE_MAX_ABS)
+    compare("dq", to_np(res["dq"]), dq_ref)
+    compare("dk", to_np(res["dk"]), dk_ref)
+    compare("dv", to_np(res["dv"]), dv_ref)
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("d,store,hkv", [(64, False, 8), (128, False, 8), (128, True, 8), (64, False, 2)],
                          ids=["d64", "d128", "d128_ds_store", "d64_2kv"])
